@@ -1,0 +1,338 @@
+"""Seeded synthetic workloads for column-sparse masked attention.
+
+This module only *describes inputs*: the four boundary vectors of a structured
+mask and the bf16 tensors Q, K, V, dO.  It holds none of the attention
+arithmetic and none of the tile classification; both the oracle and the HIP
+path consume what it produces.
+
+Column-sparse mask (FlashMask-3 paper summary, abstract): a structured mask is
+stored as four vectors over key positions j that hold query-row interval
+boundaries.  Following the predicate used throughout this library, element
+(i, j) is masked iff ``LTS[j] <= i < LTE[j]`` or ``UTS[j] <= i < UTE[j]``
+(half-open intervals; an interval with start >= end is empty).  Bounds are
+stored interleaved, ``int32 bounds[B][Hm][Sk][4] = (LTS, LTE, UTS, UTE)``.
+
+Mask families named by the paper summary's abstract (document, prefix-LM,
+share-question, sliding-window, block-sparse) are built here; every builder is
+checked against a direct definition of its pattern by the tests.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+LTS, LTE, UTS, UTE = 0, 1, 2, 3
+
+
+# --------------------------------------------------------------------------- #
+# bf16 encoding of seeded fp32 draws (round to nearest even)                   #
+# --------------------------------------------------------------------------- #
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even); return uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    return ((u + r) >> 16).astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact upcast of bf16 bit patterns to fp32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------- #
+# seeded structure draws                                                       #
+# --------------------------------------------------------------------------- #
+def composition(rng: np.random.Generator, total: int, k: int) -> list[int]:
+    """k positive lengths summing to ``total`` (uniform random cut points)."""
+    if k <= 1:
+        return [int(total)]
+    cuts = np.sort(rng.choice(np.arange(1, total), size=k - 1, replace=False))
+    return [int(x) for x in np.diff(np.concatenate([[0], cuts, [total]]))]
+
+
+def lognormal_docs(rng: np.random.Generator, total: int, median: float,
+                   sigma: float = 1.0, lo: int = 512, hi: int = 65536) -> list[int]:
+    """Document lengths drawn log-normally (median ``median``, log-space sigma),
+    clipped to [lo, hi], until they cover ``total``; the last one is cut to the
+    remainder and merged into its predecessor if that leaves it below ``lo``."""
+    lens: list[int] = []
+    while sum(lens) < total:
+        x = rng.lognormal(math.log(median), sigma)
+        lens.append(int(round(float(np.clip(x, lo, hi)))))
+    lens[-1] -= sum(lens) - total
+    if lens[-1] < lo and len(lens) > 1:
+        lens[-2] += lens.pop()
+    return lens
+
+
+def _starts_ends(lens):
+    ends = np.cumsum(np.asarray(lens, dtype=np.int64))
+    starts = ends - np.asarray(lens, dtype=np.int64)
+    return starts, ends
+
+
+# --------------------------------------------------------------------------- #
+# bound builders, one per mask family; each returns int32 [S][4]               #
+# --------------------------------------------------------------------------- #
+def causal_document_bounds(doc_lens) -> np.ndarray:
+    """Causal attention inside each document: row i sees column j iff both are
+    in the same document and j <= i.  Rows from the end of j's document on are
+    the lower interval, rows above the diagonal the upper interval."""
+    S = int(sum(doc_lens))
+    starts, ends = _starts_ends(doc_lens)
+    j = np.arange(S, dtype=np.int64)
+    doc_end = np.repeat(ends, doc_lens)
+    b = np.empty((S, 4), dtype=np.int64)
+    b[:, LTS], b[:, LTE] = doc_end, S
+    b[:, UTS], b[:, UTE] = 0, j
+    return b.astype(np.int32)
+
+
+def sliding_window_bounds(S: int, window: int) -> np.ndarray:
+    """Causal sliding window of ``window`` keys including the diagonal: row i
+    sees column j iff 0 <= i - j < window."""
+    j = np.arange(S, dtype=np.int64)
+    b = np.empty((S, 4), dtype=np.int64)
+    b[:, LTS], b[:, LTE] = np.minimum(j + window, S), S
+    b[:, UTS], b[:, UTE] = 0, j
+    return b.astype(np.int32)
+
+
+def share_question_bounds(question_len: int, answer_lens) -> np.ndarray:
+    """A causal question shared by several answers: question rows attend the
+    question causally; rows of an answer attend the whole question prefix up to
+    themselves (causally) and their own answer causally, never other answers."""
+    S = int(question_len + sum(answer_lens))
+    j = np.arange(S, dtype=np.int64)
+    b = np.empty((S, 4), dtype=np.int64)
+    b[:, UTS], b[:, UTE] = 0, j
+    b[:question_len, LTS] = S
+    b[:question_len, LTE] = S
+    starts, ends = _starts_ends(answer_lens)
+    b[question_len:, LTS] = np.repeat(ends + question_len, answer_lens)
+    b[question_len:, LTE] = S
+    return b.astype(np.int32)
+
+
+def prefix_document_bounds(doc_lens, prefix_frac: float = 0.1) -> np.ndarray:
+    """Documents with a bidirectional prefix of floor(frac * length) tokens and
+    causal attention after it.  Prefix columns are visible to every row of the
+    document; later columns only to rows at or below the diagonal."""
+    S = int(sum(doc_lens))
+    starts, ends = _starts_ends(doc_lens)
+    j = np.arange(S, dtype=np.int64)
+    doc_start = np.repeat(starts, doc_lens)
+    doc_end = np.repeat(ends, doc_lens)
+    plen = np.repeat(np.floor(np.asarray(doc_lens) * prefix_frac).astype(np.int64), doc_lens)
+    in_prefix = j < doc_start + plen
+    b = np.empty((S, 4), dtype=np.int64)
+    b[:, LTS], b[:, LTE] = doc_end, S
+    b[:, UTS] = 0
+    b[:, UTE] = np.where(in_prefix, doc_start, j)
+    return b.astype(np.int32)
+
+
+def blockwise_causal_bounds(S: int, block: int) -> np.ndarray:
+    """Block-sparse (block-causal) pattern: row i sees column j iff
+    block(j) <= block(i); rows of earlier blocks form the upper interval."""
+    j = np.arange(S, dtype=np.int64)
+    b = np.empty((S, 4), dtype=np.int64)
+    b[:, LTS], b[:, LTE] = S, S
+    b[:, UTS], b[:, UTE] = 0, (j // block) * block
+    return b.astype(np.int32)
+
+
+def empty_bounds(Sk: int, Sq: int) -> np.ndarray:
+    """No element masked (both intervals empty)."""
+    b = np.empty((Sk, 4), dtype=np.int32)
+    b[:, LTS], b[:, LTE], b[:, UTS], b[:, UTE] = Sq, Sq, 0, 0
+    return b
+
+
+def localize_bounds(global_bounds: np.ndarray, chunk_starts, chunk_len: int) -> np.ndarray:
+    """Context-parallel localisation (FlashMask-3 paper summary, abstract:
+    clip-shift-max on the boundary vectors).  A rank holds query chunks
+    ``[c0, c0+chunk_len)`` (in the given order, stacked as its local rows).
+    A global bound g becomes the number of local rows whose global index is
+    below g: for every chunk that starts at or before g take the chunk's local
+    offset plus g clipped into the chunk, and keep the maximum (0 if none).
+    The chunks must be listed in increasing global order, so that local row
+    order follows global row order; then a local row i is masked exactly when
+    its global row is."""
+    g = global_bounds.astype(np.int64)
+    out = np.zeros_like(g)
+    for ci, c0 in enumerate(chunk_starts):
+        shifted = ci * chunk_len + np.clip(g - c0, 0, chunk_len)
+        out = np.where(g >= c0, np.maximum(out, shifted), out)
+    return out.astype(np.int32)
+
+
+# --------------------------------------------------------------------------- #
+# workloads                                                                    #
+# --------------------------------------------------------------------------- #
+@dataclass
+class Workload:
+    name: str
+    B: int
+    H: int
+    Hm: int
+    Sq: int
+    Sk: int
+    D: int
+    bounds: np.ndarray            # int32 [B][Hm][Sk][4]
+    seed: int
+    structure: dict = field(default_factory=dict)
+    # how the tensors are drawn: (rows of Q drawn, slice of drawn Q rows used)
+    q_rows_drawn: int | None = None
+    q_row_index: np.ndarray | None = None
+    _rng_state: dict | None = None
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def draw(self):
+        """Return bf16 bit arrays (uint16) q[B][H][Sq][D], k, v [B][H][Sk][D],
+        do[B][H][Sq][D], drawn after the structure from the same generator."""
+        rng = np.random.default_rng()
+        rng.bit_generator.state = self._rng_state
+        B, H, D = self.B, self.H, self.D
+        qr = self.q_rows_drawn or self.Sq
+        q = bf16_bits(rng.standard_normal((B, H, qr, D), dtype=np.float32))
+        if self.q_row_index is not None:
+            q = np.ascontiguousarray(q[:, :, self.q_row_index, :])
+        k = bf16_bits(rng.standard_normal((B, H, self.Sk, D), dtype=np.float32))
+        v = bf16_bits(rng.standard_normal((B, H, self.Sk, D), dtype=np.float32))
+        do = bf16_bits(rng.standard_normal((B, H, self.Sq, D), dtype=np.float32))
+        return q, k, v, do
+
+    def nnz_per_head(self) -> np.ndarray:
+        """Unmasked (i, j) count per (b, hm), from the interval lengths (the
+        union of two half-open intervals clipped to [0, Sq))."""
+        b = self.bounds.astype(np.int64)
+        lo1, hi1 = np.clip(b[..., LTS], 0, self.Sq), np.clip(b[..., LTE], 0, self.Sq)
+        lo2, hi2 = np.clip(b[..., UTS], 0, self.Sq), np.clip(b[..., UTE], 0, self.Sq)
+        l1 = np.maximum(hi1 - lo1, 0)
+        l2 = np.maximum(hi2 - lo2, 0)
+        ov = np.maximum(np.minimum(hi1, hi2) - np.maximum(lo1, lo2), 0)
+        ov = np.where((l1 > 0) & (l2 > 0), ov, 0)
+        masked = l1 + l2 - ov
+        return (self.Sq - masked).sum(axis=-1)
+
+    def nnz_total(self) -> int:
+        per = self.nnz_per_head()                 # [B][Hm]
+        mult = self.H // self.Hm
+        return int(per.sum()) * mult
+
+    def flops(self) -> tuple[float, float]:
+        """Mask-effective flops (forward 4*D*nnz, backward 10*D*nnz)."""
+        nnz = self.nnz_total()
+        return 4.0 * self.D * nnz, 10.0 * self.D * nnz
+
+
+def _finish(name, rng, B, H, Sq, Sk, D, bounds_2d, seed, structure, **kw) -> Workload:
+    bounds = np.ascontiguousarray(
+        np.broadcast_to(bounds_2d[None, None], (B, 1, Sk, 4))).astype(np.int32)
+    return Workload(name=name, B=B, H=H, Hm=1, Sq=Sq, Sk=Sk, D=D, bounds=bounds,
+                    seed=seed, structure=structure,
+                    _rng_state=rng.bit_generator.state, **kw)
+
+
+def causal_document(B=1, H=2, S=1024, D=64, n_docs=4, seed=1) -> Workload:
+    rng = np.random.default_rng(seed)
+    docs = composition(rng, S, n_docs)
+    return _finish("causal_document", rng, B, H, S, S, D,
+                   causal_document_bounds(docs), seed, {"docs": docs})
+
+
+def sliding_window(B=2, H=16, S=8192, D=128, window=1024, seed=2) -> Workload:
+    rng = np.random.default_rng(seed)
+    return _finish("sliding_window", rng, B, H, S, S, D,
+                   sliding_window_bounds(S, window), seed, {"window": window})
+
+
+def share_question(B=1, H=16, S=32768, D=128, question=4096, n_answers=8, seed=3) -> Workload:
+    rng = np.random.default_rng(seed)
+    answers = composition(rng, S - question, n_answers)
+    return _finish("share_question", rng, B, H, S, S, D,
+                   share_question_bounds(question, answers), seed,
+                   {"question": question, "answers": answers})
+
+
+def prefix_document(B=1, H=8, S=131072, D=128, median=8192, seed=4,
+                    lo=512, hi=65536, prefix_frac=0.1) -> Workload:
+    rng = np.random.default_rng(seed)
+    docs = lognormal_docs(rng, S, median, 1.0, lo, hi)
+    return _finish("prefix_document", rng, B, H, S, S, D,
+                   prefix_document_bounds(docs, prefix_frac), seed,
+                   {"docs": docs, "prefix_frac": prefix_frac})
+
+
+def cp_rank_share(H=16, S=65536, D=128, median=4096, world=8, rank=3, seed=5,
+                  lo=512, hi=65536) -> Workload:
+    """One context-parallel rank's share under the two-chunks-per-rank layout:
+    the sequence is cut into 2*world chunks, rank r holds chunks r and
+    2*world-1-r as its local query rows and attends all S keys through the
+    localised bounds."""
+    rng = np.random.default_rng(seed)
+    docs = lognormal_docs(rng, S, median, 1.0, lo, hi)
+    gb = causal_document_bounds(docs)
+    n_chunks = 2 * world
+    C = S // n_chunks
+    chunks = [rank, n_chunks - 1 - rank]
+    starts = [c * C for c in chunks]
+    lb = localize_bounds(gb, starts, C)
+    rows = np.concatenate([np.arange(s, s + C) for s in starts])
+    w = _finish("cp_rank_share", rng, 1, H, 2 * C, S, D, lb, seed,
+                {"docs": docs, "world": world, "rank": rank, "chunks": chunks,
+                 "chunk_len": C, "global_rows": rows},
+                q_rows_drawn=S, q_row_index=rows)
+    w.structure["global_bounds"] = gb
+    return w
+
+
+def block_causal(B=1, H=4, S=4096, D=128, block=512, seed=6) -> Workload:
+    rng = np.random.default_rng(seed)
+    return _finish("block_causal", rng, B, H, S, S, D,
+                   blockwise_causal_bounds(S, block), seed, {"block": block})
+
+
+CONFIGS = {
+    1: causal_document,
+    2: sliding_window,
+    3: share_question,
+    4: prefix_document,
+    5: cp_rank_share,
+}
+
+CONFIG_NAMES = {
+    1: "causal_document B1 H2 S1024 D64",
+    2: "sliding_window w1024 B2 H16 S8192 D128",
+    3: "share_question q4096 a8 B1 H16 S32768 D128",
+    4: "prefix_document lognormal(8192) B1 H8 S131072 D128",
+    5: "cp_rank_share r3/8 Sq8192 Sk65536 H16 D128",
+}
+
+
+def config(k: int, seed: int | None = None) -> Workload:
+    """The five evaluation workloads at full size; default seed = k."""
+    return CONFIGS[k](seed=k if seed is None else seed)
+
+
+def custom(bounds_2d: np.ndarray, B: int, H: int, Sq: int, D: int, seed: int,
+           name: str = "custom", Hm: int = 1, per_head_bounds: np.ndarray | None = None) -> Workload:
+    """Workload from explicit bounds ([Sk][4], or [B][Hm][Sk][4] via
+    ``per_head_bounds``); tensors drawn from ``default_rng(seed)``."""
+    rng = np.random.default_rng(seed)
+    if per_head_bounds is not None:
+        bounds = np.ascontiguousarray(per_head_bounds, dtype=np.int32)
+        Sk = bounds.shape[2]
+        Hm = bounds.shape[1]
+    else:
+        Sk = bounds_2d.shape[0]
+        bounds = np.ascontiguousarray(
+            np.broadcast_to(bounds_2d[None, None], (B, Hm, Sk, 4))).astype(np.int32)
+    return Workload(name=name, B=B, H=H, Hm=Hm, Sq=Sq, Sk=Sk, D=D, bounds=bounds,
+                    seed=seed, _rng_state=rng.bit_generator.state)

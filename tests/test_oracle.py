@@ -1,0 +1,317 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+* torch's float64 scaled-dot-product attention on the CPU (a library routine)
+  with autograd, for the unmasked case, the causal case and general masks;
+* central finite differences of L = <dO, O> for the gradients;
+* the fully-masked-row convention (O = 0, LSE = +inf, zero gradients);
+* invariants of exact arithmetic (sum_j dK_j = 0, shift of V, unseen columns);
+* brute-force tile classes from the dense mask;
+* context-parallel consistency: a rank's share equals the matching rows of
+  the global problem, and the ranks' dK/dV add up to the global ones.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import oracle as O
+from column_sparse_masked_amd import masks as M
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def _torch_sdpa(q, k, v, do, visible, scale):
+    """float64 CPU reference through torch SDPA + autograd; ``visible`` is
+    bool [Sq][Sk] (True = may attend)."""
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq[None, None], tk[None, None], tv[None, None],
+        attn_mask=torch.tensor(visible)[None, None], scale=scale)[0, 0]
+    out.backward(torch.tensor(do))
+    return out.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def _oracle_head(q, k, v, do, bounds, scale):
+    o, lse = O.head_forward(q, k, v, bounds, scale)
+    dq, dk, dv = O.head_backward(q, k, v, do, bounds, scale, lse=lse)
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("Sq,Sk,D", [(37, 37, 16), (64, 200, 8), (300, 260, 32)])
+def test_unmasked_equals_plain_attention(Sq, Sk, D):
+    rng = np.random.default_rng(Sq + Sk)
+    q, k, v, do = _rand(rng, Sq, D), _rand(rng, Sk, D), _rand(rng, Sk, D), _rand(rng, Sq, D)
+    scale = 1 / math.sqrt(D)
+    b = M.empty_bounds(Sk, Sq)
+    o, lse, dq, dk, dv = _oracle_head(q, k, v, do, b, scale)
+    ro, rdq, rdk, rdv = _torch_sdpa(q, k, v, do, np.ones((Sq, Sk), bool), scale)
+    for a, r in ((o, ro), (dq, rdq), (dk, rdk), (dv, rdv)):
+        np.testing.assert_allclose(a, r, rtol=1e-10, atol=1e-11)
+    # LSE against its definition through scipy's logsumexp
+    from scipy.special import logsumexp
+    np.testing.assert_allclose(lse, logsumexp(scale * q @ k.T, axis=1), rtol=1e-12)
+
+
+def test_causal_equals_sdpa_is_causal():
+    rng = np.random.default_rng(7)
+    S, D = 290, 16
+    q, k, v, do = (_rand(rng, S, D) for _ in range(4))
+    scale = 1 / math.sqrt(D)
+    b = M.causal_document_bounds([S])
+    o, _, dq, dk, dv = _oracle_head(q, k, v, do, b, scale)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq[None, None], tk[None, None], tv[None, None], is_causal=True, scale=scale)[0, 0]
+    out.backward(torch.tensor(do))
+    for a, r in ((o, out.detach()), (dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(a, r.numpy(), rtol=1e-10, atol=1e-11)
+
+
+@pytest.mark.parametrize("family", ["causal_document", "sliding", "share_question", "prefix", "block"])
+def test_masked_equals_sdpa_with_dense_mask(family):
+    rng = np.random.default_rng(11)
+    S, D = 333, 16
+    if family == "causal_document":
+        b = M.causal_document_bounds(M.composition(rng, S, 5))
+    elif family == "sliding":
+        b = M.sliding_window_bounds(S, 40)
+    elif family == "share_question":
+        b = M.share_question_bounds(60, M.composition(rng, S - 60, 4))
+    elif family == "prefix":
+        b = M.prefix_document_bounds(M.composition(rng, S, 3), 0.3)
+    else:
+        b = M.blockwise_causal_bounds(S, 64)
+    q, k, v, do = (_rand(rng, S, D) for _ in range(4))
+    scale = 1 / math.sqrt(D)
+    o, _, dq, dk, dv = _oracle_head(q, k, v, do, b, scale)
+    # visibility written from the pattern definition here, not from the oracle
+    i, j = np.meshgrid(np.arange(S), np.arange(S), indexing="ij")
+    vis = ~(((b[None, :, 0] <= i) & (i < b[None, :, 1])) | ((b[None, :, 2] <= i) & (i < b[None, :, 3])))
+    assert vis.any(axis=1).all()
+    ro, rdq, rdk, rdv = _torch_sdpa(q, k, v, do, vis, scale)
+    for a, r in ((o, ro), (dq, rdq), (dk, rdk), (dv, rdv)):
+        np.testing.assert_allclose(a, r, rtol=1e-9, atol=1e-11)
+
+
+def _loss(q, k, v, do, b, scale):
+    o, _ = O.head_forward(q, k, v, b, scale)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_gradients_match_finite_differences(seed):
+    """Central differences of L = <dO, O>, h = 1e-6, fp64.  Masks are piecewise
+    constant in the inputs, so the difference quotient is valid everywhere."""
+    rng = np.random.default_rng(seed)
+    Sq, Sk, D = 23, 29, 6
+    b = rng.integers(-2, Sq + 2, size=(Sk, 4)).astype(np.int32)
+    b[3] = (5, 6, 0, 0)   # a column masked only on one row
+    q, k, v = _rand(rng, Sq, D), _rand(rng, Sk, D), _rand(rng, Sk, D)
+    do = _rand(rng, Sq, D)
+    scale = 1 / math.sqrt(D)
+    _, _, dq, dk, dv = _oracle_head(q, k, v, do, b, scale)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            orig = x[idx]
+            x[idx] = orig + h
+            lp = _loss(q, k, v, do, b, scale)
+            x[idx] = orig - h
+            lm = _loss(q, k, v, do, b, scale)
+            x[idx] = orig
+            num[idx] = (lp - lm) / (2 * h)
+        err = np.linalg.norm(num - g) / max(np.linalg.norm(g), 1e-300)
+        assert err <= 1e-6, (name, err)
+
+
+def test_fully_masked_everything():
+    rng = np.random.default_rng(3)
+    Sq, Sk, D = 40, 50, 8
+    b = np.zeros((Sk, 4), np.int32)
+    b[:, 0], b[:, 1] = 0, Sq          # lower interval covers every row
+    q, k, v, do = _rand(rng, Sq, D), _rand(rng, Sk, D), _rand(rng, Sk, D), _rand(rng, Sq, D)
+    o, lse, dq, dk, dv = _oracle_head(q, k, v, do, b, 0.3)
+    assert (o == 0).all() and np.isposinf(lse).all()
+    assert (dq == 0).all() and (dk == 0).all() and (dv == 0).all()
+
+
+def test_single_fully_masked_row():
+    """Row 5 masked in every column: O_5 = 0, LSE_5 = +inf; the other rows and
+    all gradients equal the unmasked problem with dO_5 set to zero."""
+    rng = np.random.default_rng(4)
+    Sq, Sk, D = 30, 33, 8
+    b = np.tile(np.array([5, 6, 0, 0], np.int32), (Sk, 1))
+    q, k, v, do = _rand(rng, Sq, D), _rand(rng, Sk, D), _rand(rng, Sk, D), _rand(rng, Sq, D)
+    o, lse, dq, dk, dv = _oracle_head(q, k, v, do, b, 0.4)
+    assert (o[5] == 0).all() and np.isposinf(lse[5]) and (dq[5] == 0).all()
+    do0 = do.copy()
+    do0[5] = 0
+    ro, rdq, rdk, rdv = _torch_sdpa(q, k, v, do0, np.ones((Sq, Sk), bool), 0.4)
+    keep = np.arange(Sq) != 5
+    np.testing.assert_allclose(o[keep], ro[keep], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dq[keep], rdq[keep], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, rdk, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, rdv, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_invariants(seed):
+    rng = np.random.default_rng(seed)
+    S, D = 270, 16
+    b = M.prefix_document_bounds(M.composition(rng, S, 3), 0.2)
+    b[40:44] = (0, S, 0, 0)                   # four columns nobody sees
+    q, k, v, do = (_rand(rng, S, D) for _ in range(4))
+    o, lse, dq, dk, dv = _oracle_head(q, k, v, do, b, 0.25)
+    # sum_j dS_ij = 0 for every row, hence sum_j dK_j = 0
+    np.testing.assert_allclose(dk.sum(axis=0), 0, atol=1e-10)
+    # unseen columns get no gradient
+    assert (dk[40:44] == 0).all() and (dv[40:44] == 0).all()
+    # softmax rows sum to one: shifting V by a constant vector shifts O by it
+    c = rng.standard_normal(D)
+    o2, _ = O.head_forward(q, k, v + c, b, 0.25)
+    np.testing.assert_allclose(o2, o + c, atol=1e-12)
+    # total dV equals the column sums of dO for rows that see anything
+    live = np.isfinite(lse)
+    np.testing.assert_allclose(dv.sum(axis=0), do[live].sum(axis=0), atol=1e-10)
+
+
+def test_row_subset_gradients_complete_for_their_columns():
+    """head_backward on the rows that see a column set gives those columns'
+    complete dK/dV; row-subset forward equals the full forward's rows."""
+    rng = np.random.default_rng(9)
+    S, D = 400, 8
+    b = M.causal_document_bounds(M.composition(rng, S, 6))
+    q, k, v, do = (_rand(rng, S, D) for _ in range(4))
+    full = _oracle_head(q, k, v, do, b, 0.3)
+    cols = np.arange(100, 140)
+    rows = O.rows_seeing(b, S, cols)
+    dq, dk, dv = O.head_backward(q, k, v, do, b, 0.3, rows=rows)
+    np.testing.assert_allclose(dk[cols], full[3][cols], atol=1e-12)
+    np.testing.assert_allclose(dv[cols], full[4][cols], atol=1e-12)
+    np.testing.assert_allclose(dq, full[2][rows], atol=1e-12)
+    o, lse = O.head_forward(q, k, v, b, 0.3, rows=rows[::7])
+    np.testing.assert_allclose(o, full[0][rows[::7]], atol=1e-14)
+
+
+# --------------------------------------------------------------------------- #
+# tile classification                                                         #
+# --------------------------------------------------------------------------- #
+def test_classification_hand_example():
+    """One key block of 4 columns against a query block of 4 rows (BQ=BK=4):
+    column 0 has its upper interval covering rows [0, 2) and its lower
+    interval rows [2, 4): every element is masked, yet neither single interval
+    covers the tile, so the min/max rule says partial (it is conservative)."""
+    b = np.array([[2, 4, 0, 2], [0, 4, 0, 0], [0, 4, 0, 0], [0, 4, 0, 0]], np.int32)
+    assert O.exact_tile_classes(b, 4, 4, 4)[0, 0] == O.SKIP
+    _, cls, cq, ck = O.classify(b[None, None], 4, 4, 4)
+    assert cls[0, 0, 0, 0] == O.PARTIAL and cq[0, 0, 0] == 1 and ck[0, 0, 0] == 1
+    # all four columns fully covered by the lower interval: skip
+    b2 = np.tile(np.array([0, 4, 0, 0], np.int32), (4, 1))
+    assert O.classify(b2[None, None], 4, 4, 4)[1][0, 0, 0, 0] == O.SKIP
+    # rows 0..3 of 8, all columns' intervals in rows >= 4: full for block 0,
+    # skip for block 1
+    b3 = np.tile(np.array([4, 8, 4, 6], np.int32), (4, 1))
+    c3 = O.classify(b3[None, None], 8, 4, 4)[1][0, 0, :, 0]
+    assert c3.tolist() == [O.FULL, O.SKIP]
+
+
+def test_key_block_summary_by_hand():
+    b = np.array([[5, 9, -3, 2], [7, 100, 0, 0], [1, 1, 4, 8]], np.int32)
+    ks = O.key_block_summary(b, 10, 2)
+    # block 0 = columns 0,1 clamped to [0,10]: LTS {5,7}, LTE {9,10}, UTS {0,0}, UTE {2,0}
+    assert ks[0].tolist() == [5, 7, 9, 10, 0, 0, 0, 2]
+    assert ks[1].tolist() == [1, 1, 1, 1, 4, 4, 8, 8]
+
+
+@settings(max_examples=150, deadline=None)
+@given(Sq=st.integers(1, 40), Sk=st.integers(1, 40), BQ=st.sampled_from([1, 2, 4, 8, 16]),
+       BK=st.sampled_from([1, 3, 4, 8, 16]), seed=st.integers(0, 2 ** 31))
+def test_classification_is_sound(Sq, Sk, BQ, BK, seed):
+    """skip => every element masked; full => no element masked (brute force)."""
+    rng = np.random.default_rng(seed)
+    mode = seed % 3
+    if mode == 0:
+        b = rng.integers(-3, Sq + 3, size=(Sk, 4))
+    elif mode == 1:      # structured: mostly document-like columns
+        b = np.stack([rng.integers(0, Sq + 1, Sk), np.full(Sk, Sq),
+                      np.zeros(Sk), rng.integers(0, Sq + 1, Sk)], axis=1)
+    else:                # many empty intervals
+        s = rng.integers(0, Sq + 1, size=(Sk, 2))
+        b = np.stack([s[:, 0], s[:, 0], np.zeros(Sk), s[:, 1]], axis=1)
+    b = b.astype(np.int32)
+    _, cls, cq, ck = O.classify(b[None, None], Sq, BQ, BK)
+    ex = O.exact_tile_classes(b, Sq, BQ, BK)
+    c = cls[0, 0]
+    assert np.all(ex[c == O.SKIP] == O.SKIP)
+    assert np.all(ex[c == O.FULL] == O.FULL)
+    assert np.all((c == O.SKIP) | (c == O.FULL) | (c == O.PARTIAL))
+    assert np.array_equal(cq[0, 0], (c != O.SKIP).sum(axis=1))
+    assert np.array_equal(ck[0, 0], (c != O.SKIP).sum(axis=0))
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+def test_rule_is_tight_on_workload_masks(k):
+    """On the evaluation masks the min/max rule equals the brute-force classes
+    (the bit-exact class map is then the same under either reading)."""
+    w = M.config(k)
+    Sq = w.Sq
+    if Sq > 8192:          # share-question at 32K: test the first 8K rows and keys
+        b = w.bounds[0, 0][:8192].copy()
+        b = np.clip(b, 0, 8192)
+        Sq = 8192
+    else:
+        b = w.bounds[0, 0]
+    for BQ, BK in ((128, 128), (64, 128)):
+        cls = O.classify(b[None, None], Sq, BQ, BK)[1][0, 0]
+        assert np.array_equal(cls, O.exact_tile_classes(b, Sq, BQ, BK))
+
+
+# --------------------------------------------------------------------------- #
+# context-parallel consistency                                                #
+# --------------------------------------------------------------------------- #
+def test_cp_shares_reassemble_global_problem():
+    rng = np.random.default_rng(5)
+    S, D, world = 256, 8, 4
+    docs = M.composition(rng, S, 5)
+    gb = M.causal_document_bounds(docs)
+    q, k, v, do = (_rand(rng, S, D) for _ in range(4))
+    go, glse, gdq, gdk, gdv = _oracle_head(q, k, v, do, gb, 0.3)
+    C = S // (2 * world)
+    sdk, sdv = np.zeros_like(k), np.zeros_like(v)
+    for r in range(world):
+        starts = [r * C, (2 * world - 1 - r) * C]
+        rows = np.concatenate([np.arange(s, s + C) for s in starts])
+        lb = M.localize_bounds(gb, starts, C)
+        lo, llse, ldq, ldk, ldv = _oracle_head(q[rows], k, v, do[rows], lb, 0.3)
+        np.testing.assert_allclose(lo, go[rows], atol=1e-14)
+        np.testing.assert_allclose(llse, glse[rows], atol=1e-13)
+        np.testing.assert_allclose(ldq, gdq[rows], atol=1e-13)
+        sdk += ldk
+        sdv += ldv
+    np.testing.assert_allclose(sdk, gdk, atol=1e-12)
+    np.testing.assert_allclose(sdv, gdv, atol=1e-12)
+
+
+def test_batched_entry_points_match_heads():
+    """forward/backward over [B][H] with per-head masks equal per-head calls."""
+    rng = np.random.default_rng(12)
+    B, H, Sq, Sk, D = 2, 3, 40, 50, 8
+    bounds = rng.integers(0, Sq + 1, size=(B, H, Sk, 4)).astype(np.int32)
+    q, do = _rand(rng, B, H, Sq, D), _rand(rng, B, H, Sq, D)
+    k, v = _rand(rng, B, H, Sk, D), _rand(rng, B, H, Sk, D)
+    o, lse, dq, dk, dv = O.attention(q, k, v, do, bounds, 0.35)
+    for b in range(B):
+        for h in range(H):
+            ref = _oracle_head(q[b, h], k[b, h], v[b, h], do[b, h], bounds[b, h], 0.35)
+            for a, r in zip((o, lse, dq, dk, dv), ref):
+                np.testing.assert_array_equal(a[b, h], r)
+    # one shared mask head
+    o1, *_ = O.attention(q, k, v, do, bounds[:, :1], 0.35)
+    for h in range(H):
+        r = O.head_forward(q[1, h], k[1, h], v[1, h], bounds[1, 0], 0.35)[0]
+        np.testing.assert_array_equal(o1[1, h], r)
