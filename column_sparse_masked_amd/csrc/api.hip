@@ -1,0 +1,276 @@
+// C ABI of libfm: argument checks, tileinfo layout and kernel launches.
+// Declared and documented in include/fm.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/fm.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr long kMaxSeq = 32768L * fm::BQ;   // list entries hold block indices < 32768
+static_assert(fm::BQ == fm::BK, "tile shape is square");
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+fm_status check_problem(const fm_problem* p) {
+  if (!p) return FM_ERR_NULL;
+  if (p->batch < 0 || p->heads < 1 || p->mask_heads < 1 || p->seqlen_q < 0 || p->seqlen_k < 0)
+    return FM_ERR_SHAPE;
+  if (p->seqlen_q > kMaxSeq || p->seqlen_k > kMaxSeq) return FM_ERR_SHAPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return FM_ERR_UNSUPPORTED;
+  if (p->mask_heads != 1 && p->mask_heads != p->heads) return FM_ERR_UNSUPPORTED;
+  if (!(p->softmax_scale > 0.f) || !std::isfinite(p->softmax_scale)) return FM_ERR_UNSUPPORTED;
+  const long nQ = (p->seqlen_q + fm::BQ - 1) / fm::BQ, nK = (p->seqlen_k + fm::BK - 1) / fm::BK;
+  const long items = (long)p->batch * p->heads * (nQ > nK ? nQ : nK);
+  if (items >= (1L << 31)) return FM_ERR_SHAPE;
+  return FM_OK;
+}
+
+struct Layout {
+  int nQ, nK;
+  size_t counters, kbsum, cls, cnt_q, cnt_k, list_q, list_k, fwd_queue, bwd_queue, total;
+};
+
+Layout make_layout(const fm_problem* p) {
+  Layout L;
+  L.nQ = (p->seqlen_q + fm::BQ - 1) / fm::BQ;
+  L.nK = (p->seqlen_k + fm::BK - 1) / fm::BK;
+  const size_t bhm = (size_t)p->batch * p->mask_heads, bh = (size_t)p->batch * p->heads;
+  size_t off = 0;
+  L.counters = off;  off = align256(off + 16 * sizeof(uint32_t));
+  L.kbsum = off;     off = align256(off + bhm * L.nK * 8 * sizeof(int32_t));
+  L.cls = off;       off = align256(off + bhm * L.nQ * L.nK);
+  L.cnt_q = off;     off = align256(off + bhm * L.nQ * sizeof(int32_t));
+  L.cnt_k = off;     off = align256(off + bhm * L.nK * sizeof(int32_t));
+  L.list_q = off;    off = align256(off + bhm * L.nQ * L.nK * sizeof(uint16_t));
+  L.list_k = off;    off = align256(off + bhm * L.nK * L.nQ * sizeof(uint16_t));
+  L.fwd_queue = off; off = align256(off + bh * L.nQ * sizeof(uint32_t));
+  L.bwd_queue = off; off = align256(off + bh * L.nK * sizeof(uint32_t));
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+std::mutex g_cu_mutex;
+int g_cu_count[64] = {0};
+
+fm_status cu_count(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FM_ERR_HIP;
+  if (dev < 0 || dev >= 64) return FM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_cu_mutex);
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return FM_ERR_HIP;
+    g_cu_count[dev] = n;
+  }
+  *out = g_cu_count[dev];
+  return FM_OK;
+}
+
+bool tensor_ok(const void* p) { return p != nullptr; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fm_status_str(fm_status s) {
+  switch (s) {
+    case FM_OK: return "FM_OK";
+    case FM_ERR_NULL: return "FM_ERR_NULL: a required pointer is NULL";
+    case FM_ERR_SHAPE: return "FM_ERR_SHAPE: a size is negative or beyond the supported range";
+    case FM_ERR_UNSUPPORTED:
+      return "FM_ERR_UNSUPPORTED: head_dim must be 64 or 128, mask_heads 1 or heads, scale > 0";
+    case FM_ERR_ALIGN: return "FM_ERR_ALIGN: a tensor pointer is not suitably aligned";
+    case FM_ERR_HIP: return "FM_ERR_HIP: the HIP runtime rejected a call or launch";
+  }
+  return "unknown fm_status";
+}
+
+fm_status fm_tile_shape(const fm_problem* p, int32_t* block_q, int32_t* block_k) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  if (!block_q || !block_k) return FM_ERR_NULL;
+  *block_q = fm::BQ;
+  *block_k = fm::BK;
+  return FM_OK;
+}
+
+fm_status fm_tileinfo_layout_query(const fm_problem* p, fm_tileinfo_layout* out) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  if (!out) return FM_ERR_NULL;
+  Layout L = make_layout(p);
+  out->block_q = fm::BQ;
+  out->block_k = fm::BK;
+  out->n_qblocks = L.nQ;
+  out->n_kblocks = L.nK;
+  out->counters = L.counters;
+  out->kbsum = L.kbsum;
+  out->cls = L.cls;
+  out->cnt_q = L.cnt_q;
+  out->cnt_k = L.cnt_k;
+  out->list_q = L.list_q;
+  out->list_k = L.list_k;
+  out->fwd_queue = L.fwd_queue;
+  out->bwd_queue = L.bwd_queue;
+  out->total = L.total;
+  return FM_OK;
+}
+
+fm_status fm_bwd_workspace_bytes(const fm_problem* p, size_t* bytes) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  if (!bytes) return FM_ERR_NULL;
+  const size_t rows = (size_t)p->batch * p->heads * p->seqlen_q;
+  *bytes = align256(rows * p->head_dim * sizeof(float)) + align256(rows * sizeof(float));
+  return FM_OK;
+}
+
+fm_status fm_device_cu_count(int32_t* cus) {
+  if (!cus) return FM_ERR_NULL;
+  int n = 0;
+  fm_status st = cu_count(&n);
+  if (st == FM_OK) *cus = n;
+  return st;
+}
+
+fm_status fm_tile_bounds(const fm_problem* p, const int32_t* bounds, void* tileinfo, void* stream) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  if (!tileinfo) return FM_ERR_NULL;
+  if (!aligned(tileinfo, 256)) return FM_ERR_ALIGN;
+  const bool has_cols = p->batch > 0 && p->seqlen_k > 0;
+  if (has_cols && !bounds) return FM_ERR_NULL;
+  if (bounds && !aligned(bounds, 16)) return FM_ERR_ALIGN;
+  Layout L = make_layout(p);
+  fm::TileArgs a;
+  a.bounds = reinterpret_cast<const int4*>(bounds);
+  a.kbsum = at<int>(tileinfo, L.kbsum);
+  a.cls = at<uint8_t>(tileinfo, L.cls);
+  a.cnt_q = at<int>(tileinfo, L.cnt_q);
+  a.cnt_k = at<int>(tileinfo, L.cnt_k);
+  a.list_q = at<uint16_t>(tileinfo, L.list_q);
+  a.list_k = at<uint16_t>(tileinfo, L.list_k);
+  a.fwd_queue = at<uint32_t>(tileinfo, L.fwd_queue);
+  a.bwd_queue = at<uint32_t>(tileinfo, L.bwd_queue);
+  a.counters = at<uint32_t>(tileinfo, L.counters);
+  a.B = p->batch; a.H = p->heads; a.Hm = p->mask_heads;
+  a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
+  if (p->batch == 0 || (L.nQ == 0 && L.nK == 0)) {
+    // nothing to classify; still leave empty queues behind
+    if (hipMemsetAsync(a.counters, 0, 16 * sizeof(uint32_t), (hipStream_t)stream) != hipSuccess)
+      return FM_ERR_HIP;
+    return FM_OK;
+  }
+  return fm::launch_tile_bounds(a, (hipStream_t)stream) == hipSuccess ? FM_OK : FM_ERR_HIP;
+}
+
+fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const void* v,
+                      const int32_t* bounds, void* tileinfo, void* o, float* lse, void* stream) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  const bool has_rows = p->batch > 0 && p->seqlen_q > 0;
+  const bool has_cols = p->batch > 0 && p->seqlen_k > 0;
+  if (!tileinfo) return FM_ERR_NULL;
+  if (has_rows && (!tensor_ok(q) || !tensor_ok(o) || !lse)) return FM_ERR_NULL;
+  if (has_cols && (!tensor_ok(k) || !tensor_ok(v) || !bounds)) return FM_ERR_NULL;
+  if (!aligned(tileinfo, 256) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(o, 16) || !aligned(bounds, 16) || !aligned(lse, 4))
+    return FM_ERR_ALIGN;
+  if (!has_rows) return FM_OK;
+  Layout L = make_layout(p);
+  int cus = 0;
+  if ((st = cu_count(&cus)) != FM_OK) return st;
+  fm::FwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<__bf16*>(o);
+  a.lse = lse;
+  a.bounds = reinterpret_cast<const int4*>(bounds);
+  a.list_q = at<uint16_t>(tileinfo, L.list_q);
+  a.cnt_q = at<int>(tileinfo, L.cnt_q);
+  a.queue = at<uint32_t>(tileinfo, L.fwd_queue);
+  a.counters = at<uint32_t>(tileinfo, L.counters);
+  a.B = p->batch; a.H = p->heads; a.Hm = p->mask_heads;
+  a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
+  a.scale_log2 = p->softmax_scale * fm::kLog2e;
+  const long items = (long)p->batch * p->heads * L.nQ;
+  const long slots = (long)cus * fm::fwd_blocks_per_cu(p->head_dim);
+  const int grid = (int)(items < slots ? items : slots);
+  return fm::launch_attn_fwd(a, p->head_dim, grid, (hipStream_t)stream) == hipSuccess ? FM_OK
+                                                                                      : FM_ERR_HIP;
+}
+
+fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
+                      const void* o, const void* dout, const float* lse,
+                      const int32_t* bounds, void* tileinfo,
+                      void* dq, void* dk, void* dv, void* workspace, void* stream) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  const bool has_rows = p->batch > 0 && p->seqlen_q > 0;
+  const bool has_cols = p->batch > 0 && p->seqlen_k > 0;
+  if (!tileinfo) return FM_ERR_NULL;
+  if (has_rows && (!tensor_ok(q) || !tensor_ok(o) || !tensor_ok(dout) || !lse || !tensor_ok(dq) ||
+                   !workspace))
+    return FM_ERR_NULL;
+  if (has_cols && (!tensor_ok(k) || !tensor_ok(v) || !bounds || !tensor_ok(dk) || !tensor_ok(dv)))
+    return FM_ERR_NULL;
+  if (!aligned(tileinfo, 256) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(o, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
+      !aligned(dv, 16) || !aligned(bounds, 16) || !aligned(lse, 4) || !aligned(workspace, 16))
+    return FM_ERR_ALIGN;
+  if (!has_rows && !has_cols) return FM_OK;
+  Layout L = make_layout(p);
+  const hipStream_t s = (hipStream_t)stream;
+  if (!has_rows) {
+    // no query rows: every key gets zero gradient
+    const size_t bytes = (size_t)p->batch * p->heads * p->seqlen_k * p->head_dim * 2;
+    if (hipMemsetAsync(dk, 0, bytes, s) != hipSuccess || hipMemsetAsync(dv, 0, bytes, s) != hipSuccess)
+      return FM_ERR_HIP;
+    return FM_OK;
+  }
+  int cus = 0;
+  if ((st = cu_count(&cus)) != FM_OK) return st;
+  const size_t rows = (size_t)p->batch * p->heads * p->seqlen_q;
+  fm::BwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<const __bf16*>(o);
+  a.dout = static_cast<const __bf16*>(dout);
+  a.lse = lse;
+  a.bounds = reinterpret_cast<const int4*>(bounds);
+  a.list_k = at<uint16_t>(tileinfo, L.list_k);
+  a.cnt_k = at<int>(tileinfo, L.cnt_k);
+  a.queue = at<uint32_t>(tileinfo, L.bwd_queue);
+  a.counters = at<uint32_t>(tileinfo, L.counters);
+  a.dq = static_cast<__bf16*>(dq);
+  a.dk = static_cast<__bf16*>(dk);
+  a.dv = static_cast<__bf16*>(dv);
+  a.dq_acc = static_cast<float*>(workspace);
+  a.delta = at<float>(workspace, align256(rows * p->head_dim * sizeof(float)));
+  a.B = p->batch; a.H = p->heads; a.Hm = p->mask_heads;
+  a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = p->softmax_scale * fm::kLog2e;
+  const long items = (long)p->batch * p->heads * L.nK;
+  const long slots = (long)cus * fm::bwd_blocks_per_cu(p->head_dim);
+  const int grid = (int)(items < slots ? items : slots);
+  return fm::launch_attn_bwd(a, p->head_dim, grid, s) == hipSuccess ? FM_OK : FM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Device-side definitions shared by the libfm kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fm {
+
+// Tile shape: BQ query rows x BK key columns.  The forward gives each of the 4
+// waves of a workgroup 32 query rows; the backward gives each wave 32 keys.
+constexpr int BQ = 128;
+constexpr int BK = 128;
+constexpr int kListPartial = 0x8000;   // bit 15 of a list entry: tile is partial
+constexpr int kListIndex = 0x7fff;
+
+// counters[] slots inside the tileinfo buffer
+constexpr int kCtrFwdItems = 0, kCtrBwdItems = 1, kCtrFwdNext = 2, kCtrBwdNext = 3,
+              kCtrFwdExit = 4, kCtrBwdExit = 5;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D = A(32x16) * B(16x32) + C on the matrix cores.  Lane l supplies
+//   A[l%32][8*(l/32) .. +8]   and   B[8*(l/32) .. +8][l%32],
+// and holds C[8*(v/4) + 4*(l/32) + v%4][l%32] in element v of the result.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Position of key (or query) offset x inside a 16-wide group when a transposed
+// operand is staged in LDS: swap bits 2 and 3.  A 32x32 accumulator lane holds
+// offsets {8a + 4h + q}; after the swap those 8 offsets are contiguous, so the
+// accumulator can be fed back as an MFMA operand without moving data between
+// lanes, and the matching operand is one 16-byte LDS read.
+__device__ __forceinline__ int perm16(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
+  return z;
+}
+
+}  // namespace fm
+
+namespace fm {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives, as element e (0..3), the 16-bit value number (i % 4) of the
+// 8-byte chunk addressed by lane 4*e + i/4.  If lane 4*e + c of a group points
+// at row r_e, columns c0 + 4c of a row-major tile, lane i of the group gets
+// rows r_0..r_3 of column c0 + i: four k-values of a "column" operand.
+__device__ __forceinline__ i16x4 lds_read_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<bf16*>(p)));
+}
+
+__device__ __forceinline__ bf16x8 cat_bf16(i16x4 lo, i16x4 hi) {
+  i16x8 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ const bf16x8& as_bf16x8(const bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+}  // namespace fm

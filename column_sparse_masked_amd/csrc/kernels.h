@@ -1,0 +1,68 @@
+// Launch interfaces between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fm {
+
+struct TileArgs {
+  const int4* bounds;
+  int* kbsum;
+  uint8_t* cls;
+  int* cnt_q;
+  int* cnt_k;
+  uint16_t* list_q;
+  uint16_t* list_k;
+  uint32_t* fwd_queue;
+  uint32_t* bwd_queue;
+  uint32_t* counters;
+  int B, H, Hm, Sq, Sk, nQ, nK;
+};
+
+struct FwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;
+  const int4* bounds;
+  const uint16_t* list_q;
+  const int* cnt_q;
+  const uint32_t* queue;
+  uint32_t* counters;
+  int B, H, Hm, Sq, Sk, nQ, nK;
+  float scale_log2;   // softmax_scale * log2(e)
+};
+
+struct BwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* o;
+  const __bf16* dout;
+  const float* lse;
+  const int4* bounds;
+  const uint16_t* list_k;
+  const int* cnt_k;
+  const uint32_t* queue;
+  uint32_t* counters;
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  float* dq_acc;      // fp32 [B][H][Sq][D]
+  float* delta;       // fp32 [B][H][Sq]
+  int B, H, Hm, Sq, Sk, nQ, nK;
+  float scale;        // softmax_scale
+  float scale_log2;   // softmax_scale * log2(e)
+};
+
+hipError_t launch_tile_bounds(const TileArgs& a, hipStream_t stream);
+hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream);
+hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
+
+// Workgroups per compute unit the persistent kernels are sized for.
+int fwd_blocks_per_cu(int head_dim);
+int bwd_blocks_per_cu(int head_dim);
+
+}  // namespace fm

@@ -1,0 +1,148 @@
+/*
+ * fm.h - C ABI of libfm, mask-aware (column-sparse masked) attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The mask is the column-wise sparse form described in the FlashMask-3 paper
+ * summary (abstract): for every key column j four int32 values give query-row
+ * interval boundaries, and element (i, j) is masked iff
+ *
+ *        LTS[j] <= i < LTE[j]   or   UTS[j] <= i < UTE[j]
+ *
+ * (half-open intervals; start >= end means empty).  Masked scores are -inf.
+ * A query row with no visible key outputs O = 0, LSE = +inf and gets no
+ * gradient.  The softmax scale is passed in (normally 1/sqrt(head_dim)).
+ *
+ * Layouts (all contiguous, row-major, every tensor pointer 16-byte aligned):
+ *   q, o, dout, dq     bf16  [batch][heads][seqlen_q][head_dim]
+ *   k, v, dk, dv       bf16  [batch][heads][seqlen_k][head_dim]
+ *   lse                fp32  [batch][heads][seqlen_q]   natural-log units
+ *   bounds             int32 [batch][mask_heads][seqlen_k][4] = LTS,LTE,UTS,UTE
+ * mask_heads is 1 (one mask for every head) or heads (one mask per head).
+ * Bound values may be any int32; they are compared as given (clamping them to
+ * [0, seqlen_q] changes nothing).
+ *
+ * Memory: every pointer is a device pointer owned by the caller.  The library
+ * allocates nothing and keeps no per-call state; it caches only the device's
+ * compute-unit count.  `tileinfo` (size from fm_tileinfo_layout) is written by
+ * fm_tile_bounds and then read by fm_attn_fwd / fm_attn_bwd, which also use
+ * two work counters inside it; the counters are left at zero when a call's
+ * kernels finish.  So at most one forward and one backward may be in flight
+ * per tileinfo buffer; calls that share a tileinfo must be ordered (one stream).
+ *
+ * Streams: `stream` is a hipStream_t (NULL = default stream).  Every entry
+ * point validates its arguments on the host, enqueues its kernels on `stream`
+ * and returns without synchronising.
+ *
+ * Errors: validation happens before anything is enqueued; a failed check
+ * returns its code and enqueues nothing.  FM_ERR_HIP means a launch was
+ * rejected by the runtime (hipGetLastError); faults inside kernels surface at
+ * the caller's next synchronisation.  Nothing is printed.
+ */
+#ifndef FM_H
+#define FM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FM_OK = 0,
+  FM_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  FM_ERR_SHAPE = 2,       /* a size is negative or beyond the supported range   */
+  FM_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, or mask_heads not 1 or heads  */
+  FM_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned            */
+  FM_ERR_HIP = 5          /* the HIP runtime rejected a call or launch          */
+} fm_status;
+
+typedef struct {
+  int32_t batch;          /* B  >= 0                                            */
+  int32_t heads;          /* H  >= 1                                            */
+  int32_t mask_heads;     /* Hm, 1 or H                                         */
+  int32_t seqlen_q;       /* Sq >= 0                                            */
+  int32_t seqlen_k;       /* Sk >= 0                                            */
+  int32_t head_dim;       /* D, 64 or 128                                       */
+  float softmax_scale;    /* multiplies q.k before the softmax                  */
+} fm_problem;
+
+/* Byte offsets of the parts of a tileinfo buffer (each 256-byte aligned), as
+ * written by fm_tile_bounds.  nQ = ceil(Sq/block_q), nK = ceil(Sk/block_k).
+ *   counters  uint32[16]: [0] forward items, [1] backward items,
+ *             [2],[3] forward / backward next-item counters, [4],[5] exit counters
+ *   kbsum     int32 [B][Hm][nK][8]  per key block, over its columns j < Sk, the
+ *             min and max of each bound clamped to [0, Sq]:
+ *             LTS min, LTS max, LTE min, LTE max, UTS min, UTS max, UTE min, UTE max
+ *   cls       uint8 [B][Hm][nQ][nK] tile class: 0 skip, 1 full, 2 partial
+ *   cnt_q     int32 [B][Hm][nQ]     non-skipped tiles per query block
+ *   cnt_k     int32 [B][Hm][nK]     non-skipped tiles per key block
+ *   list_q    uint16[B][Hm][nQ][nK] per query block, its non-skipped key blocks in
+ *             increasing order (first cnt_q entries), bit 15 set if partial
+ *   list_k    uint16[B][Hm][nK][nQ] per key block, its non-skipped query blocks
+ *   fwd_queue uint32[B*H*nQ]         forward items (b*H+h)*nQ+qb, most tiles first
+ *   bwd_queue uint32[B*H*nK]         backward items (b*H+h)*nK+kb, most tiles first */
+typedef struct {
+  int32_t block_q, block_k, n_qblocks, n_kblocks;
+  size_t counters, kbsum, cls, cnt_q, cnt_k, list_q, list_k, fwd_queue, bwd_queue;
+  size_t total;           /* bytes the caller must allocate                     */
+} fm_tileinfo_layout;
+
+/* Human-readable name of a status code (static string). */
+const char* fm_status_str(fm_status status);
+
+/* Tile shape used by the kernels (block_q query rows x block_k key columns). */
+fm_status fm_tile_shape(const fm_problem* p, int32_t* block_q, int32_t* block_k);
+
+/* Size and layout of the tileinfo buffer for problem p (host only). */
+fm_status fm_tileinfo_layout_query(const fm_problem* p, fm_tileinfo_layout* out);
+
+/* Bytes of device workspace fm_attn_bwd needs: an fp32 dQ accumulator
+ * [B][H][Sq][D] followed by fp32 [B][H][Sq] row terms (host only). */
+fm_status fm_bwd_workspace_bytes(const fm_problem* p, size_t* bytes);
+
+/* Number of compute units of the current device (queried once, then cached). */
+fm_status fm_device_cu_count(int32_t* cus);
+
+/*
+ * fm_tile_bounds - classify every (query block, key block) tile.
+ * Paper summary, abstract: the column-wise sparse mask stores query-axis
+ * interval boundaries indexed by key positions, which lets whole tiles be
+ * recognised as fully masked (skipped), unmasked (full) or mixed (partial).
+ * Reads `bounds`; writes every part of `tileinfo` and zeroes its counters.
+ * Three kernels: key-block min/max, tile classification with per-block lists,
+ * and the cost-sorted work queues (heaviest items first).
+ */
+fm_status fm_tile_bounds(const fm_problem* p, const int32_t* bounds, void* tileinfo, void* stream);
+
+/*
+ * fm_attn_fwd - masked scaled-dot-product attention forward.
+ * For every query row i: O_i = sum_j softmax_j(scale * q_i.k_j, masked -> -inf) v_j,
+ * LSE_i = log sum_j exp(scale * q_i.k_j) over visible j (+inf if none).
+ * Skipped tiles are never touched; the elementwise mask is evaluated only on
+ * partial tiles.  bf16 MFMA with fp32 accumulation; O rounded to nearest even.
+ * Needs a tileinfo from fm_tile_bounds for the same problem and bounds.
+ */
+fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const void* v,
+                      const int32_t* bounds, void* tileinfo, void* o, float* lse, void* stream);
+
+/*
+ * fm_attn_bwd - gradients of fm_attn_fwd given dL/dO.
+ * With P = exp(scale * q.k - LSE) (0 where masked), dP = dO v^T,
+ * Delta_i = sum_d dO_id O_id, dS = P (dP - Delta):
+ *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+ * `o` and `lse` are the forward's outputs.  `workspace` must hold
+ * fm_bwd_workspace_bytes bytes, 16-byte aligned; its contents on entry do not
+ * matter.  dQ is accumulated in fp32 with atomics, so its last bits can vary
+ * from run to run; dK and dV are deterministic.
+ */
+fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
+                      const void* o, const void* dout, const float* lse,
+                      const int32_t* bounds, void* tileinfo,
+                      void* dq, void* dk, void* dv, void* workspace, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FM_H */

@@ -1,0 +1,112 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+and compare with the fp64 oracle.
+
+Tolerances (fixed by the evaluation contract for this library):
+  O      max-abs <= 2e-2 over the tensor,
+  dQ/dK/dV  relative L2 = ||x - ref|| / ||ref|| <= 1e-2 per tensor,
+  LSE    max-abs <= 1e-3 on finite entries, +inf at the same positions,
+  tile classes, key-block summaries, counts, lists: bit-exact.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+
+O_TOL = 2e-2
+GRAD_TOL = 1e-2
+LSE_TOL = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(w, tensors=None, device="cuda", want_bwd=True):
+    """Upload a workload, run tile pass + forward (+ backward) on the GPU and
+    return numpy results (float64) and the tileinfo dictionary."""
+    import torch
+    from column_sparse_masked_amd.api import MaskedAttention, to_device_bf16, to_device_bounds
+    q, k, v, do = tensors if tensors is not None else w.draw()
+    tq, tk, tv, tdo = (to_device_bf16(x, device) for x in (q, k, v, do))
+    tb = to_device_bounds(w.bounds, device)
+    att = MaskedAttention.for_workload(w, device)
+    att.tile_bounds(tb)
+    o, lse = att.forward(tq, tk, tv, tb)
+    res = {"o": o, "lse": lse}
+    if want_bwd:
+        dq, dk, dv = att.backward(tq, tk, tv, o, tdo, lse, tb)
+        res.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    out = {n: t.float().cpu().numpy().astype(np.float64) for n, t in res.items()}
+    out["tileinfo"] = att.read_tileinfo()
+    return out, (q, k, v, do)
+
+
+def rel_l2(x, ref):
+    nr = np.linalg.norm(ref)
+    if nr == 0:
+        return float(np.linalg.norm(x))
+    return float(np.linalg.norm(x - ref) / nr)
+
+
+def check_lse(got, ref):
+    ref_inf = np.isposinf(ref)
+    assert np.array_equal(np.isposinf(got), ref_inf), "LSE +inf positions differ"
+    fin = ~ref_inf
+    if fin.any():
+        err = float(np.abs(got[fin] - ref[fin]).max())
+        assert err <= LSE_TOL, f"LSE max-abs {err}"
+
+
+def check_full(w, got, tensors, label=""):
+    """Complete oracle comparison (small problems)."""
+    up = oracle.upcast_bf16
+    q, k, v, do = tensors
+    ro, rl, rdq, rdk, rdv = oracle.attention(up(q), up(k), up(v), up(do), w.bounds, w.scale)
+    err_o = float(np.abs(got["o"] - ro).max()) if ro.size else 0.0
+    assert err_o <= O_TOL, f"{label} O max-abs {err_o}"
+    check_lse(got["lse"], rl)
+    errs = {}
+    for n, r in (("dq", rdq), ("dk", rdk), ("dv", rdv)):
+        if n in got:
+            errs[n] = rel_l2(got[n], r)
+            assert errs[n] <= GRAD_TOL, f"{label} {n} rel-L2 {errs[n]}"
+    say(f"{label}: O max-abs {err_o:.3e} " + " ".join(f"{n} {e:.3e}" for n, e in errs.items()))
+    return err_o, errs
+
+
+def check_tileinfo(w, ti):
+    """Bit-exact tile pass against the oracle's classification."""
+    kbsum, cls, cq, ck = oracle.classify(w.bounds, w.Sq, 128, 128)
+    assert np.array_equal(ti["kbsum"], kbsum), "kbsum differs"
+    assert np.array_equal(ti["cls"], cls), "tile classes differ"
+    assert np.array_equal(ti["cnt_q"], cq), "cnt_q differs"
+    assert np.array_equal(ti["cnt_k"], ck), "cnt_k differs"
+    B, Hm, nQ, nK = cls.shape
+    for b in range(B):
+        for hm in range(Hm):
+            for qb in range(nQ):
+                row = cls[b, hm, qb]
+                kbs = np.nonzero(row)[0]
+                want = kbs | np.where(row[kbs] == 2, 0x8000, 0)
+                assert np.array_equal(ti["list_q"][b, hm, qb, :kbs.size], want), (b, hm, qb)
+            for kb in range(nK):
+                col = cls[b, hm, :, kb]
+                qbs = np.nonzero(col)[0]
+                want = qbs | np.where(col[qbs] == 2, 0x8000, 0)
+                assert np.array_equal(ti["list_k"][b, hm, kb, :qbs.size], want), (b, hm, kb)
+    # queues: a permutation of every item, tile counts non-increasing
+    H = w.H
+    for name, cnt, nb in (("fwd_queue", cq, nQ), ("bwd_queue", ck, nK)):
+        qu = ti[name].astype(np.int64)
+        assert np.array_equal(np.sort(qu), np.arange(B * H * nb)), name
+        bh, blk = qu // nb, qu % nb
+        b_, h_ = bh // H, bh % H
+        cost = cnt[b_, 0 if Hm == 1 else h_, blk]
+        assert np.all(np.diff(np.minimum(cost, 4095)) <= 0), f"{name} not sorted by tile count"
+    c = ti["counters"]
+    assert c[0] == B * H * nQ and c[1] == B * H * nK and c[2] == 0 and c[3] == 0

@@ -1,0 +1,144 @@
+"""The C ABI on the host (no GPU): exported symbols, argument checks, layout.
+
+Only calls that fail validation (which returns before any HIP call) or that
+are host-only queries are made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from column_sparse_masked_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = _declared_functions()
+    assert {"fm_tile_bounds", "fm_attn_fwd", "fm_attn_bwd"} <= set(names)
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_sizes_match_header():
+    assert ctypes.sizeof(L.Problem) == 28
+    assert ctypes.sizeof(L.TileinfoLayout) == 16 + 10 * 8
+
+
+def _p(**kw):
+    base = dict(batch=1, heads=2, mask_heads=1, seqlen_q=300, seqlen_k=500, head_dim=128, softmax_scale=0.1)
+    base.update(kw)
+    return L.problem(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), L.FM_ERR_SHAPE),
+    (dict(heads=0), L.FM_ERR_SHAPE),
+    (dict(seqlen_q=-5), L.FM_ERR_SHAPE),
+    (dict(seqlen_k=-1), L.FM_ERR_SHAPE),
+    (dict(seqlen_q=32768 * 128 + 1), L.FM_ERR_SHAPE),
+    (dict(head_dim=96), L.FM_ERR_UNSUPPORTED),
+    (dict(head_dim=256), L.FM_ERR_UNSUPPORTED),
+    (dict(mask_heads=3, heads=4), L.FM_ERR_UNSUPPORTED),
+    (dict(softmax_scale=0.0), L.FM_ERR_UNSUPPORTED),
+    (dict(softmax_scale=-1.0), L.FM_ERR_UNSUPPORTED),
+    (dict(softmax_scale=float("nan")), L.FM_ERR_UNSUPPORTED),
+    (dict(softmax_scale=float("inf")), L.FM_ERR_UNSUPPORTED),
+    (dict(batch=65536, heads=1024, seqlen_q=4096), L.FM_ERR_SHAPE),
+])
+def test_bad_problems_rejected_everywhere(kw, code):
+    p = _p(**kw)
+    bq, bk = ctypes.c_int32(), ctypes.c_int32()
+    assert L.lib.fm_tile_shape(ctypes.byref(p), ctypes.byref(bq), ctypes.byref(bk)) == code
+    lay = L.TileinfoLayout()
+    assert L.lib.fm_tileinfo_layout_query(ctypes.byref(p), ctypes.byref(lay)) == code
+    n = ctypes.c_size_t()
+    assert L.lib.fm_bwd_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == code
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.lib.fm_tile_bounds(ctypes.byref(p), fake, fake, None) == code
+    assert L.lib.fm_attn_fwd(ctypes.byref(p), *([fake] * 7), None) == code
+    assert L.lib.fm_attn_bwd(ctypes.byref(p), *([fake] * 12), None) == code
+
+
+def test_null_problem_and_outputs():
+    assert L.lib.fm_tile_shape(None, None, None) == L.FM_ERR_NULL
+    p = _p()
+    assert L.lib.fm_tile_shape(ctypes.byref(p), None, None) == L.FM_ERR_NULL
+    assert L.lib.fm_tileinfo_layout_query(ctypes.byref(p), None) == L.FM_ERR_NULL
+    assert L.lib.fm_bwd_workspace_bytes(ctypes.byref(p), None) == L.FM_ERR_NULL
+    assert L.lib.fm_device_cu_count(None) == L.FM_ERR_NULL
+
+
+def test_null_tensors_rejected_before_launch():
+    p = _p()
+    ok = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first
+    assert L.lib.fm_tile_bounds(ctypes.byref(p), ok, None, None) == L.FM_ERR_NULL
+    assert L.lib.fm_tile_bounds(ctypes.byref(p), None, ok, None) == L.FM_ERR_NULL
+    args = [ok] * 7
+    for i in range(7):
+        a = list(args)
+        a[i] = None
+        assert L.lib.fm_attn_fwd(ctypes.byref(p), *a, None) == L.FM_ERR_NULL, i
+    args = [ok] * 12
+    for i in range(12):
+        a = list(args)
+        a[i] = None
+        assert L.lib.fm_attn_bwd(ctypes.byref(p), *a, None) == L.FM_ERR_NULL, i
+
+
+def test_misaligned_tensors_rejected_before_launch():
+    p = _p()
+    ok = ctypes.c_void_p(1 << 20)
+    bad = ctypes.c_void_p((1 << 20) + 8)
+    assert L.lib.fm_tile_bounds(ctypes.byref(p), ok, bad, None) == L.FM_ERR_ALIGN   # tileinfo needs 256
+    assert L.lib.fm_tile_bounds(ctypes.byref(p), bad, ok, None) == L.FM_ERR_ALIGN   # bounds need 16
+    for i in range(7):
+        a = [ok] * 7
+        a[i] = bad
+        want = L.FM_OK if i == 6 else L.FM_ERR_ALIGN   # lse only needs 4-byte alignment
+        if want == L.FM_OK:
+            continue
+        assert L.lib.fm_attn_fwd(ctypes.byref(p), *a, None) == want, i
+    for i in range(12):
+        a = [ok] * 12
+        a[i] = bad
+        if i == 5:     # lse
+            continue
+        assert L.lib.fm_attn_bwd(ctypes.byref(p), *a, None) == L.FM_ERR_ALIGN, i
+
+
+def test_status_strings():
+    for c in range(6):
+        s = L.status_str(c)
+        assert s.startswith("FM_")
+    assert L.status_str(99) == "unknown fm_status"
+
+
+@pytest.mark.parametrize("B,H,Hm,Sq,Sk", [(1, 2, 1, 1024, 1024), (2, 3, 3, 300, 517),
+                                          (1, 16, 1, 8192, 65536), (1, 1, 1, 1, 1), (0, 1, 1, 5, 5),
+                                          (1, 4, 1, 0, 100), (1, 4, 4, 100, 0)])
+def test_tileinfo_layout(B, H, Hm, Sq, Sk):
+    p = _p(batch=B, heads=H, mask_heads=Hm, seqlen_q=Sq, seqlen_k=Sk)
+    lay = L.tileinfo_layout(p)
+    nQ, nK = -(-Sq // 128), -(-Sk // 128)
+    assert (lay.block_q, lay.block_k, lay.n_qblocks, lay.n_kblocks) == (128, 128, nQ, nK)
+    parts = [("counters", 64), ("kbsum", B * Hm * nK * 32), ("cls", B * Hm * nQ * nK),
+             ("cnt_q", B * Hm * nQ * 4), ("cnt_k", B * Hm * nK * 4),
+             ("list_q", B * Hm * nQ * nK * 2), ("list_k", B * Hm * nK * nQ * 2),
+             ("fwd_queue", B * H * nQ * 4), ("bwd_queue", B * H * nK * 4)]
+    end = 0
+    for name, size in parts:
+        off = getattr(lay, name)
+        assert off % 256 == 0 and off >= end, name
+        end = off + size
+    assert lay.total >= end
+    ws = L.bwd_workspace_bytes(p)
+    assert ws >= B * H * Sq * (128 * 4 + 4)
