@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of column-sparse masked attention (forward + backward) on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--seed S]
+
+One step is the whole hot path over one batch: the tile pass
+(fm_tile_bounds), the forward (fm_attn_fwd) and the backward (fm_attn_bwd),
+all through the C ABI, on inputs already resident in device memory.  W untimed
+steps, then K timed steps bracketed by torch.cuda.synchronize().
+
+The throughput is mask-effective: forward 4*D*nnz and backward 10*D*nnz flops
+per (batch, head), nnz being the number of unmasked (query, key) pairs, so
+masked work the kernels skip is not credited and masked elements they compute
+inside partial tiles are not credited either.
+
+Printed: one JSON line with the whole-step throughput, the roofline of the
+dominant kernel (timed live with HIP events recorded by the library right
+around that kernel, on the stream it runs on) and the fp64 CPU oracle timed on
+a bounded sample of the same workload on the host cores (a reported baseline,
+not a target).  The default workload is the causal sliding window (w = 1024)
+at B=2, H=16, S=8192, D=128, seed 2; --config picks another of the five
+evaluation workloads (1 causal documents S=1K D=64, 3 share-question S=32K,
+4 documents with prefix-LM S=128K, 5 one context-parallel rank's share).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "mask-effective attention fwd+bwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
+# Dense bf16 MFMA peak of MI355X: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
+PEAK_BF16_TFLOPS = 2516.6
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--seed", type=int, default=None, help="default: the config's index")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the CPU oracle sample (at least one head is always run)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="leave out the oracle timing (profiling runs)")
+    return ap.parse_args(argv)
+
+
+def kernel_source_digest(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "column_sparse_masked_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload_tag: str, digest: str):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 PMC
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration),
+    or None when there is none or it was taken on other kernel source."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload_tag}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith("#"):
+                key, val = ln.split(":", 1)
+                vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, tensors, budget_s):
+    """The fp64 oracle (forward + backward) on whole heads, in (b, h) order,
+    until the time budget is spent; mask-effective TFLOP/s of what ran."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS default is one thread per core
+        cores = os.cpu_count() or 1
+    q, k, v, do = tensors
+    nnz = w.nnz_per_head()
+    up = oracle.upcast_bf16
+    done, flops = [], 0.0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            hm = 0 if w.Hm == 1 else h
+            bh = w.bounds[b, hm]
+            qh, kh, vh, doh = up(q[b, h]), up(k[b, h]), up(v[b, h]), up(do[b, h])
+            oh, lse = oracle.head_forward(qh, kh, vh, bh, w.scale)
+            oracle.head_backward(qh, kh, vh, doh, bh, w.scale, lse=lse)
+            done.append((b, h))
+            flops += 14.0 * w.D * float(nnz[b, hm])
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        else:
+            continue
+        break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{len(done)} of {w.B * w.H} (batch, head) pairs of the same workload, whole "
+                  f"forward+backward in float64 numpy, {dt:.1f} s",
+    }
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(no sharding, no collectives).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from column_sparse_masked_amd import _lib, masks
+    from column_sparse_masked_amd.api import MaskedAttention, to_device_bf16, to_device_bounds
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    w = masks.config(args.config, args.seed)
+    print(f"# workload {masks.CONFIG_NAMES[args.config]} seed {w.seed}", file=sys.stderr, flush=True)
+    tensors = w.draw()
+    tq, tk, tv, tdo = (to_device_bf16(x, dev) for x in tensors)
+    tb = to_device_bounds(w.bounds, dev)
+    att = MaskedAttention.for_workload(w, dev)
+    o = torch.empty((w.B, w.H, w.Sq, w.D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+
+    nnz = w.nnz_total()
+    f_fwd, f_bwd = 4.0 * w.D * nnz, 10.0 * w.D * nnz
+
+    def new_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()          # creates the HIP event
+        return e
+
+    def step(ev=None):
+        if ev is not None:
+            ev["s0"].record()
+        att.tile_bounds(tb)
+        if ev is not None:
+            ev["s1"].record()
+            _lib.set_kernel_events(ev["fk0"], ev["fk1"])
+        att.forward(tq, tk, tv, tb, o=o, lse=lse)
+        if ev is not None:
+            ev["s2"].record()
+            _lib.set_kernel_events(ev["bk0"], ev["bk1"])
+        att.backward(tq, tk, tv, o, tdo, lse, tb, dq=dq, dk=dk, dv=dv)
+        if ev is not None:
+            _lib.set_kernel_events(None, None)
+            ev["s3"].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# warmup {args.warmup} steps done", file=sys.stderr, flush=True)
+
+    evs = [{n: new_event() for n in ("s0", "s1", "s2", "s3", "fk0", "fk1", "bk0", "bk1")}
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"# timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    def avg_ms(a, b):
+        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+
+    t_tile, t_fwd, t_bwd = avg_ms("s0", "s1"), avg_ms("s1", "s2"), avg_ms("s2", "s3")
+    k_fwd, k_bwd = avg_ms("fk0", "fk1"), avg_ms("bk0", "bk1")
+    ms_per_step = wall / args.steps * 1e3
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: the longer of the forward and backward attention kernels
+    if k_bwd >= k_fwd:
+        kname, kflops, kms, srcs = "attn_bwd_kernel", f_bwd, k_bwd, ["bwd.hip", "common.h"]
+    else:
+        kname, kflops, kms, srcs = "attn_fwd_kernel", f_fwd, k_fwd, ["fwd.hip", "common.h"]
+    achieved = kflops / (kms * 1e-3) / 1e12
+    tag = f"cfg{args.config}_seed{w.seed}"
+    roofline = {
+        "bound": "mfma",
+        "kernel": kname,
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": read_traffic(kname, tag, kernel_source_digest(srcs)),
+        "avg_kernel_ms": round(kms, 4),
+        "algorithmic_flops_per_launch": kflops,
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": masks.CONFIG_NAMES[args.config],
+            "seed": w.seed, "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "D": w.D,
+            "nnz_per_head_mean": nnz / (w.B * w.H),
+            "mask_flops_fwd_bwd": f_fwd + f_bwd,
+        },
+        "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "stages_ms": {"tile_bounds": round(t_tile, 4), "fwd": round(t_fwd, 4), "bwd": round(t_bwd, 4)},
+        "tflops_fwd_kernel": round(f_fwd / (k_fwd * 1e-3) / 1e12, 2),
+        "tflops_bwd_kernel": round(f_bwd / (k_bwd * 1e-3) / 1e12, 2),
+        "tflops_without_tile_pass": round((f_fwd + f_bwd) / ((t_fwd + t_bwd) * 1e-3) / 1e12, 2),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print(f"# oracle sample on the host ({args.cpu_seconds:.0f} s budget)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, tensors, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

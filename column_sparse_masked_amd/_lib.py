@@ -18,7 +18,27 @@ FM_OK, FM_ERR_NULL, FM_ERR_SHAPE, FM_ERR_UNSUPPORTED, FM_ERR_ALIGN, FM_ERR_HIP =
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m column_sparse_masked_amd.build`")
+
+# torch ships its own copy of the HIP runtime.  libfm must bind to that same
+# copy, or the process holds two runtimes and the streams torch hands over are
+# foreign handles to libfm (every launch is then rejected).  Loading torch
+# first makes the dynamic loader resolve libfm's runtime dependency to it.
+import torch  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_mapped() -> list[str]:
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+if len(_hip_runtimes_mapped()) > 1:
+    raise ImportError("two HIP runtimes are loaded in this process (libfm would not share "
+                      f"torch's streams): {_hip_runtimes_mapped()}")
 
 
 class Problem(ctypes.Structure):
@@ -147,3 +167,19 @@ def alloc_buffers(p: Problem, device) -> Buffers:
     ws = torch.empty(max(bwd_workspace_bytes(p), 256), dtype=torch.uint8, device=device)
     assert ti.data_ptr() % 256 == 0 and ws.data_ptr() % 16 == 0
     return Buffers(ti, ws, L)
+
+
+lib.fm_set_kernel_events.argtypes = [_vp, _vp]
+lib.fm_set_kernel_events.restype = ctypes.c_int
+
+
+def set_kernel_events(begin, end):
+    """Record the torch.cuda.Event pair ``begin``/``end`` around the main
+    attention kernel of the following fm_attn_fwd / fm_attn_bwd calls on this
+    thread; ``None, None`` turns it off.  The events must already exist on the
+    device (torch creates them at their first record)."""
+    if begin is None and end is None:
+        _check(lib.fm_set_kernel_events(None, None), "fm_set_kernel_events")
+        return
+    _check(lib.fm_set_kernel_events(ctypes.c_void_p(begin.cuda_event), ctypes.c_void_p(end.cuda_event)),
+           "fm_set_kernel_events")

@@ -82,6 +82,8 @@ fm_status cu_count(int* out) {
 
 bool tensor_ok(const void* p) { return p != nullptr; }
 
+thread_local fm::KernelEvents g_events;
+
 }  // namespace
 
 extern "C" {
@@ -145,6 +147,13 @@ fm_status fm_device_cu_count(int32_t* cus) {
   fm_status st = cu_count(&n);
   if (st == FM_OK) *cus = n;
   return st;
+}
+
+fm_status fm_set_kernel_events(void* begin, void* end) {
+  if ((begin == nullptr) != (end == nullptr)) return FM_ERR_NULL;
+  g_events.begin = static_cast<hipEvent_t>(begin);
+  g_events.end = static_cast<hipEvent_t>(end);
+  return FM_OK;
 }
 
 fm_status fm_tile_bounds(const fm_problem* p, const int32_t* bounds, void* tileinfo, void* stream) {
@@ -211,8 +220,9 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
   const long items = (long)p->batch * p->heads * L.nQ;
   const long slots = (long)cus * fm::fwd_blocks_per_cu(p->head_dim);
   const int grid = (int)(items < slots ? items : slots);
-  return fm::launch_attn_fwd(a, p->head_dim, grid, (hipStream_t)stream) == hipSuccess ? FM_OK
-                                                                                      : FM_ERR_HIP;
+  return fm::launch_attn_fwd(a, p->head_dim, grid, (hipStream_t)stream, g_events) == hipSuccess
+             ? FM_OK
+             : FM_ERR_HIP;
 }
 
 fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
@@ -270,7 +280,7 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   const long items = (long)p->batch * p->heads * L.nK;
   const long slots = (long)cus * fm::bwd_blocks_per_cu(p->head_dim);
   const int grid = (int)(items < slots ? items : slots);
-  return fm::launch_attn_bwd(a, p->head_dim, grid, s) == hipSuccess ? FM_OK : FM_ERR_HIP;
+  return fm::launch_attn_bwd(a, p->head_dim, grid, s, g_events) == hipSuccess ? FM_OK : FM_ERR_HIP;
 }
 
 }  // extern "C"

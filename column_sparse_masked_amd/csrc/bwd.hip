@@ -275,20 +275,26 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
 
 int bwd_blocks_per_cu(int) { return 1; }
 
-hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, hipStream_t stream) {
+hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, hipStream_t stream,
+                           const KernelEvents& ev) {
   const long rows = (long)a.B * a.H * a.Sq;
   const long n8 = rows * head_dim / 8;
   const unsigned pre_grid = (unsigned)((n8 + 255) / 256);
+  hipError_t err;
   if (head_dim == 128)
     bwd_pre_kernel<128><<<pre_grid, 256, 0, stream>>>(a.o, a.dout, a.delta, a.dq_acc, rows);
   else
     bwd_pre_kernel<64><<<pre_grid, 256, 0, stream>>>(a.o, a.dout, a.delta, a.dq_acc, rows);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (ev.begin && (err = hipEventRecord(ev.begin, stream)) != hipSuccess) return err;
   if (grid > 0) {
     if (head_dim == 128)
       attn_bwd_kernel<128><<<grid, 256, 0, stream>>>(a);
     else
       attn_bwd_kernel<64><<<grid, 256, 0, stream>>>(a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  if (ev.end && (err = hipEventRecord(ev.end, stream)) != hipSuccess) return err;
   dq_convert_kernel<<<pre_grid, 256, 0, stream>>>(a.dq_acc, a.dq, n8);
   return hipGetLastError();
 }

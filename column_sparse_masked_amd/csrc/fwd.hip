@@ -195,12 +195,17 @@ void attn_fwd_kernel(const FwdArgs a) {
 
 int fwd_blocks_per_cu(int) { return 2; }
 
-hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream) {
+hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream,
+                           const KernelEvents& ev) {
+  hipError_t err;
+  if (ev.begin && (err = hipEventRecord(ev.begin, stream)) != hipSuccess) return err;
   if (head_dim == 128)
     attn_fwd_kernel<128><<<grid, 256, 0, stream>>>(a);
   else
     attn_fwd_kernel<64><<<grid, 256, 0, stream>>>(a);
-  return hipGetLastError();
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (ev.end && (err = hipEventRecord(ev.end, stream)) != hipSuccess) return err;
+  return hipSuccess;
 }
 
 }  // namespace fm

@@ -58,8 +58,16 @@ struct BwdArgs {
 };
 
 hipError_t launch_tile_bounds(const TileArgs& a, hipStream_t stream);
-hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream);
-hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
+// Optional events recorded right before / after the main attention kernel
+// (null: not recorded).
+struct KernelEvents {
+  hipEvent_t begin = nullptr, end = nullptr;
+};
+
+hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream,
+                           const KernelEvents& ev);
+hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, hipStream_t stream,
+                           const KernelEvents& ev);
 
 // Workgroups per compute unit the persistent kernels are sized for.
 int fwd_blocks_per_cu(int head_dim);

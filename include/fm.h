@@ -104,6 +104,16 @@ fm_status fm_bwd_workspace_bytes(const fm_problem* p, size_t* bytes);
 /* Number of compute units of the current device (queried once, then cached). */
 fm_status fm_device_cu_count(int32_t* cus);
 
+/* Benchmark hook.  While set, every fm_attn_fwd / fm_attn_bwd call made from
+ * this host thread records the caller's hipEvent_t `begin` on its stream right
+ * before launching its main attention kernel and `end` right after it, so that
+ * hipEventElapsedTime(begin, end) spans that one kernel (the backward's
+ * prologue and dQ conversion kernels fall outside).  Both events must have
+ * been created with timing enabled.  fm_set_kernel_events(NULL, NULL) turns
+ * the hook off; giving only one of the two is FM_ERR_NULL.  Nothing else about
+ * the calls changes; a failed record makes the call return FM_ERR_HIP. */
+fm_status fm_set_kernel_events(void* begin, void* end);
+
 /*
  * fm_tile_bounds - classify every (query block, key block) tile.
  * Paper summary, abstract: the column-wise sparse mask stores query-axis
