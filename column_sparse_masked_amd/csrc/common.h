@@ -20,6 +20,7 @@ constexpr int kCtrFwdItems = 0, kCtrBwdItems = 1, kCtrFwdNext = 2, kCtrBwdNext =
 typedef __bf16 bf16;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -71,6 +72,37 @@ __device__ __forceinline__ i16x4 lds_read_tr(const bf16* p) {
 __device__ __forceinline__ bf16x8 cat_bf16(i16x4 lo, i16x4 hi) {
   i16x8 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, r);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+
+// Buffer resource over [base, base + bytes): raw 16-byte loads through it
+// return zeros at offsets at or past `bytes` (the hardware range check), which
+// zero-fills ragged tiles without branches.  bytes < 2^31.
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ bf16x8 buf_load16(BufRsrc r, uint32_t byte_offset) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_offset, 0, 0));
+}
+
+// Returns x unchanged, but opaque to the optimiser: a per-lane base offset
+// passed through this inside a loop is not hoisted out of it, so the constant
+// parts of the addresses built on it fold into the instructions' immediate
+// offset fields instead of occupying one register each for the whole kernel.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Entry i of a uint16 tile list through an aligned 32-bit load, so that a
+// list walked by a whole workgroup is read with scalar loads.
+__device__ __forceinline__ int list_entry(const uint16_t* lst, int i) {
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(lst + i);
+  const uint32_t word = *reinterpret_cast<const uint32_t*>(addr & ~(uintptr_t)3);
+  return (int)((addr & 2) ? (word >> 16) : (word & 0xffffu));
 }
 
 __device__ __forceinline__ const bf16x8& as_bf16x8(const bf16* p) {

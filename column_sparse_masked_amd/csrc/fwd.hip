@@ -5,13 +5,19 @@
 // Persistent grid: each workgroup (4 waves) repeatedly takes the next item
 // (batch*head, query block) from the cost-sorted queue built by the tile pass,
 // holds that block's 128 query rows in registers (32 rows per wave) and walks
-// the block's list of non-skipped key blocks.  Per key block, K and V are
-// staged row-major in LDS; each wave computes S^T = K Q^T (32 keys x 32 rows
-// per MFMA), applies the elementwise interval test only on partial (or
-// ragged) tiles, updates an online softmax in the log2 domain and accumulates
-// O^T += V^T P^T, reading V^T with transposed LDS loads.  Keeping S^T (not S)
-// lets the accumulator of one MFMA be the B operand of the next with no data
-// movement between lanes.
+// the block's list of non-skipped key blocks.  Per key block, K is staged
+// row-major and V transposed in LDS, so that every MFMA operand read is one
+// 16-byte LDS load.  Each wave computes S^T = K Q^T (32 keys x 32 rows per
+// MFMA), applies the elementwise interval test only on partial (or ragged)
+// tiles, updates an online softmax in the log2 domain and accumulates
+// O^T += V^T P^T.  Keeping S^T (not S) lets the accumulator of one MFMA be the
+// B operand of the next with no data movement between lanes.
+//
+// The next key block is fetched into registers while the current one
+// computes: K during S, V during the softmax and the PV product, each written
+// to LDS as soon as every wave is done with the previous contents.  Global
+// loads go through buffer resources whose range check zero-fills the rows
+// past the end of a ragged key (or query) range.
 #include <climits>
 
 #include "common.h"
@@ -21,27 +27,107 @@ namespace fm {
 
 template <int D>
 struct alignas(16) FwdSmem {
-  static constexpr int KST = D + 8;    // K row stride (elements): 16-byte row reads
-  static constexpr int VST = D + 16;   // V row stride: 8-byte transposed reads
-  bf16 k[BK * KST];
-  bf16 v[BK * VST];
-  int4 bnd[BK];
+  static constexpr int KST = D + 8;    // K row stride (elements): conflict-free 16-byte row reads
+  static constexpr int VTS = BK + 8;   // V^T row stride (elements)
+  bf16 k[BK * KST];                    // K tile, one key per row
+  bf16 vt[D * VTS];                    // V^T tile, one head-dim column per row, keys in vt_pos order
+  int4 bnd[2][BK];                     // bounds of key blocks t (even/odd), for partial tiles only
   uint32_t item;
 };
+
+// Place of key x (0 <= x < BK) inside a V^T row: bits 2 and 3 of the offset
+// within each group of 16 keys are swapped, so that the 8 keys one lane holds
+// in the P operand of the PV product are 8 neighbouring elements.
+__device__ __forceinline__ int vt_pos(int x) { return (x & ~15) | perm16(x & 15); }
+
+// Global -> register staging of one key block (256 threads).
+//   K: thread t holds column chunk t % CPR (8 head-dim values) of the NK
+//      consecutive rows NK*(t / CPR) ...  (loads and LDS stores then differ
+//      only by constant offsets);
+//   V: thread t holds 4*NV consecutive keys x column chunk (t/8) % CPR, with
+//      the key range chosen so that the transposed 8-byte LDS stores of 16
+//      neighbouring lanes fall on distinct banks.
+template <int D>
+struct Stage {
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int NK = BK * CPR / 256;       // K rows per thread
+  static constexpr int NV = (BK / 4) * CPR / 256; // V key groups (of 4) per thread
+  bf16x8 k[NK];
+  bf16x8 v[4 * NV];
+
+  static __device__ __forceinline__ int k_row(unsigned t) { return NK * (int)(t / CPR); }
+  static __device__ __forceinline__ int k_col(unsigned t) { return (int)(t % CPR); }
+  static __device__ __forceinline__ int v_key(unsigned t) {
+    return 4 * NV * (int)((t & 7u) + 8u * (t / (8u * CPR)));
+  }
+  static __device__ __forceinline__ int v_col(unsigned t) { return (int)((t >> 3) % CPR); }
+};
+
+template <int D>
+__device__ __forceinline__ void load_k(Stage<D>& r, BufRsrc kb, int k0, unsigned t) {
+  using S = Stage<D>;
+  const uint32_t base = opaque(((uint32_t)S::k_row(t) * S::CPR + S::k_col(t)) * 16u) + (uint32_t)k0 * (D * 2);
+#pragma unroll
+  for (int i = 0; i < S::NK; ++i) r.k[i] = buf_load16(kb, base + (uint32_t)i * (D * 2));
+}
+
+template <int D>
+__device__ __forceinline__ void store_k(const Stage<D>& r, bf16* sk, unsigned t) {
+  using S = Stage<D>;
+  constexpr int KST = FwdSmem<D>::KST;
+  bf16* dst = sk + opaque(S::k_row(t) * KST + S::k_col(t) * 8);
+#pragma unroll
+  for (int i = 0; i < S::NK; ++i) *reinterpret_cast<bf16x8*>(dst + i * KST) = r.k[i];
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(Stage<D>& r, BufRsrc vb, int k0, unsigned t) {
+  using S = Stage<D>;
+  const uint32_t base = opaque(((uint32_t)S::v_key(t) * S::CPR + S::v_col(t)) * 16u) + (uint32_t)k0 * (D * 2);
+#pragma unroll
+  for (int q = 0; q < 4 * S::NV; ++q) r.v[q] = buf_load16(vb, base + (uint32_t)q * (D * 2));
+}
+
+template <int D>
+__device__ __forceinline__ void store_vt(const Stage<D>& r, bf16* vt, unsigned t) {
+  using S = Stage<D>;
+  constexpr int VTS = FwdSmem<D>::VTS;
+#pragma unroll
+  for (int i = 0; i < S::NV; ++i) {
+    bf16* dst = vt + opaque((8 * S::v_col(t)) * VTS + vt_pos(S::v_key(t) + 4 * i));
+    // 4 keys x 8 columns -> 8 rows of 4 keys (constant shuffles only, so the
+    // compiler keeps everything in registers)
+    const bf16x16 p01 = __builtin_shufflevector(r.v[4 * i], r.v[4 * i + 1], 0, 8, 1, 9, 2, 10, 3,
+                                                11, 4, 12, 5, 13, 6, 14, 7, 15);
+    const bf16x16 p23 = __builtin_shufflevector(r.v[4 * i + 2], r.v[4 * i + 3], 0, 8, 1, 9, 2, 10,
+                                                3, 11, 4, 12, 5, 13, 6, 14, 7, 15);
+#define FM_VT_ROW(e)                                                                      \
+  *reinterpret_cast<bf16x4*>(dst + (e) * VTS) =                                           \
+      __builtin_shufflevector(p01, p23, 2 * (e), 2 * (e) + 1, 16 + 2 * (e), 17 + 2 * (e))
+    FM_VT_ROW(0); FM_VT_ROW(1); FM_VT_ROW(2); FM_VT_ROW(3);
+    FM_VT_ROW(4); FM_VT_ROW(5); FM_VT_ROW(6); FM_VT_ROW(7);
+#undef FM_VT_ROW
+  }
+}
+
+// Bounds of key k0 + t for an elementwise-masked tile; keys past the end get
+// an interval that covers every row.
+__device__ __forceinline__ int4 load_bnd(BufRsrc bb, int k0, int Sk, int t) {
+  const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(bb, (k0 + t) * 16, 0, 0);
+  return (k0 + t < Sk) ? make_int4(x[0], x[1], x[2], x[3]) : make_int4(INT_MIN, INT_MAX, 0, 0);
+}
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const FwdArgs a) {
   constexpr int NS = D / 16;   // k-steps over the head dimension
   constexpr int ND = D / 32;   // 32-wide blocks of the head dimension
-  constexpr int KST = FwdSmem<D>::KST, VST = FwdSmem<D>::VST;
+  constexpr int KST = FwdSmem<D>::KST, VTS = FwdSmem<D>::VTS;
   __shared__ FwdSmem<D> sm;
 
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const unsigned t = threadIdx.x;
+  const int lane = (int)(t & 63), w = (int)(t >> 6);
   const int li = lane & 31, hh = lane >> 5;
-  const int gc = (lane >> 4) & 1, m16 = lane & 15;
-  // lane offset of the transposed V read: row 4*hh + m16/4, column 16*gc + 4*(m16%4)
-  const int v_lane = (4 * hh + (m16 >> 2)) * VST + 16 * gc + 4 * (m16 & 3);
   // item count and queue entries are range-checked so that a stale or foreign
   // tileinfo cannot make the kernel read outside its tensors
   const uint32_t max_items = (uint32_t)((long)a.B * a.H * a.nQ);
@@ -51,7 +137,9 @@ void attn_fwd_kernel(const FwdArgs a) {
   for (;;) {
     if (t == 0) sm.item = atomicAdd(&a.counters[kCtrFwdNext], 1u);
     __syncthreads();
-    const uint32_t idx = sm.item;
+    // the item is the same for the whole workgroup: keep it (and everything
+    // derived from it) in scalar registers
+    const uint32_t idx = __builtin_amdgcn_readfirstlane(sm.item);
     if (idx >= n_items) break;
     const uint32_t it = min(a.queue[idx], max_items - 1);
     const long bh = it / a.nQ;
@@ -60,17 +148,18 @@ void attn_fwd_kernel(const FwdArgs a) {
     const long bhm = (long)b * a.Hm + (a.Hm == 1 ? 0 : h);
     const int cnt = min(a.cnt_q[bhm * a.nQ + qb], a.nK);
     const uint16_t* lst = a.list_q + (bhm * a.nQ + qb) * (long)a.nK;
+    // buffer resources over this head's Q, K, V and bounds: loads past the
+    // end of the rows return zeros
+    const BufRsrc qbase = make_rsrc(a.q + bh * Sq * (long)D, (uint32_t)Sq * D * 2u);
+    const BufRsrc kbase = make_rsrc(a.k + bh * Sk * (long)D, (uint32_t)Sk * D * 2u);
+    const BufRsrc vbase = make_rsrc(a.v + bh * Sk * (long)D, (uint32_t)Sk * D * 2u);
+    const BufRsrc bbase = make_rsrc(a.bounds + bhm * Sk, (uint32_t)Sk * 16u);
+    // key block list entry -> first key, and whether the tile needs the
+    // elementwise interval test (partial, or ragged at the end of the keys)
+    auto block_start = [&](int e) { return min(e & kListIndex, a.nK - 1) * BK; };
+    auto block_masked = [&](int e, int k0) { return (e & kListPartial) || (k0 + BK > Sk); };
 
     const int qrow = qb * BQ + 32 * w + li;
-    bf16x8 qf[NS];
-    if (qrow < Sq) {
-      const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + (bh * Sq + qrow) * D);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) qf[s] = qp[2 * s + hh];
-    } else {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) qf[s] = zero_bf16x8();
-    }
     f32x16 acc[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d)
@@ -78,90 +167,141 @@ void attn_fwd_kernel(const FwdArgs a) {
       for (int v = 0; v < 16; ++v) acc[d][v] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    const bf16x8* kbase = reinterpret_cast<const bf16x8*>(a.k + bh * Sk * (long)D);
-    const bf16x8* vbase = reinterpret_cast<const bf16x8*>(a.v + bh * Sk * (long)D);
-
-    for (int tt = 0; tt < cnt; ++tt) {
-      const int e = lst[tt];
-      const int kb = min(e & kListIndex, a.nK - 1);
-      const int k0 = kb * BK;
-      const bool need_mask = (e & kListPartial) || (k0 + BK > Sk);
+    if (cnt > 0) {
+      // Q rows of this wave (B operand of S^T = K Q^T); issued first so that
+      // the key-block loads issued after it can stay in flight
+      bf16x8 qf[NS];
+      {
+        const uint32_t qoff = ((uint32_t)qrow * D + 8u * hh) * 2u;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) qf[s] = buf_load16(qbase, qoff + 32u * s);
+      }
+      // ---- first key block: global -> registers -> LDS; second K block in flight ----
+      // List entries are read one block ahead through a buffer resource (a
+      // vector load whose value is the same in every lane).
+      const BufRsrc lbase = make_rsrc(lst, (uint32_t)cnt * 2u);
+      auto list_at = [&](int i) -> uint32_t {
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(lbase, i * 2, 0, 0);
+      };
+      Stage<D> st;
+      int e_cur = __builtin_amdgcn_readfirstlane(list_at(0));
+      int e_next = cnt > 1 ? __builtin_amdgcn_readfirstlane(list_at(1)) : 0;
+      {
+        const int k0 = block_start(e_cur);
+        load_k<D>(st, kbase, k0, t);
+        load_v<D>(st, vbase, k0, t);
+        int4 breg = make_int4(0, 0, 0, 0);
+        if (block_masked(e_cur, k0) && t < BK) breg = load_bnd(bbase, k0, Sk, t);
+        store_k<D>(st, sm.k, t);
+        store_vt<D>(st, sm.vt, t);
+        if (block_masked(e_cur, k0) && t < BK) sm.bnd[0][t] = breg;
+      }
+      if (cnt > 1) load_k<D>(st, kbase, block_start(e_next), t);
       __syncthreads();
-      // ---- stage K and V rows [k0, k0+BK) row-major ----
-#pragma unroll 2
-      for (int c = t; c < BK * D / 8; c += 256) {
-        const int j = c / (D / 8), dc = c % (D / 8);
-        const bool ok = k0 + j < Sk;
-        const long g = (long)k0 * (D / 8) + c;
-        bf16x8 kv = ok ? kbase[g] : zero_bf16x8();
-        bf16x8 vv = ok ? vbase[g] : zero_bf16x8();
-        *reinterpret_cast<bf16x8*>(&sm.k[j * KST + dc * 8]) = kv;
-        *reinterpret_cast<bf16x8*>(&sm.v[j * VST + dc * 8]) = vv;
-      }
-      if (need_mask) {
-        // keys past the end get an interval covering every row
-        for (int c = t; c < BK; c += 256)
-          sm.bnd[c] = (k0 + c < Sk) ? a.bounds[bhm * Sk + k0 + c] : make_int4(INT_MIN, INT_MAX, 0, 0);
-      }
-      __syncthreads();
 
-      // ---- S^T = K Q^T : lane holds query column li, keys 32*jb + 8r + 4hh + q ----
-      f32x16 s[4];
+      // Per key block t (K_t, V^T_t, bounds_t in LDS; K_{t+1} in registers):
+      //   S_t, interval mask | barrier | K_{t+1} -> LDS; bounds_{t+1}, V_{t+1}
+      //   -> registers; softmax and PV_t; bounds_{t+1} -> LDS | barrier |
+      //   V_{t+1} -> LDS, K_{t+2} -> registers.
+      for (int tt = 0; tt < cnt; ++tt) {
+        const int k0 = block_start(e_cur);
+        const bool need_mask = block_masked(e_cur, k0);
+        const bool has_next = tt + 1 < cnt;
+        const int k0n = block_start(e_next);
+        const bool nm_next = has_next && block_masked(e_next, k0n);
+        // list entry of block t+2, consumed after the second barrier
+        const uint32_t e2_pending = (tt + 2 < cnt) ? list_at(tt + 2) : 0u;
+
+        // ---- S^T = K Q^T : lane holds query column li, keys 32*jb + 8r + 4hh + q ----
+        f32x16 s[4];
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
+        for (int jb = 0; jb < 4; ++jb) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[jb][v] = 0.f;
+          for (int v = 0; v < 16; ++v) s[jb][v] = 0.f;
 #pragma unroll
-        for (int st = 0; st < NS; ++st)
-          s[jb] = mfma32(as_bf16x8(&sm.k[(32 * jb + li) * KST + 16 * st + 8 * hh]), qf[st], s[jb]);
-      }
-      if (need_mask) {
-        const int4* bl = &sm.bnd[4 * hh];
+          for (int kk = 0; kk < NS; ++kk)
+            s[jb] = mfma32(as_bf16x8(&sm.k[(32 * jb + li) * KST + 16 * kk + 8 * hh]), qf[kk], s[jb]);
+        }
+        if (need_mask) {
+          const int4* bl = &sm.bnd[tt & 1][4 * hh];
+#pragma unroll
+          for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int4 bd = bl[32 * jb + 8 * (v >> 2) + (v & 3)];
+              const bool masked = ((bd.x <= qrow) & (qrow < bd.y)) | ((bd.z <= qrow) & (qrow < bd.w));
+              s[jb][v] = masked ? -INFINITY : s[jb][v];
+            }
+        }
+        __syncthreads();   // every wave is done with this block's K
+        int4 breg = make_int4(0, 0, 0, 0);
+        if (has_next) {
+          store_k<D>(st, sm.k, t);
+          if (nm_next && t < BK) breg = load_bnd(bbase, k0n, Sk, t);
+          load_v<D>(st, vbase, k0n, t);
+        }
+
+        // ---- online softmax in the log2 domain ----
+        // The running maximum m_run is only moved when a row's tile maximum
+        // exceeds it by more than 8 (P <= 2^8 otherwise): O and l are sums
+        // taken against the same reference, so their ratio is unchanged, and
+        // most tiles skip the rescale of the accumulators.
+        float mx = -INFINITY;
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int4 bd = bl[32 * jb + 8 * (v >> 2) + (v & 3)];
-            const bool masked = ((bd.x <= qrow) & (qrow < bd.y)) | ((bd.z <= qrow) & (qrow < bd.w));
-            s[jb][v] = masked ? -INFINITY : s[jb][v];
-          }
-      }
-      // ---- online softmax (log2 domain) ----
-      float mx = -INFINITY;
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[jb][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_tile = mx * a.scale_log2;
+        if (__any(m_tile > m_run + 8.f)) {
+          const float m_new = fmaxf(m_run, m_tile);
+          const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
+          for (int d = 0; d < ND; ++d)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[jb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
-      const float base = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - base);
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < ND; ++d)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[d][v] *= alpha;
-      // ---- P (8 keys at a time) and O^T += V^T P^T ----
-      float rs = 0.f;
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          bf16x8 pb;
-#pragma unroll
-          for (int e8 = 0; e8 < 8; ++e8) {
-            const float pv = fast_exp2(fmaf(s[jb][8 * t2 + e8], a.scale_log2, -base));
-            rs += pv;
-            pb[e8] = (bf16)pv;
-          }
-#pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            const bf16* vp = &sm.v[(32 * jb + 16 * t2) * VST + 32 * d + v_lane];
-            const bf16x8 vo = cat_bf16(lds_read_tr(vp), lds_read_tr(vp + 8 * VST));
-            acc[d] = mfma32(vo, pb, acc[d]);
-          }
+            for (int v = 0; v < 16; ++v) acc[d][v] *= alpha;
+          l_run *= alpha;
+          m_run = m_new;
         }
-      l_run = l_run * alpha + rs;
+        const float base = (m_run == -INFINITY) ? 0.f : m_run;
+
+        // ---- P (8 keys at a time, rounded to bf16) and O^T += V^T P^T ----
+        float rs = 0.f;
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) {
+            bf16x8 pb;
+#pragma unroll
+            for (int e8 = 0; e8 < 8; ++e8) {
+              const float pv = fast_exp2(fmaf(s[jb][8 * t2 + e8], a.scale_log2, -base));
+              rs += pv;
+              pb[e8] = (bf16)pv;
+            }
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+              acc[d] = mfma32(as_bf16x8(&sm.vt[(32 * d + li) * VTS + 32 * jb + 16 * t2 + 8 * hh]),
+                              pb, acc[d]);
+          }
+        // keep the row sum here: left to itself the compiler sinks it past
+        // the barrier and keeps all 64 P values alive into the next loads
+        asm volatile("" : "+v"(rs));
+        l_run += rs;
+        // the other bounds buffer was last read before the first barrier of block t-1
+        if (nm_next && t < BK) sm.bnd[(tt + 1) & 1][t] = breg;
+
+        __syncthreads();   // every wave is done with this block's V^T; K_{t+1} is in LDS
+        if (has_next) {
+          store_vt<D>(st, sm.vt, t);
+          int e2 = 0;
+          if (tt + 2 < cnt) {
+            e2 = __builtin_amdgcn_readfirstlane(e2_pending);
+            load_k<D>(st, kbase, block_start(e2), t);
+          }
+          e_cur = e_next;
+          e_next = e2;
+        }
+      }
     }
 
     // ---- finalise: O = acc / l, LSE = (m + log2 l) ln 2 ----
