@@ -14,10 +14,14 @@
 //                        dQ += dS K   (fp32 atomics into the accumulator);
 //   dq_convert_kernel  dQ = bf16(accumulator), round to nearest even.
 // With S = Q K^T computed as C[i][j] a lane holds one key and several query
-// rows, which is exactly the A-operand shape of P^T dO and dS^T Q; Q and dO
-// are therefore staged once, row-major, and read either by rows (16-byte
-// loads) or by columns (transposed LDS loads).
+// rows, which is exactly the A-operand shape of P^T dO and dS^T Q.  Each chunk
+// of Q and dO is therefore staged twice, row-major (A operands of S and dP)
+// and transposed (B operands of dV and dK), and K is staged transposed once
+// per item (B operand of dQ), so that every MFMA operand read from LDS is one
+// 16-byte load.  The next chunk is fetched into registers while the current
+// one computes, and the dQ atomics of a chunk are issued after those loads.
 #include <climits>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -54,31 +58,142 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
 // ---------------------------------------------------------------- main
 template <int D>
 struct alignas(16) BwdSmem {
-  static constexpr int RST = D + 8;    // Q / dO row stride (elements)
-  static constexpr int KST = D + 16;   // K row stride (transposed reads only)
-  static constexpr int SST = BK + 8;   // dS row stride
-  bf16 k[BK * KST];
-  bf16 q[QC * RST];
-  bf16 dout[QC * RST];
-  bf16 ds[QC * SST];
+  static constexpr int QST = D + 8;    // Q / dO row stride (elements)
+  static constexpr int QTS = QC + 8;   // Q^T / dO^T row stride; rows in vt_pos order
+  static constexpr int KTS = BK + 8;   // K^T row stride; keys in natural order
+  static constexpr int DSS = BK + 8;   // dS row stride
+  bf16 q[QC * QST];
+  bf16 dout[QC * QST];
+  bf16 qt[D * QTS];
+  bf16 dot[D * QTS];
+  bf16 kt[D * KTS];
+  bf16 ds[QC * DSS];
   float lse2[QC];   // LSE * log2(e); +inf for rows past the end
   float delta[QC];
   uint32_t item;
 };
 
+// Place of row x (0 <= x < QC) inside a Q^T / dO^T row: bits 2 and 3 of the
+// offset within each group of 16 swapped, so that the 8 query rows one lane
+// holds in the P^T (dS^T) operand are 8 neighbouring elements.
+__device__ __forceinline__ int qt_pos(int x) { return (x & ~15) | perm16(x & 15); }
+
+// Global -> register staging of one chunk of QC query rows of Q and dO
+// (256 threads).  A unit is 4 consecutive rows x 8 head-dim columns of one of
+// the two tensors; the rows of the 16 lanes of a group are chosen so that the
+// transposed 8-byte LDS stores fall on distinct banks.  Threads < 2*QC also
+// carry the LSE (first QC) or Delta (next QC) of one row.
+template <int D>
+struct ChunkStage {
+  static constexpr int CPR = D / 8;
+  static constexpr int NPAIR = (QC / 4) * CPR;   // units per tensor
+  static constexpr int NU = 2 * NPAIR / 256;     // units per thread
+  bf16x8 v[NU][4];
+  float row_term;
+
+  // 0 = Q, 1 = dO; the same in every lane of a wave (NPAIR is a multiple of 64)
+  static __device__ __forceinline__ int tensor(unsigned t, int j) {
+    if constexpr (NU == 2) {
+      return j;
+    } else {
+      return __builtin_amdgcn_readfirstlane((int)(t / NPAIR));
+    }
+  }
+  static __device__ __forceinline__ int row(unsigned t, int j) {
+    const unsigned p = (t + 256u * j) % NPAIR;
+    return 4 * (int)((p & 7u) + 8u * (p / (8u * CPR)));
+  }
+  static __device__ __forceinline__ int col(unsigned t) { return (int)((t >> 3) % CPR); }
+};
+
+template <int D>
+__device__ __forceinline__ void load_chunk(ChunkStage<D>& r, BufRsrc qb, BufRsrc ob, BufRsrc lb,
+                                           BufRsrc db, int q0, int Sq, unsigned t) {
+  using C = ChunkStage<D>;
+#pragma unroll
+  for (int j = 0; j < C::NU; ++j) {
+    const BufRsrc src = C::tensor(t, j) == 0 ? qb : ob;
+    const uint32_t base =
+        opaque(((uint32_t)C::row(t, j) * C::CPR + C::col(t)) * 16u) + (uint32_t)q0 * (D * 2);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) r.v[j][rr] = buf_load16(src, base + (uint32_t)rr * (D * 2));
+  }
+  r.row_term = 0.f;
+  const int i = q0 + (int)(t % QC);
+  if (t < QC) {
+    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lb, i * 4, 0, 0));
+    r.row_term = (i < Sq) ? x * kLog2e : INFINITY;
+  } else if (t < 2 * QC) {
+    r.row_term = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(db, i * 4, 0, 0));
+  }
+}
+
+template <int D, typename Smem>
+__device__ __forceinline__ void store_chunk(const ChunkStage<D>& r, Smem& sm, unsigned t) {
+  using C = ChunkStage<D>;
+  constexpr int QST = Smem::QST, QTS = Smem::QTS;
+#pragma unroll
+  for (int j = 0; j < C::NU; ++j) {
+    const bool is_q = C::tensor(t, j) == 0;
+    bf16* rm = (is_q ? sm.q : sm.dout) + opaque(C::row(t, j) * QST + 8 * C::col(t));
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) *reinterpret_cast<bf16x8*>(rm + rr * QST) = r.v[j][rr];
+    bf16* tp = (is_q ? sm.qt : sm.dot) + opaque((8 * C::col(t)) * QTS + qt_pos(C::row(t, j)));
+    const bf16x16 p01 = __builtin_shufflevector(r.v[j][0], r.v[j][1], 0, 8, 1, 9, 2, 10, 3, 11, 4,
+                                                12, 5, 13, 6, 14, 7, 15);
+    const bf16x16 p23 = __builtin_shufflevector(r.v[j][2], r.v[j][3], 0, 8, 1, 9, 2, 10, 3, 11, 4,
+                                                12, 5, 13, 6, 14, 7, 15);
+#define FM_T_ROW(e)                                                                       \
+  *reinterpret_cast<bf16x4*>(tp + (e) * QTS) =                                            \
+      __builtin_shufflevector(p01, p23, 2 * (e), 2 * (e) + 1, 16 + 2 * (e), 17 + 2 * (e))
+    FM_T_ROW(0); FM_T_ROW(1); FM_T_ROW(2); FM_T_ROW(3);
+    FM_T_ROW(4); FM_T_ROW(5); FM_T_ROW(6); FM_T_ROW(7);
+#undef FM_T_ROW
+  }
+  if (t < QC)
+    sm.lse2[t] = r.row_term;
+  else if (t < 2 * QC)
+    sm.delta[t - QC] = r.row_term;
+}
+
+// K^T of a key block into LDS (once per item): thread t transposes 4*NV
+// consecutive keys x 8 head-dim columns, as the forward does for V.
+template <int D, typename Smem>
+__device__ __forceinline__ void stage_kt(BufRsrc kb, int k0, Smem& sm, unsigned t) {
+  constexpr int CPR = D / 8, NV = (BK / 4) * CPR / 256, KTS = Smem::KTS;
+  const int key = 4 * NV * (int)((t & 7u) + 8u * (t / (8u * CPR)));
+  const int c = (int)((t >> 3) % CPR);
+  bf16x8 v[4 * NV];
+  const uint32_t base = ((uint32_t)(k0 + key) * CPR + c) * 16u;
+#pragma unroll
+  for (int q = 0; q < 4 * NV; ++q) v[q] = buf_load16(kb, base + (uint32_t)q * (D * 2));
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    bf16* dst = sm.kt + (8 * c) * KTS + key + 4 * i;
+    const bf16x16 p01 = __builtin_shufflevector(v[4 * i], v[4 * i + 1], 0, 8, 1, 9, 2, 10, 3, 11, 4,
+                                                12, 5, 13, 6, 14, 7, 15);
+    const bf16x16 p23 = __builtin_shufflevector(v[4 * i + 2], v[4 * i + 3], 0, 8, 1, 9, 2, 10, 3, 11,
+                                                4, 12, 5, 13, 6, 14, 7, 15);
+#define FM_T_ROW(e)                                                                       \
+  *reinterpret_cast<bf16x4*>(dst + (e) * KTS) =                                           \
+      __builtin_shufflevector(p01, p23, 2 * (e), 2 * (e) + 1, 16 + 2 * (e), 17 + 2 * (e))
+    FM_T_ROW(0); FM_T_ROW(1); FM_T_ROW(2); FM_T_ROW(3);
+    FM_T_ROW(4); FM_T_ROW(5); FM_T_ROW(6); FM_T_ROW(7);
+#undef FM_T_ROW
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bwd_kernel(const BwdArgs a) {
   constexpr int NS = D / 16, ND = D / 32;
-  constexpr int RST = BwdSmem<D>::RST, KST = BwdSmem<D>::KST, SST = BwdSmem<D>::SST;
-  __shared__ BwdSmem<D> sm;
+  using Smem = BwdSmem<D>;
+  constexpr int QST = Smem::QST, QTS = Smem::QTS, KTS = Smem::KTS, DSS = Smem::DSS;
+  __shared__ Smem sm;
 
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const unsigned t = threadIdx.x;
+  const int lane = (int)(t & 63), w = (int)(t >> 6);
   const int li = lane & 31, hh = lane >> 5;
-  const int gc = (lane >> 4) & 1, m16 = lane & 15;
-  // transposed-read lane offsets: P-ordered rows (8u + 4hh + e) and natural rows (8hh + 4u + e)
-  const int tr_p = (4 * hh + (m16 >> 2)) * RST + 16 * gc + 4 * (m16 & 3);
-  const int tr_k = (8 * hh + (m16 >> 2)) * KST + 16 * gc + 4 * (m16 & 3);
   const uint32_t max_items = (uint32_t)((long)a.B * a.H * a.nK);
   const uint32_t n_items = min(a.counters[kCtrBwdItems], max_items);
   const int Sq = a.Sq, Sk = a.Sk;
@@ -86,7 +201,7 @@ void attn_bwd_kernel(const BwdArgs a) {
   for (;;) {
     if (t == 0) sm.item = atomicAdd(&a.counters[kCtrBwdNext], 1u);
     __syncthreads();
-    const uint32_t idx = sm.item;
+    const uint32_t idx = __builtin_amdgcn_readfirstlane(sm.item);
     if (idx >= n_items) break;
     const uint32_t it = min(a.queue[idx], max_items - 1);
     const long bh = it / a.nK;
@@ -97,29 +212,29 @@ void attn_bwd_kernel(const BwdArgs a) {
     const uint16_t* lst = a.list_k + (bhm * a.nK + kb) * (long)a.nQ;
     const int k0 = kb * BK;
     const bool ragged_k = k0 + BK > Sk;
+    const BufRsrc qbase = make_rsrc(a.q + bh * Sq * (long)D, (uint32_t)Sq * D * 2u);
+    const BufRsrc obase = make_rsrc(a.dout + bh * Sq * (long)D, (uint32_t)Sq * D * 2u);
+    const BufRsrc kbase = make_rsrc(a.k + bh * Sk * (long)D, (uint32_t)Sk * D * 2u);
+    const BufRsrc vbase = make_rsrc(a.v + bh * Sk * (long)D, (uint32_t)Sk * D * 2u);
+    const BufRsrc lbase = make_rsrc(a.lse + bh * Sq, (uint32_t)Sq * 4u);
+    const BufRsrc dbase = make_rsrc(a.delta + bh * Sq, (uint32_t)Sq * 4u);
+    const BufRsrc listb = make_rsrc(lst, (uint32_t)cnt * 2u);
+    auto list_at = [&](int i) -> uint32_t {
+      return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(listb, i * 2, 0, 0);
+    };
 
-    // this lane's key and its bounds; K and V rows as MFMA B operands
+    // this lane's key: bounds (keys past the end are masked for every row),
+    // K and V rows as MFMA B operands
     const int jrow = k0 + 32 * w + li;
-    const bool jvalid = jrow < Sk;
-    // a key past the end gets an interval covering every row
-    const int4 bd = jvalid ? a.bounds[bhm * Sk + jrow] : make_int4(INT_MIN, INT_MAX, 0, 0);
+    int4 bd = make_int4(INT_MIN, INT_MAX, 0, 0);
+    if (jrow < Sk) bd = a.bounds[bhm * Sk + jrow];
     bf16x8 kf[NS], vf[NS];
     {
-      const bf16x8* kp = reinterpret_cast<const bf16x8*>(a.k + (bh * Sk + jrow) * D);
-      const bf16x8* vp = reinterpret_cast<const bf16x8*>(a.v + (bh * Sk + jrow) * D);
+      const uint32_t off = ((uint32_t)jrow * D + 8u * hh) * 2u;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        kf[s] = jvalid ? kp[2 * s + hh] : zero_bf16x8();
-        vf[s] = jvalid ? vp[2 * s + hh] : zero_bf16x8();
-      }
-    }
-    // whole K block in LDS (read by columns for dQ)
-    {
-      const bf16x8* kg = reinterpret_cast<const bf16x8*>(a.k + (bh * Sk + k0) * D);
-      for (int c = t; c < BK * D / 8; c += 256) {
-        const int j = c / (D / 8), dc = c % (D / 8);
-        *reinterpret_cast<bf16x8*>(&sm.k[j * KST + dc * 8]) =
-            (k0 + j < Sk) ? kg[c] : zero_bf16x8();
+        kf[s] = buf_load16(kbase, off + 32u * s);
+        vf[s] = buf_load16(vbase, off + 32u * s);
       }
     }
     f32x16 dk[ND], dv[ND];
@@ -131,31 +246,28 @@ void attn_bwd_kernel(const BwdArgs a) {
         dv[d][v] = 0.f;
       }
 
-    for (int tt = 0; tt < cnt; ++tt) {
-      const int e = lst[tt];
-      const int qb = min(e & kListIndex, a.nQ - 1);
-      const bool need_mask = (e & kListPartial) || ragged_k;
-      for (int ch = 0; ch < BQ / QC; ++ch) {
-        const int q0 = qb * BQ + ch * QC;
-        if (q0 >= Sq) break;
-        __syncthreads();
-        // ---- stage Q, dO rows [q0, q0+QC), LSE and Delta ----
-        {
-          const bf16x8* qg = reinterpret_cast<const bf16x8*>(a.q + (bh * Sq + q0) * D);
-          const bf16x8* og = reinterpret_cast<const bf16x8*>(a.dout + (bh * Sq + q0) * D);
-          for (int c = t; c < QC * D / 8; c += 256) {
-            const int i = c / (D / 8), dc = c % (D / 8);
-            const bool ok = q0 + i < Sq;
-            *reinterpret_cast<bf16x8*>(&sm.q[i * RST + dc * 8]) = ok ? qg[c] : zero_bf16x8();
-            *reinterpret_cast<bf16x8*>(&sm.dout[i * RST + dc * 8]) = ok ? og[c] : zero_bf16x8();
-          }
-          if (t < QC) {
-            const bool ok = q0 + t < Sq;
-            sm.lse2[t] = ok ? a.lse[bh * Sq + q0 + t] * kLog2e : INFINITY;
-            sm.delta[t] = ok ? a.delta[bh * Sq + q0 + t] : 0.f;
-          }
+    const int nchunks = 2 * cnt;   // each query block is two chunks of QC rows
+    if (nchunks > 0) {
+      stage_kt<D>(kbase, k0, sm, t);
+      ChunkStage<D> cs;
+      int e_cur = __builtin_amdgcn_readfirstlane(list_at(0));
+      load_chunk<D>(cs, qbase, obase, lbase, dbase, min(e_cur & kListIndex, a.nQ - 1) * BQ, Sq, t);
+      store_chunk<D>(cs, sm, t);
+      __syncthreads();
+
+      // Per chunk c (its Q, dO, Q^T, dO^T and row terms in LDS):
+      //   chunk c+1 -> registers; S, dP; P, dS (dS -> LDS); dV, dK |
+      //   barrier | chunk c+1 -> LDS; dQ = dS K -> atomics | barrier
+      for (int c = 0; c < nchunks; ++c) {
+        const int q0 = min(e_cur & kListIndex, a.nQ - 1) * BQ + (c & 1) * QC;
+        const bool need_mask = (e_cur & kListPartial) || ragged_k;
+        const bool has_next = c + 1 < nchunks;
+        int e_next = e_cur;
+        if (has_next) {
+          if (c & 1) e_next = __builtin_amdgcn_readfirstlane(list_at((c + 1) >> 1));
+          const int q0n = min(e_next & kListIndex, a.nQ - 1) * BQ + ((c + 1) & 1) * QC;
+          load_chunk<D>(cs, qbase, obase, lbase, dbase, q0n, Sq, t);
         }
-        __syncthreads();
 
         // ---- S = Q K^T and dP = dO V^T: lane holds key li, rows 32ib + 8r + 4hh + q ----
         f32x16 s[QC / 32], dp[QC / 32];
@@ -167,52 +279,58 @@ void attn_bwd_kernel(const BwdArgs a) {
             dp[ib][v] = 0.f;
           }
 #pragma unroll
-          for (int st = 0; st < NS; ++st) {
-            const int off = (32 * ib + li) * RST + 16 * st + 8 * hh;
-            s[ib] = mfma32(as_bf16x8(&sm.q[off]), kf[st], s[ib]);
-            dp[ib] = mfma32(as_bf16x8(&sm.dout[off]), vf[st], dp[ib]);
+          for (int kk = 0; kk < NS; ++kk) {
+            const int off = (32 * ib + li) * QST + 16 * kk + 8 * hh;
+            s[ib] = mfma32(as_bf16x8(&sm.q[off]), kf[kk], s[ib]);
+            dp[ib] = mfma32(as_bf16x8(&sm.dout[off]), vf[kk], dp[ib]);
           }
         }
-        // ---- P and dS ----
+        // ---- P = exp(S - LSE) (interval mask on partial tiles), dS = P (dP - Delta) ----
         bf16x8 pb[QC / 32][2], dsb[QC / 32][2];
+        auto p_and_ds = [&](auto masked_tile) {
 #pragma unroll
-        for (int ib = 0; ib < QC / 32; ++ib)
+          for (int ib = 0; ib < QC / 32; ++ib)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int il = 32 * ib + 8 * r + 4 * hh;
-            const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse2[il]);
-            const float4 d4 = *reinterpret_cast<const float4*>(&sm.delta[il]);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+            for (int r = 0; r < 4; ++r) {
+              const int il = 32 * ib + 8 * r + 4 * hh;
+              const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse2[il]);
+              const float4 d4 = *reinterpret_cast<const float4*>(&sm.delta[il]);
+              const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+              const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int v = 4 * r + q;
-              float p = fast_exp2(fmaf(s[ib][v], a.scale_log2, -lv[q]));
-              if (need_mask) {
-                const int gi = q0 + il + q;
-                const bool masked = ((bd.x <= gi) & (gi < bd.y)) | ((bd.z <= gi) & (gi < bd.w));
-                p = masked ? 0.f : p;
+              for (int q = 0; q < 4; ++q) {
+                const int v = 4 * r + q;
+                float p = fast_exp2(fmaf(s[ib][v], a.scale_log2, -lv[q]));
+                if constexpr (decltype(masked_tile)::value) {
+                  const int gi = q0 + il + q;
+                  const bool masked = ((bd.x <= gi) & (gi < bd.y)) | ((bd.z <= gi) & (gi < bd.w));
+                  p = masked ? 0.f : p;
+                }
+                const float dsv = p * (dp[ib][v] - dl[q]);
+                pb[ib][v >> 3][v & 7] = (bf16)p;
+                dsb[ib][v >> 3][v & 7] = (bf16)dsv;
+                sm.ds[(il + q) * DSS + 32 * w + li] = (bf16)dsv;
               }
-              const float dsv = p * (dp[ib][v] - dl[q]);
-              pb[ib][v >> 3][v & 7] = (bf16)p;
-              dsb[ib][v >> 3][v & 7] = (bf16)dsv;
-              sm.ds[(il + q) * SST + 32 * w + li] = (bf16)dsv;
             }
-          }
-        // ---- dV += P^T dO,  dK += dS^T Q  (B operands by transposed reads) ----
+        };
+        if (need_mask)
+          p_and_ds(std::true_type{});
+        else
+          p_and_ds(std::false_type{});
+        // ---- dV += P^T dO, dK += dS^T Q (B operands: rows of dO^T, Q^T) ----
 #pragma unroll
         for (int d = 0; d < ND; ++d)
 #pragma unroll
           for (int ib = 0; ib < QC / 32; ++ib)
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2) {
-              const int off = (32 * ib + 16 * t2) * RST + 32 * d + tr_p;
-              const bf16x8 ob = cat_bf16(lds_read_tr(&sm.dout[off]), lds_read_tr(&sm.dout[off + 8 * RST]));
-              const bf16x8 qbv = cat_bf16(lds_read_tr(&sm.q[off]), lds_read_tr(&sm.q[off + 8 * RST]));
-              dv[d] = mfma32(pb[ib][t2], ob, dv[d]);
-              dk[d] = mfma32(dsb[ib][t2], qbv, dk[d]);
+              const int off = (32 * d + li) * QTS + 32 * ib + 16 * t2 + 8 * hh;
+              dv[d] = mfma32(pb[ib][t2], as_bf16x8(&sm.dot[off]), dv[d]);
+              dk[d] = mfma32(dsb[ib][t2], as_bf16x8(&sm.qt[off]), dk[d]);
             }
-        __syncthreads();
+        __syncthreads();   // dS is in LDS; every wave is done with this chunk's Q and dO
+        if (has_next) store_chunk<D>(cs, sm, t);
+
         // ---- dQ[q0.., :] += scale dS K : wave w takes (ib, d) blocks w, w+4, ... ----
         for (int blk = w; blk < (QC / 32) * ND; blk += 4) {
           const int ib = blk / ND, d = blk % ND;
@@ -220,12 +338,9 @@ void attn_bwd_kernel(const BwdArgs a) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
-          for (int ks = 0; ks < BK / 16; ++ks) {
-            const bf16x8 av = as_bf16x8(&sm.ds[(32 * ib + li) * SST + 16 * ks + 8 * hh]);
-            const int off = (16 * ks) * KST + 32 * d + tr_k;
-            const bf16x8 bv = cat_bf16(lds_read_tr(&sm.k[off]), lds_read_tr(&sm.k[off + 4 * KST]));
-            acc = mfma32(av, bv, acc);
-          }
+          for (int ks = 0; ks < BK / 16; ++ks)
+            acc = mfma32(as_bf16x8(&sm.ds[(32 * ib + li) * DSS + 16 * ks + 8 * hh]),
+                         as_bf16x8(&sm.kt[(32 * d + li) * KTS + 16 * ks + 8 * hh]), acc);
           float* dqp = a.dq_acc + (bh * Sq + q0) * D + 32 * d + li;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
@@ -233,6 +348,8 @@ void attn_bwd_kernel(const BwdArgs a) {
             if (q0 + il < Sq) unsafeAtomicAdd(dqp + (long)il * D, acc[v] * a.scale);
           }
         }
+        __syncthreads();   // every wave is done with dS; the next chunk is in LDS
+        e_cur = e_next;
       }
     }
 
@@ -248,7 +365,7 @@ void attn_bwd_kernel(const BwdArgs a) {
           a.dv[off] = (bf16)dv[d][v];
         }
       }
-    __syncthreads();
+    __syncthreads();   // every thread has read sm.item and finished with LDS
   }
   if (t == 0) {
     __threadfence();
