@@ -29,6 +29,7 @@
 namespace fm {
 
 constexpr int QC = 64;   // query rows per backward chunk
+constexpr int CPB = BQ / QC;   // chunks per query block
 
 // ---------------------------------------------------------------- prologue
 template <int D>
@@ -86,19 +87,17 @@ __device__ __forceinline__ int qt_pos(int x) { return (x & ~15) | perm16(x & 15)
 template <int D>
 struct ChunkStage {
   static constexpr int CPR = D / 8;
-  static constexpr int NPAIR = (QC / 4) * CPR;   // units per tensor
-  static constexpr int NU = 2 * NPAIR / 256;     // units per thread
+  static constexpr int NPAIR = (QC / 4) * CPR;   // units per tensor (a multiple of 64)
+  static constexpr int NU = (2 * NPAIR + 255) / 256;   // units per thread (some idle if < 256)
+  static_assert(NPAIR % 64 == 0, "a unit's tensor must be uniform across a wave");
   bf16x8 v[NU][4];
   float row_term;
 
   // 0 = Q, 1 = dO; the same in every lane of a wave (NPAIR is a multiple of 64)
   static __device__ __forceinline__ int tensor(unsigned t, int j) {
-    if constexpr (NU == 2) {
-      return j;
-    } else {
-      return __builtin_amdgcn_readfirstlane((int)(t / NPAIR));
-    }
+    return __builtin_amdgcn_readfirstlane((int)((t + 256u * j) / NPAIR));
   }
+  static __device__ __forceinline__ bool active(unsigned t, int j) { return t + 256u * j < 2u * NPAIR; }
   static __device__ __forceinline__ int row(unsigned t, int j) {
     const unsigned p = (t + 256u * j) % NPAIR;
     return 4 * (int)((p & 7u) + 8u * (p / (8u * CPR)));
@@ -112,6 +111,7 @@ __device__ __forceinline__ void load_chunk(ChunkStage<D>& r, BufRsrc qb, BufRsrc
   using C = ChunkStage<D>;
 #pragma unroll
   for (int j = 0; j < C::NU; ++j) {
+    if (!C::active(t, j)) continue;
     const BufRsrc src = C::tensor(t, j) == 0 ? qb : ob;
     const uint32_t base =
         opaque(((uint32_t)C::row(t, j) * C::CPR + C::col(t)) * 16u) + (uint32_t)q0 * (D * 2);
@@ -134,6 +134,7 @@ __device__ __forceinline__ void store_chunk(const ChunkStage<D>& r, Smem& sm, un
   constexpr int QST = Smem::QST, QTS = Smem::QTS;
 #pragma unroll
   for (int j = 0; j < C::NU; ++j) {
+    if (!C::active(t, j)) continue;
     const bool is_q = C::tensor(t, j) == 0;
     bf16* rm = (is_q ? sm.q : sm.dout) + opaque(C::row(t, j) * QST + 8 * C::col(t));
 #pragma unroll
@@ -236,6 +237,11 @@ void attn_bwd_kernel(const BwdArgs a) {
         kf[s] = buf_load16(kbase, off + 32u * s);
         vf[s] = buf_load16(vbase, off + 32u * s);
       }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        pin_agpr(kf[s]);
+        pin_agpr(vf[s]);
+      }
     }
     f32x16 dk[ND], dv[ND];
 #pragma unroll
@@ -246,7 +252,7 @@ void attn_bwd_kernel(const BwdArgs a) {
         dv[d][v] = 0.f;
       }
 
-    const int nchunks = 2 * cnt;   // each query block is two chunks of QC rows
+    const int nchunks = CPB * cnt;   // each query block is CPB chunks of QC rows
     if (nchunks > 0) {
       stage_kt<D>(kbase, k0, sm, t);
       ChunkStage<D> cs;
@@ -259,37 +265,47 @@ void attn_bwd_kernel(const BwdArgs a) {
       //   chunk c+1 -> registers; S, dP; P, dS (dS -> LDS); dV, dK |
       //   barrier | chunk c+1 -> LDS; dQ = dS K -> atomics | barrier
       for (int c = 0; c < nchunks; ++c) {
-        const int q0 = min(e_cur & kListIndex, a.nQ - 1) * BQ + (c & 1) * QC;
+        const int q0 = min(e_cur & kListIndex, a.nQ - 1) * BQ + (c % CPB) * QC;
         const bool need_mask = (e_cur & kListPartial) || ragged_k;
         const bool has_next = c + 1 < nchunks;
         int e_next = e_cur;
         if (has_next) {
-          if (c & 1) e_next = __builtin_amdgcn_readfirstlane(list_at((c + 1) >> 1));
-          const int q0n = min(e_next & kListIndex, a.nQ - 1) * BQ + ((c + 1) & 1) * QC;
+          if ((c + 1) % CPB == 0) e_next = __builtin_amdgcn_readfirstlane(list_at((c + 1) / CPB));
+          const int q0n = min(e_next & kListIndex, a.nQ - 1) * BQ + ((c + 1) % CPB) * QC;
           load_chunk<D>(cs, qbase, obase, lbase, dbase, q0n, Sq, t);
         }
 
-        // ---- S = Q K^T and dP = dO V^T: lane holds key li, rows 32ib + 8r + 4hh + q ----
-        f32x16 s[QC / 32], dp[QC / 32];
-#pragma unroll
+        // The chunk's two halves of 32 rows go through S, dP, P, dS and the dV,
+        // dK products one after the other, which halves the live tile state.
+#pragma unroll 1
         for (int ib = 0; ib < QC / 32; ++ib) {
+          // ---- S = Q K^T and dP = dO V^T: lane holds key li, rows 32ib + 8r + 4hh + q ----
+          f32x16 s, dp;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            s[ib][v] = 0.f;
-            dp[ib][v] = 0.f;
+            s[v] = 0.f;
+            dp[v] = 0.f;
           }
+          // operands of the whole phase are read first: many LDS reads in
+          // flight instead of one read ahead of each MFMA
+          {
+            bf16x8 qa[NS], oa[NS];
 #pragma unroll
-          for (int kk = 0; kk < NS; ++kk) {
-            const int off = (32 * ib + li) * QST + 16 * kk + 8 * hh;
-            s[ib] = mfma32(as_bf16x8(&sm.q[off]), kf[kk], s[ib]);
-            dp[ib] = mfma32(as_bf16x8(&sm.dout[off]), vf[kk], dp[ib]);
+            for (int kk = 0; kk < NS; ++kk) {
+              const int off = (32 * ib + li) * QST + 16 * kk + 8 * hh;
+              qa[kk] = as_bf16x8(&sm.q[off]);
+              oa[kk] = as_bf16x8(&sm.dout[off]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk < NS; ++kk) {
+              s = mfma32(qa[kk], kf[kk], s);
+              dp = mfma32(oa[kk], vf[kk], dp);
+            }
           }
-        }
-        // ---- P = exp(S - LSE) (interval mask on partial tiles), dS = P (dP - Delta) ----
-        bf16x8 pb[QC / 32][2], dsb[QC / 32][2];
-        auto p_and_ds = [&](auto masked_tile) {
-#pragma unroll
-          for (int ib = 0; ib < QC / 32; ++ib)
+          // ---- P = exp(S - LSE) (interval mask on partial tiles), dS = P (dP - Delta) ----
+          bf16x8 pb[2], dsb[2];
+          auto p_and_ds = [&](auto masked_tile) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int il = 32 * ib + 8 * r + 4 * hh;
@@ -300,34 +316,49 @@ void attn_bwd_kernel(const BwdArgs a) {
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
                 const int v = 4 * r + q;
-                float p = fast_exp2(fmaf(s[ib][v], a.scale_log2, -lv[q]));
+                float p = fast_exp2(fmaf(s[v], a.scale_log2, -lv[q]));
                 if constexpr (decltype(masked_tile)::value) {
                   const int gi = q0 + il + q;
                   const bool masked = ((bd.x <= gi) & (gi < bd.y)) | ((bd.z <= gi) & (gi < bd.w));
                   p = masked ? 0.f : p;
                 }
-                const float dsv = p * (dp[ib][v] - dl[q]);
-                pb[ib][v >> 3][v & 7] = (bf16)p;
-                dsb[ib][v >> 3][v & 7] = (bf16)dsv;
+                const float dsv = p * (dp[v] - dl[q]);
+                pb[v >> 3][v & 7] = (bf16)p;
+                dsb[v >> 3][v & 7] = (bf16)dsv;
                 sm.ds[(il + q) * DSS + 32 * w + li] = (bf16)dsv;
               }
             }
-        };
-        if (need_mask)
-          p_and_ds(std::true_type{});
-        else
-          p_and_ds(std::false_type{});
-        // ---- dV += P^T dO, dK += dS^T Q (B operands: rows of dO^T, Q^T) ----
+          };
+          if (need_mask)
+            p_and_ds(std::true_type{});
+          else
+            p_and_ds(std::false_type{});
+          // ---- dV += P^T dO, dK += dS^T Q (B operands: rows of dO^T, Q^T) ----
+          {
+            bf16x8 ob[ND][2], qtb[ND][2];
 #pragma unroll
-        for (int d = 0; d < ND; ++d)
+            for (int d = 0; d < ND; ++d)
 #pragma unroll
-          for (int ib = 0; ib < QC / 32; ++ib)
+              for (int t2 = 0; t2 < 2; ++t2) {
+                const int off = (32 * d + li) * QTS + 32 * ib + 16 * t2 + 8 * hh;
+                ob[d][t2] = as_bf16x8(&sm.dot[off]);
+                qtb[d][t2] = as_bf16x8(&sm.qt[off]);
+              }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-              const int off = (32 * d + li) * QTS + 32 * ib + 16 * t2 + 8 * hh;
-              dv[d] = mfma32(pb[ib][t2], as_bf16x8(&sm.dot[off]), dv[d]);
-              dk[d] = mfma32(dsb[ib][t2], as_bf16x8(&sm.qt[off]), dk[d]);
-            }
+            for (int d = 0; d < ND; ++d)
+#pragma unroll
+              for (int t2 = 0; t2 < 2; ++t2) {
+                dv[d] = mfma32(pb[t2], ob[d][t2], dv[d]);
+                dk[d] = mfma32(dsb[t2], qtb[d][t2], dk[d]);
+              }
+          }
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            pin_agpr(dv[d]);
+            pin_agpr(dk[d]);
+          }
+        }
         __syncthreads();   // dS is in LDS; every wave is done with this chunk's Q and dO
         if (has_next) store_chunk<D>(cs, sm, t);
 
@@ -337,10 +368,17 @@ void attn_bwd_kernel(const BwdArgs a) {
           f32x16 acc;
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+          {
+            bf16x8 da[BK / 16], kb2[BK / 16];
 #pragma unroll
-          for (int ks = 0; ks < BK / 16; ++ks)
-            acc = mfma32(as_bf16x8(&sm.ds[(32 * ib + li) * DSS + 16 * ks + 8 * hh]),
-                         as_bf16x8(&sm.kt[(32 * d + li) * KTS + 16 * ks + 8 * hh]), acc);
+            for (int ks = 0; ks < BK / 16; ++ks) {
+              da[ks] = as_bf16x8(&sm.ds[(32 * ib + li) * DSS + 16 * ks + 8 * hh]);
+              kb2[ks] = as_bf16x8(&sm.kt[(32 * d + li) * KTS + 16 * ks + 8 * hh]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ++ks) acc = mfma32(da[ks], kb2[ks], acc);
+          }
           float* dqp = a.dq_acc + (bh * Sq + q0) * D + 32 * d + li;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {

@@ -97,6 +97,34 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   return x;
 }
 
+// Register-class pins (no instruction is emitted): keep an MFMA accumulator
+// that is only ever fed back into MFMAs in the AGPR file, and a result the
+// vector ALU reads next in the VGPR file, so that the allocator does not
+// shuttle whole tiles between the two files.
+__device__ __forceinline__ void pin_agpr(f32x16& x) { asm volatile("" : "+a"(x)); }
+__device__ __forceinline__ void pin_vgpr(f32x16& x) { asm volatile("" : "+v"(x)); }
+// MFMA reads its A/B operands from either file: an operand held for a whole
+// loop (K, V rows of a key block) can live in the AGPRs.
+__device__ __forceinline__ void pin_agpr(bf16x8& x) { asm volatile("" : "+a"(x)); }
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
+// Orders the MFMAs and LDS reads of the current scheduling region as
+// LEAD reads, then (MFMA, read) pairs, then the remaining MFMAs, so that
+// LEAD operand loads are in flight ahead of the matrix core.
+template <int N_MFMA, int N_READ, int LEAD>
+__device__ __forceinline__ void pipeline_mfma_reads() {
+  static_assert(N_READ >= LEAD, "");
+#pragma unroll
+  for (int i = 0; i < LEAD; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+#pragma unroll
+  for (int i = 0; i < N_MFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (i + LEAD < N_READ) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+}
+
 // Entry i of a uint16 tile list through an aligned 32-bit load, so that a
 // list walked by a whole workgroup is read with scalar loads.
 __device__ __forceinline__ int list_entry(const uint16_t* lst, int i) {
