@@ -1,6 +1,6 @@
 // Tile classification for the column-sparse mask (FlashMask-3 paper summary,
-// abstract: the mask is indexed by key positions and stores query-axis
-// interval boundaries).  Three kernels:
+// abstract: per key column, the mask keeps the bounds of the query-row ranges
+// it hides).  Three kernels:
 //   kbsum_kernel     per key block, min and max of each clamped bound;
 //   classify_kernel  class of every (query block, key block) tile plus, per
 //                    query block and per key block, the list of tiles that are

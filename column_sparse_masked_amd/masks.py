@@ -19,6 +19,8 @@ checked against a direct definition of its pattern by the tests.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -34,6 +36,37 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     r = ((u >> 16) & 1) + np.uint32(0x7FFF)
     return ((u + r) >> 16).astype(np.uint16)
+
+
+_CHUNK = 1 << 22          # elements per independently seeded block of a tensor
+
+
+def _pool_size() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def draw_bf16_normal(seed_seq: np.random.SeedSequence, shape) -> np.ndarray:
+    """bf16 bits of N(0, 1) fp32 draws of the given shape.  The flat tensor is
+    cut into blocks of 2^22 elements; block i is drawn by
+    default_rng(seed_seq.spawn(n_blocks)[i]) and rounded to bf16 (nearest
+    even).  Blocks are independent, so they are filled by a thread pool, and
+    the values do not depend on the number of threads."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    n_blocks = max(1, -(-n // _CHUNK))
+    children = seed_seq.spawn(n_blocks)
+
+    def fill(i):
+        lo, hi = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        x = np.random.default_rng(children[i]).standard_normal(hi - lo, dtype=np.float32)
+        out[lo:hi] = bf16_bits(x)
+
+    if n_blocks == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(max_workers=_pool_size()) as ex:
+            list(ex.map(fill, range(n_blocks)))
+    return out.reshape(shape)
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -153,7 +186,8 @@ def empty_bounds(Sk: int, Sq: int) -> np.ndarray:
 
 def localize_bounds(global_bounds: np.ndarray, chunk_starts, chunk_len: int) -> np.ndarray:
     """Context-parallel localisation (FlashMask-3 paper summary, abstract:
-    clip-shift-max on the boundary vectors).  A rank holds query chunks
+    each rank clips, shifts and takes the maximum of the bounds without
+    any communication).  A rank holds query chunks
     ``[c0, c0+chunk_len)`` (in the given order, stacked as its local rows).
     A global bound g becomes the number of local rows whose global index is
     below g: for every chunk that starts at or before g take the chunk's local
@@ -187,7 +221,7 @@ class Workload:
     # how the tensors are drawn: (rows of Q drawn, slice of drawn Q rows used)
     q_rows_drawn: int | None = None
     q_row_index: np.ndarray | None = None
-    _rng_state: dict | None = None
+    tensor_seed: int = 0          # entropy of the tensors' SeedSequence
 
     @property
     def scale(self) -> float:
@@ -195,17 +229,18 @@ class Workload:
 
     def draw(self):
         """Return bf16 bit arrays (uint16) q[B][H][Sq][D], k, v [B][H][Sk][D],
-        do[B][H][Sq][D], drawn after the structure from the same generator."""
-        rng = np.random.default_rng()
-        rng.bit_generator.state = self._rng_state
+        do[B][H][Sq][D].  The four tensors are drawn from four children of one
+        SeedSequence whose entropy is the next draw of the workload's own
+        generator after the structure (see draw_bf16_normal)."""
         B, H, D = self.B, self.H, self.D
         qr = self.q_rows_drawn or self.Sq
-        q = bf16_bits(rng.standard_normal((B, H, qr, D), dtype=np.float32))
+        sq, sk, sv, sdo = np.random.SeedSequence(self.tensor_seed).spawn(4)
+        q = draw_bf16_normal(sq, (B, H, qr, D))
         if self.q_row_index is not None:
             q = np.ascontiguousarray(q[:, :, self.q_row_index, :])
-        k = bf16_bits(rng.standard_normal((B, H, self.Sk, D), dtype=np.float32))
-        v = bf16_bits(rng.standard_normal((B, H, self.Sk, D), dtype=np.float32))
-        do = bf16_bits(rng.standard_normal((B, H, self.Sq, D), dtype=np.float32))
+        k = draw_bf16_normal(sk, (B, H, self.Sk, D))
+        v = draw_bf16_normal(sv, (B, H, self.Sk, D))
+        do = draw_bf16_normal(sdo, (B, H, self.Sq, D))
         return q, k, v, do
 
     def nnz_per_head(self) -> np.ndarray:
@@ -237,7 +272,7 @@ def _finish(name, rng, B, H, Sq, Sk, D, bounds_2d, seed, structure, **kw) -> Wor
         np.broadcast_to(bounds_2d[None, None], (B, 1, Sk, 4))).astype(np.int32)
     return Workload(name=name, B=B, H=H, Hm=1, Sq=Sq, Sk=Sk, D=D, bounds=bounds,
                     seed=seed, structure=structure,
-                    _rng_state=rng.bit_generator.state, **kw)
+                    tensor_seed=int(rng.integers(0, 2**63)), **kw)
 
 
 def causal_document(B=1, H=2, S=1024, D=64, n_docs=4, seed=1) -> Workload:
@@ -335,4 +370,4 @@ def custom(bounds_2d: np.ndarray, B: int, H: int, Sq: int, D: int, seed: int,
         bounds = np.ascontiguousarray(
             np.broadcast_to(bounds_2d[None, None], (B, Hm, Sk, 4))).astype(np.int32)
     return Workload(name=name, B=B, H=H, Hm=Hm, Sq=Sq, Sk=Sk, D=D, bounds=bounds,
-                    seed=seed, _rng_state=rng.bit_generator.state)
+                    seed=seed, tensor_seed=int(rng.integers(0, 2**63)))

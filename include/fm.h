@@ -116,8 +116,8 @@ fm_status fm_set_kernel_events(void* begin, void* end);
 
 /*
  * fm_tile_bounds - classify every (query block, key block) tile.
- * Paper summary, abstract: the column-wise sparse mask stores query-axis
- * interval boundaries indexed by key positions, which lets whole tiles be
+ * Paper summary, abstract: the mask keeps, per key column, the bounds of the
+ * query-row ranges it hides, which lets whole tiles be
  * recognised as fully masked (skipped), unmasked (full) or mixed (partial).
  * Reads `bounds`; writes every part of `tileinfo` and zeroes its counters.
  * Three kernels: key-block min/max, tile classification with per-block lists,

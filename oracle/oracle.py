@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
 leg of the benchmark may import this module.  It shares no code with the HIP
 library or its Python binding, and it never imports either.
 
-What it computes (FlashMask-3 paper summary, abstract; the column-wise sparse
-mask "indexed by key positions" holding "query-axis interval boundaries"):
+What it computes (FlashMask-3 paper summary, abstract: a structured mask is
+stored per key column as the row ranges that column hides):
 
 * mask:  element (i, j) is masked iff LTS[j] <= i < LTE[j] or
   UTS[j] <= i < UTE[j]  (half-open intervals, empty when start >= end);
