@@ -52,7 +52,22 @@ def parse_args(argv=None):
                     help="budget of the CPU oracle sample (at least one head is always run)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="leave out the oracle timing (profiling runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run 5 device-to-device copies of BYTES bytes (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters to bytes)")
     return ap.parse_args(argv)
+
+
+def copy_calibration(nbytes: int) -> int:
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 5}), flush=True)
+    return 0
 
 
 def kernel_source_digest(files) -> str:
@@ -126,6 +141,8 @@ def cpu_baseline(w, tensors, budget_s):
 
 def main(argv=None):
     args = parse_args(argv)
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(no sharding, no collectives).", file=sys.stderr)
