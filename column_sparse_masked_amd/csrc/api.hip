@@ -19,6 +19,13 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// rows of the fp32 dQ accumulator: every (batch, head) gets whole query
+// blocks, so that the backward's atomics need no row bound check
+size_t acc_rows(const fm_problem* p) {
+  const size_t nQ = ((size_t)p->seqlen_q + fm::BQ - 1) / fm::BQ;
+  return (size_t)p->batch * p->heads * nQ * fm::BQ;
+}
+
 fm_status check_problem(const fm_problem* p) {
   if (!p) return FM_ERR_NULL;
   if (p->batch < 0 || p->heads < 1 || p->mask_heads < 1 || p->seqlen_q < 0 || p->seqlen_k < 0)
@@ -137,7 +144,7 @@ fm_status fm_bwd_workspace_bytes(const fm_problem* p, size_t* bytes) {
   if (st != FM_OK) return st;
   if (!bytes) return FM_ERR_NULL;
   const size_t rows = (size_t)p->batch * p->heads * p->seqlen_q;
-  *bytes = align256(rows * p->head_dim * sizeof(float)) + align256(rows * sizeof(float));
+  *bytes = align256(acc_rows(p) * p->head_dim * sizeof(float)) + align256(rows * sizeof(float));
   return FM_OK;
 }
 
@@ -272,7 +279,7 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   a.dk = static_cast<__bf16*>(dk);
   a.dv = static_cast<__bf16*>(dv);
   a.dq_acc = static_cast<float*>(workspace);
-  a.delta = at<float>(workspace, align256(rows * p->head_dim * sizeof(float)));
+  a.delta = at<float>(workspace, align256(acc_rows(p) * p->head_dim * sizeof(float)));
   a.B = p->batch; a.H = p->heads; a.Hm = p->mask_heads;
   a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
   a.scale = p->softmax_scale;

@@ -32,28 +32,38 @@ constexpr int QC = 64;   // query rows per backward chunk
 constexpr int CPB = BQ / QC;   // chunks per query block
 
 // ---------------------------------------------------------------- prologue
+// Delta and a zeroed accumulator.  The accumulator has Sqp >= Sq rows per
+// (batch, head) (whole query blocks); thread groups of D/8 walk its rows and
+// the real ones (i < Sq) also get their Delta.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o,
                                                       const bf16* __restrict__ dout,
                                                       float* __restrict__ delta,
-                                                      float* __restrict__ dq_acc, long rows) {
+                                                      float* __restrict__ dq_acc, long acc_rows,
+                                                      int Sq, int Sqp) {
   constexpr int TPR = D / 8;   // threads per row, 8 elements each
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long row = gid / TPR;
+  const long arow = gid / TPR;   // accumulator row
   const int c = (int)(gid % TPR);
+  const long bh = arow / Sqp;
+  const int i = (int)(arow % Sqp);
+  const bool real = arow < acc_rows && i < Sq;
+  const long row = bh * Sq + i;
   float sum = 0.f;
-  if (row < rows) {
+  if (real) {
     const bf16x8 ov = reinterpret_cast<const bf16x8*>(o)[row * TPR + c];
     const bf16x8 dv = reinterpret_cast<const bf16x8*>(dout)[row * TPR + c];
 #pragma unroll
     for (int e = 0; e < 8; ++e) sum += (float)ov[e] * (float)dv[e];
-    float4* z = reinterpret_cast<float4*>(dq_acc + row * D + 8 * c);
+  }
+  if (arow < acc_rows) {
+    float4* z = reinterpret_cast<float4*>(dq_acc + arow * D + 8 * c);
     z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
     z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-  if (row < rows && c == 0) delta[row] = sum;
+  if (real && c == 0) delta[row] = sum;
 }
 
 // ---------------------------------------------------------------- main
@@ -63,14 +73,16 @@ struct alignas(16) BwdSmem {
   static constexpr int QTS = QC + 8;   // Q^T / dO^T row stride; rows in vt_pos order
   static constexpr int KTS = BK + 8;   // K^T row stride; keys in natural order
   static constexpr int DSS = BK + 8;   // dS row stride
+  // small and many-times-indexed arrays first, so that their addresses fit
+  // the 16-bit immediate offset of LDS instructions
+  float lse2[QC];   // LSE * log2(e); +inf for rows past the end
+  float delta[QC];
+  bf16 ds[QC * DSS];
   bf16 q[QC * QST];
   bf16 dout[QC * QST];
   bf16 qt[D * QTS];
   bf16 dot[D * QTS];
   bf16 kt[D * KTS];
-  bf16 ds[QC * DSS];
-  float lse2[QC];   // LSE * log2(e); +inf for rows past the end
-  float delta[QC];
   uint32_t item;
 };
 
@@ -80,16 +92,21 @@ struct alignas(16) BwdSmem {
 __device__ __forceinline__ int qt_pos(int x) { return (x & ~15) | perm16(x & 15); }
 
 // Global -> register staging of one chunk of QC query rows of Q and dO
-// (256 threads).  A unit is 4 consecutive rows x 8 head-dim columns of one of
-// the two tensors; the rows of the 16 lanes of a group are chosen so that the
-// transposed 8-byte LDS stores fall on distinct banks.  Threads < 2*QC also
-// carry the LSE (first QC) or Delta (next QC) of one row.
+// (256 threads).  A unit is 4 consecutive rows (4m .. 4m+3) x 8 head-dim
+// columns (chunk c) of one of the two tensors.  Each group of 16 lanes takes 4
+// consecutive m by 4 consecutive c: with the row stride of 16 bytes past a
+// multiple of 256, the 16 row-major 16-byte stores of a group then cover all
+// LDS banks once, and the transposed 8-byte stores of a group fall on 8
+// distinct bank pairs.  A wave's 4 groups cover 16 chunks of 4 rows (whole
+// 256-byte rows for D = 128) so that the global loads stay row-contiguous.
+// Threads < 2*QC also carry the LSE (first QC) or Delta (next QC) of one row.
 template <int D>
 struct ChunkStage {
-  static constexpr int CPR = D / 8;
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int NPAIR = (QC / 4) * CPR;   // units per tensor (a multiple of 64)
   static constexpr int NU = (2 * NPAIR + 255) / 256;   // units per thread (some idle if < 256)
   static_assert(NPAIR % 64 == 0, "a unit's tensor must be uniform across a wave");
+  static_assert(CPR % 4 == 0 && QC % 16 == 0, "groups are 4 row-units x 4 chunks");
   bf16x8 v[NU][4];
   float row_term;
 
@@ -98,17 +115,32 @@ struct ChunkStage {
     return __builtin_amdgcn_readfirstlane((int)((t + 256u * j) / NPAIR));
   }
   static __device__ __forceinline__ bool active(unsigned t, int j) { return t + 256u * j < 2u * NPAIR; }
+  // unit p = (group G, lane-in-group l): chunk c = 4 (G % (CPR/4)) + l / 4,
+  // row-unit m = 4 (G / (CPR/4)) + l % 4
   static __device__ __forceinline__ int row(unsigned t, int j) {
     const unsigned p = (t + 256u * j) % NPAIR;
-    return 4 * (int)((p & 7u) + 8u * (p / (8u * CPR)));
+    return 4 * (int)(4u * ((p >> 4) / (CPR / 4)) + (p & 3u));
   }
-  static __device__ __forceinline__ int col(unsigned t) { return (int)((t >> 3) % CPR); }
+  static __device__ __forceinline__ int col(unsigned t) {
+    const unsigned p = t % NPAIR;   // 256 % NPAIR == 0, so the same for every j
+    return (int)(4u * ((p >> 4) % (CPR / 4)) + ((p >> 2) & 3u));
+  }
 };
 
 template <int D>
 __device__ __forceinline__ void load_chunk(ChunkStage<D>& r, BufRsrc qb, BufRsrc ob, BufRsrc lb,
-                                           BufRsrc db, int q0, int Sq, unsigned t) {
+                                           BufRsrc db, int q0, unsigned t) {
   using C = ChunkStage<D>;
+  // The row term first: the oldest load of the chunk, so that waiting for it
+  // never waits for memory operations issued after the chunk's loads (the
+  // dQ atomics).  Wave 0 carries LSE, wave 1 Delta (QC is the wave size);
+  // rows past the end read 0 (buffer range check) and are fixed on store.
+  static_assert(QC == 64, "one wave per row term");
+  if (t < 2 * QC) {
+    const BufRsrc src = __builtin_amdgcn_readfirstlane((int)(t < QC)) ? lb : db;   // per wave
+    r.row_term = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(src, (q0 + (int)(t % QC)) * 4, 0, 0));
+  }
 #pragma unroll
   for (int j = 0; j < C::NU; ++j) {
     if (!C::active(t, j)) continue;
@@ -118,18 +150,11 @@ __device__ __forceinline__ void load_chunk(ChunkStage<D>& r, BufRsrc qb, BufRsrc
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) r.v[j][rr] = buf_load16(src, base + (uint32_t)rr * (D * 2));
   }
-  r.row_term = 0.f;
-  const int i = q0 + (int)(t % QC);
-  if (t < QC) {
-    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lb, i * 4, 0, 0));
-    r.row_term = (i < Sq) ? x * kLog2e : INFINITY;
-  } else if (t < 2 * QC) {
-    r.row_term = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(db, i * 4, 0, 0));
-  }
 }
 
 template <int D, typename Smem>
-__device__ __forceinline__ void store_chunk(const ChunkStage<D>& r, Smem& sm, unsigned t) {
+__device__ __forceinline__ void store_chunk(const ChunkStage<D>& r, Smem& sm, int q0, int Sq,
+                                            unsigned t) {
   using C = ChunkStage<D>;
   constexpr int QST = Smem::QST, QTS = Smem::QTS;
 #pragma unroll
@@ -151,8 +176,9 @@ __device__ __forceinline__ void store_chunk(const ChunkStage<D>& r, Smem& sm, un
     FM_T_ROW(4); FM_T_ROW(5); FM_T_ROW(6); FM_T_ROW(7);
 #undef FM_T_ROW
   }
+  // LSE * log2(e), +inf for rows past the end (P = 0 there); Delta as is
   if (t < QC)
-    sm.lse2[t] = r.row_term;
+    sm.lse2[t] = q0 + (int)t < Sq ? r.row_term * kLog2e : INFINITY;
   else if (t < 2 * QC)
     sm.delta[t - QC] = r.row_term;
 }
@@ -204,12 +230,14 @@ void attn_bwd_kernel(const BwdArgs a) {
     __syncthreads();
     const uint32_t idx = __builtin_amdgcn_readfirstlane(sm.item);
     if (idx >= n_items) break;
-    const uint32_t it = min(a.queue[idx], max_items - 1);
+    // values loaded from memory are not known to be uniform: broadcast them,
+    // so that the buffer resources built from them stay in scalar registers
+    const uint32_t it = __builtin_amdgcn_readfirstlane(min(a.queue[idx], max_items - 1));
     const long bh = it / a.nK;
     const int kb = (int)(it % a.nK);
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
     const long bhm = (long)b * a.Hm + (a.Hm == 1 ? 0 : h);
-    const int cnt = min(a.cnt_k[bhm * a.nK + kb], a.nQ);
+    const int cnt = __builtin_amdgcn_readfirstlane(min(a.cnt_k[bhm * a.nK + kb], a.nQ));
     const uint16_t* lst = a.list_k + (bhm * a.nK + kb) * (long)a.nQ;
     const int k0 = kb * BK;
     const bool ragged_k = k0 + BK > Sk;
@@ -219,9 +247,12 @@ void attn_bwd_kernel(const BwdArgs a) {
     const BufRsrc vbase = make_rsrc(a.v + bh * Sk * (long)D, (uint32_t)Sk * D * 2u);
     const BufRsrc lbase = make_rsrc(a.lse + bh * Sq, (uint32_t)Sq * 4u);
     const BufRsrc dbase = make_rsrc(a.delta + bh * Sq, (uint32_t)Sq * 4u);
-    const BufRsrc listb = make_rsrc(lst, (uint32_t)cnt * 2u);
-    auto list_at = [&](int i) -> uint32_t {
-      return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(listb, i * 2, 0, 0);
+    // Each item starts its walk at block kb % cnt (and wraps): neighbouring
+    // key blocks, which run at the same time, then add into different dQ rows.
+    const int rot = cnt > 0 ? kb % cnt : 0;
+    auto list_at = [&](int i) {
+      const int j = i + rot;
+      return list_entry(lst, j < cnt ? j : j - cnt);
     };
 
     // this lane's key: bounds (keys past the end are masked for every row),
@@ -255,135 +286,221 @@ void attn_bwd_kernel(const BwdArgs a) {
     const int nchunks = CPB * cnt;   // each query block is CPB chunks of QC rows
     if (nchunks > 0) {
       stage_kt<D>(kbase, k0, sm, t);
+      // chunk c starts at row block_row(c) * BQ + (c % CPB) * QC
+      auto chunk_q0 = [&](int c) __attribute__((always_inline)) {
+        const int e = list_at(c / CPB);
+        return min(e & kListIndex, a.nQ - 1) * BQ + (c % CPB) * QC;
+      };
       ChunkStage<D> cs;
-      int e_cur = __builtin_amdgcn_readfirstlane(list_at(0));
-      load_chunk<D>(cs, qbase, obase, lbase, dbase, min(e_cur & kListIndex, a.nQ - 1) * BQ, Sq, t);
-      store_chunk<D>(cs, sm, t);
+      int e_cur = list_at(0);
+      load_chunk<D>(cs, qbase, obase, lbase, dbase, chunk_q0(0), t);
+      store_chunk<D>(cs, sm, chunk_q0(0), Sq, t);
       __syncthreads();
+      // B operands of dQ = dS K for this wave's head-dim columns 32 (w % ND)..:
+      // the same for every chunk of the item, so read from K^T once
+      bf16x8 ktr[BK / 16];
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks)
+        ktr[ks] = as_bf16x8(&sm.kt[(32 * (w % ND) + li) * KTS + 16 * ks + 8 * hh]);
 
       // Per chunk c (its Q, dO, Q^T, dO^T and row terms in LDS):
-      //   chunk c+1 -> registers; S, dP; P, dS (dS -> LDS); dV, dK |
-      //   barrier | chunk c+1 -> LDS; dQ = dS K -> atomics | barrier
+      //   chunk c+1 -> registers; S, dP, P, dS (-> LDS), dV, dK | barrier |
+      //   chunk c+1 -> LDS; dQ = dS K -> atomics | barrier
+      // The loads of chunk c+1 are issued after the atomics of chunk c-1, so
+      // waiting for them also waits for those atomics, which had the whole
+      // previous dQ step and this chunk's work to complete.
       for (int c = 0; c < nchunks; ++c) {
         const int q0 = min(e_cur & kListIndex, a.nQ - 1) * BQ + (c % CPB) * QC;
         const bool need_mask = (e_cur & kListPartial) || ragged_k;
         const bool has_next = c + 1 < nchunks;
         int e_next = e_cur;
-        if (has_next) {
-          if ((c + 1) % CPB == 0) e_next = __builtin_amdgcn_readfirstlane(list_at((c + 1) / CPB));
-          const int q0n = min(e_next & kListIndex, a.nQ - 1) * BQ + ((c + 1) % CPB) * QC;
-          load_chunk<D>(cs, qbase, obase, lbase, dbase, q0n, Sq, t);
-        }
+        if (has_next && (c + 1) % CPB == 0)
+          e_next = list_at((c + 1) / CPB);
+        if (has_next) load_chunk<D>(cs, qbase, obase, lbase, dbase, chunk_q0(c + 1), t);
 
-        // The chunk's two halves of 32 rows go through S, dP, P, dS and the dV,
-        // dK products one after the other, which halves the live tile state.
-#pragma unroll 1
-        for (int ib = 0; ib < QC / 32; ++ib) {
-          // ---- S = Q K^T and dP = dO V^T: lane holds key li, rows 32ib + 8r + 4hh + q ----
-          f32x16 s, dp;
+        // S, dP, P, dS, dV and dK of the chunk's two halves (32 rows each),
+        // software-pipelined so that the vector work of one half runs while
+        // the matrix cores work on the other:
+        //   (a)  S, dP of half 0
+        //   (b1) S of half 1          |  P of half 0
+        //   (b2) dP of half 1         |  dS of half 0 (-> LDS)
+        //   (c1) dV from half 0       |  P of half 1
+        //   (c2) dK from half 0       |  dS of half 1 (-> LDS)
+        //   (d)  dV, dK from half 1
+        // On partial tiles P is masked between the P and dS steps (a separate,
+        // uniform branch that only rewrites P in place).
+        // S, dP: lane holds key li, rows 32 ib + 8 r + 4 hh + q in element 4r+q.
+        {
+          f32x16 s0, dp0, s1, dp1;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            s[v] = 0.f;
-            dp[v] = 0.f;
+            s0[v] = 0.f; dp0[v] = 0.f; s1[v] = 0.f; dp1[v] = 0.f;
           }
-          // operands of the whole phase are read first: many LDS reads in
-          // flight instead of one read ahead of each MFMA
-          {
-            bf16x8 qa[NS], oa[NS];
-#pragma unroll
-            for (int kk = 0; kk < NS; ++kk) {
-              const int off = (32 * ib + li) * QST + 16 * kk + 8 * hh;
-              qa[kk] = as_bf16x8(&sm.q[off]);
-              oa[kk] = as_bf16x8(&sm.dout[off]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int kk = 0; kk < NS; ++kk) {
-              s = mfma32(qa[kk], kf[kk], s);
-              dp = mfma32(oa[kk], vf[kk], dp);
-            }
-          }
-          // ---- P = exp(S - LSE) (interval mask on partial tiles), dS = P (dP - Delta) ----
-          bf16x8 pb[2], dsb[2];
-          auto p_and_ds = [&](auto masked_tile) {
+          bf16x8 pb[2][2], dsb[2][2];
+          float pf[2][16];                 // P in fp32 between its step and dS's
+          float4 lrow[4], drow[4];         // LSE*log2(e) and Delta of the lane's rows
+          auto read_rows = [&](int ib) __attribute__((always_inline)) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int il = 32 * ib + 8 * r + 4 * hh;
-              const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse2[il]);
-              const float4 d4 = *reinterpret_cast<const float4*>(&sm.delta[il]);
-              const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-              const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const int v = 4 * r + q;
-                float p = fast_exp2(fmaf(s[v], a.scale_log2, -lv[q]));
-                if constexpr (decltype(masked_tile)::value) {
-                  const int gi = q0 + il + q;
-                  const bool masked = ((bd.x <= gi) & (gi < bd.y)) | ((bd.z <= gi) & (gi < bd.w));
-                  p = masked ? 0.f : p;
-                }
-                const float dsv = p * (dp[v] - dl[q]);
-                pb[v >> 3][v & 7] = (bf16)p;
-                dsb[v >> 3][v & 7] = (bf16)dsv;
-                sm.ds[(il + q) * DSS + 32 * w + li] = (bf16)dsv;
-              }
+              lrow[r] = *reinterpret_cast<const float4*>(&sm.lse2[32 * ib + 8 * r + 4 * hh]);
+              drow[r] = *reinterpret_cast<const float4*>(&sm.delta[32 * ib + 8 * r + 4 * hh]);
             }
           };
-          if (need_mask)
-            p_and_ds(std::true_type{});
-          else
-            p_and_ds(std::false_type{});
-          // ---- dV += P^T dO, dK += dS^T Q (B operands: rows of dO^T, Q^T) ----
-          {
-            bf16x8 ob[ND][2], qtb[ND][2];
+          auto q_op = [&](int ib, int kk) __attribute__((always_inline)) {
+            return as_bf16x8(&sm.q[(32 * ib + li) * QST + 16 * kk + 8 * hh]);
+          };
+          auto o_op = [&](int ib, int kk) __attribute__((always_inline)) {
+            return as_bf16x8(&sm.dout[(32 * ib + li) * QST + 16 * kk + 8 * hh]);
+          };
+          auto ot_op = [&](int ib, int d, int t2) __attribute__((always_inline)) {
+            return as_bf16x8(&sm.dot[(32 * d + li) * QTS + 32 * ib + 16 * t2 + 8 * hh]);
+          };
+          auto qt_op = [&](int ib, int d, int t2) __attribute__((always_inline)) {
+            return as_bf16x8(&sm.qt[(32 * d + li) * QTS + 32 * ib + 16 * t2 + 8 * hh]);
+          };
+          auto f4 = [](const float4& x, int q) __attribute__((always_inline)) {
+            return q == 0 ? x.x : q == 1 ? x.y : q == 2 ? x.z : x.w;
+          };
+          // P = exp2(S scale log2(e) - LSE log2(e))
+          auto p_of = [&](const f32x16& sv, int v) __attribute__((always_inline)) {
+            return fast_exp2(fmaf(sv[v], a.scale_log2, -f4(lrow[v >> 2], v & 3)));
+          };
+          // partial tile: P = 0 where the lane's key hides the row.  Bit
+          // 8r + q of `hidden` covers row 32 ib + 8 r + 4 hh + q: the union of
+          // the key's two intervals clipped to the half's 32 rows.
+          auto mask_p = [&](int ib) __attribute__((always_inline)) {
+            const int base = q0 + 32 * ib;
+            auto clip = [&](int x) { return min(max(x, base), base + 32) - base; };
+            auto rows = [](int lo, int hi) {
+              return hi > lo ? (~0u >> (32 - hi)) & (~0u << lo) : 0u;
+            };
+            const uint32_t hidden =
+                (rows(clip(bd.x), clip(bd.y)) | rows(clip(bd.z), clip(bd.w))) >> (4 * hh);
 #pragma unroll
-            for (int d = 0; d < ND; ++d)
+            for (int v = 0; v < 16; ++v) {
+              const int keep = (int)(~hidden << (31 - (8 * (v >> 2) + (v & 3)))) >> 31;
+              pf[ib][v] = __builtin_bit_cast(float, __builtin_bit_cast(int, pf[ib][v]) & keep);
+            }
+          };
+          // dS = P (dP - Delta) into the MFMA operand and the LDS tile; P packed
+          auto ds_of = [&](const f32x16& dpv, int ib, int v) __attribute__((always_inline)) {
+            const float p = pf[ib][v];
+            const float dsv = p * (dpv[v] - f4(drow[v >> 2], v & 3));
+            pb[ib][v >> 3][v & 7] = (bf16)p;
+            dsb[ib][v >> 3][v & 7] = (bf16)dsv;
+            sm.ds[(32 * ib + 8 * (v >> 2) + 4 * hh + (v & 3)) * DSS + 32 * w + li] = (bf16)dsv;
+          };
+          constexpr int EPK = 16 / NS;   // elements per MFMA in (b1), (b2)
+          constexpr int EPC = 16 / ND;   // elements per MFMA in (c1), (c2)
+
+          // (a): operand reads run 6 ahead of the MFMAs
 #pragma unroll
-              for (int t2 = 0; t2 < 2; ++t2) {
-                const int off = (32 * d + li) * QTS + 32 * ib + 16 * t2 + 8 * hh;
-                ob[d][t2] = as_bf16x8(&sm.dot[off]);
-                qtb[d][t2] = as_bf16x8(&sm.qt[off]);
-              }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int d = 0; d < ND; ++d)
-#pragma unroll
-              for (int t2 = 0; t2 < 2; ++t2) {
-                dv[d] = mfma32(pb[t2], ob[d][t2], dv[d]);
-                dk[d] = mfma32(dsb[t2], qtb[d][t2], dk[d]);
-              }
+          for (int kk = 0; kk < NS; ++kk) {
+            s0 = mfma32(q_op(0, kk), kf[kk], s0);
+            dp0 = mfma32(o_op(0, kk), vf[kk], dp0);
           }
+          read_rows(0);
+          interleave_mfma<2 * NS, 2 * NS + 8, 6, 0, 0>();
+          __builtin_amdgcn_sched_barrier(0);
+          // (b1)
 #pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            pin_agpr(dv[d]);
-            pin_agpr(dk[d]);
+          for (int kk = 0; kk < NS; ++kk) {
+            s1 = mfma32(q_op(1, kk), kf[kk], s1);
+#pragma unroll
+            for (int e = 0; e < EPK; ++e) pf[0][EPK * kk + e] = p_of(s0, EPK * kk + e);
           }
+          interleave_mfma<NS, NS, 3, 3 * EPK, 0>();
+          __builtin_amdgcn_sched_barrier(0);
+          if (need_mask) mask_p(0);
+          __builtin_amdgcn_sched_barrier(0);
+          // (b2)
+#pragma unroll
+          for (int kk = 0; kk < NS; ++kk) {
+            dp1 = mfma32(o_op(1, kk), vf[kk], dp1);
+#pragma unroll
+            for (int e = 0; e < EPK; ++e) ds_of(dp0, 0, EPK * kk + e);
+          }
+          interleave_mfma<NS, NS, 3, 4 * EPK, EPK>();
+          __builtin_amdgcn_sched_barrier(0);
+          // (c1)
+          read_rows(1);
+#pragma unroll
+          for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+              dv[d] = mfma32(pb[0][t2], ot_op(0, d, t2), dv[d]);
+#pragma unroll
+              for (int e = 0; e < EPC / 2; ++e) {
+                const int v = (EPC / 2) * (2 * d + t2) + e;
+                pf[1][v] = p_of(s1, v);
+              }
+            }
+          interleave_mfma<2 * ND, 2 * ND + 8, 4, 3 * EPC / 2, 0>();
+          __builtin_amdgcn_sched_barrier(0);
+          if (need_mask) mask_p(1);
+          __builtin_amdgcn_sched_barrier(0);
+          // (c2)
+#pragma unroll
+          for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+              dk[d] = mfma32(dsb[0][t2], qt_op(0, d, t2), dk[d]);
+#pragma unroll
+              for (int e = 0; e < EPC / 2; ++e) ds_of(dp1, 1, (EPC / 2) * (2 * d + t2) + e);
+            }
+          interleave_mfma<2 * ND, 2 * ND, 3, 4 * EPC / 2, EPC / 2>();
+          __builtin_amdgcn_sched_barrier(0);
+          // (d)
+#pragma unroll
+          for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+              dv[d] = mfma32(pb[1][t2], ot_op(1, d, t2), dv[d]);
+              dk[d] = mfma32(dsb[1][t2], qt_op(1, d, t2), dk[d]);
+            }
+          interleave_mfma<4 * ND, 4 * ND, 4, 0, 0>();
+        }
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          pin_agpr(dv[d]);
+          pin_agpr(dk[d]);
         }
         __syncthreads();   // dS is in LDS; every wave is done with this chunk's Q and dO
-        if (has_next) store_chunk<D>(cs, sm, t);
+        if (has_next) store_chunk<D>(cs, sm, chunk_q0(c + 1), Sq, t);
 
-        // ---- dQ[q0.., :] += scale dS K : wave w takes (ib, d) blocks w, w+4, ... ----
-        for (int blk = w; blk < (QC / 32) * ND; blk += 4) {
-          const int ib = blk / ND, d = blk % ND;
-          f32x16 acc;
+        // ---- dQ[q0.., :] += scale dS K: wave w takes head-dim columns
+        //      32 (w % ND) .. +32 of the chunk rows 32 ib .. +32 for ib = w / ND, +4/ND, ...
+        {
+          constexpr int NB = (QC / 32) * ND / 4;   // (ib, d) blocks per wave
+          const int d = w % ND;
+          f32x16 acc[NB];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-          {
-            bf16x8 da[BK / 16], kb2[BK / 16];
+          for (int j = 0; j < NB; ++j)
 #pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-              da[ks] = as_bf16x8(&sm.ds[(32 * ib + li) * DSS + 16 * ks + 8 * hh]);
-              kb2[ks] = as_bf16x8(&sm.kt[(32 * d + li) * KTS + 16 * ks + 8 * hh]);
+            for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < BK / 16; ++ks) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+              const int ib = (w + 4 * j) / ND;
+              acc[j] = mfma32(as_bf16x8(&sm.ds[(32 * ib + li) * DSS + 16 * ks + 8 * hh]), ktr[ks], acc[j]);
             }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) acc = mfma32(da[ks], kb2[ks], acc);
           }
-          float* dqp = a.dq_acc + (bh * Sq + q0) * D + 32 * d + li;
+          // The accumulator has whole query blocks of rows, so no row needs a
+          // bound check.  Addresses: uniform base + 32-bit lane offset (kept
+          // opaque so that the per-row offsets are not hoisted out of the
+          // loop and kept live) + a constant per row.
+          char* const dq0 = reinterpret_cast<char*>(a.dq_acc + ((long)bh * a.nQ * BQ + q0) * D);
+          const uint32_t lane_off = opaque((uint32_t)(4 * hh * D + 32 * d + li) * 4u);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int il = 32 * ib + 8 * (v >> 2) + 4 * hh + (v & 3);
-            if (q0 + il < Sq) unsafeAtomicAdd(dqp + (long)il * D, acc[v] * a.scale);
+          for (int j = 0; j < NB; ++j) {
+            const int ib = (w + 4 * j) / ND;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const uint32_t row = 32 * ib + 8 * (v >> 2) + (v & 3);
+              unsafeAtomicAdd(reinterpret_cast<float*>(dq0 + (lane_off + row * (D * 4))),
+                              acc[j][v] * a.scale);
+            }
           }
         }
         __syncthreads();   // every wave is done with dS; the next chunk is in LDS
@@ -392,17 +509,23 @@ void attn_bwd_kernel(const BwdArgs a) {
     }
 
     // ---- write dK (scaled) and dV: lane holds column 32d + li, keys 8r + 4hh + q ----
+    {
+      // uniform base + opaque 32-bit lane offset + constant: no per-element
+      // 64-bit address is computed ahead and kept live through the loops
+      const long base = (bh * Sk + k0) * D;
+      const uint32_t lane_off = opaque((uint32_t)((32 * w + 4 * hh) * D + li));
 #pragma unroll
-    for (int d = 0; d < ND; ++d)
+      for (int d = 0; d < ND; ++d)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int jl = 32 * w + 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (k0 + jl < Sk) {
-          const long off = (bh * Sk + k0 + jl) * D + 32 * d + li;
-          a.dk[off] = (bf16)(dk[d][v] * a.scale);
-          a.dv[off] = (bf16)dv[d][v];
+        for (int v = 0; v < 16; ++v) {
+          const int jl = 32 * w + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (k0 + jl < Sk) {
+            const uint32_t off = lane_off + (uint32_t)((8 * (v >> 2) + (v & 3)) * D + 32 * d);
+            a.dk[base + off] = (bf16)(dk[d][v] * a.scale);
+            a.dv[base + off] = (bf16)dv[d][v];
+          }
         }
-      }
+    }
     __syncthreads();   // every thread has read sm.item and finished with LDS
   }
   if (t == 0) {
@@ -416,12 +539,19 @@ void attn_bwd_kernel(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- epilogue
+// dQ = bf16(accumulator) for the real rows; 8 elements per thread.
+template <int D>
 __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc,
-                                                         bf16* __restrict__ dq, long n8) {
+                                                         bf16* __restrict__ dq, long n8, int Sq,
+                                                         int Sqp) {
+  constexpr int TPR = D / 8;
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
-  const float4 x = reinterpret_cast<const float4*>(acc)[2 * i];
-  const float4 y = reinterpret_cast<const float4*>(acc)[2 * i + 1];
+  const long row = i / TPR;
+  const long arow = (row / Sq) * Sqp + row % Sq;
+  const float4* src = reinterpret_cast<const float4*>(acc + arow * D + 8 * (i % TPR));
+  const float4 x = src[0];
+  const float4 y = src[1];
   bf16x8 r;
   r[0] = (bf16)x.x; r[1] = (bf16)x.y; r[2] = (bf16)x.z; r[3] = (bf16)x.w;
   r[4] = (bf16)y.x; r[5] = (bf16)y.y; r[6] = (bf16)y.z; r[7] = (bf16)y.w;
@@ -433,13 +563,18 @@ int bwd_blocks_per_cu(int) { return 1; }
 hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, hipStream_t stream,
                            const KernelEvents& ev) {
   const long rows = (long)a.B * a.H * a.Sq;
+  const int Sqp = a.nQ * BQ;
+  const long acc_rows = (long)a.B * a.H * Sqp;
   const long n8 = rows * head_dim / 8;
-  const unsigned pre_grid = (unsigned)((n8 + 255) / 256);
+  const unsigned pre_grid = (unsigned)((acc_rows * head_dim / 8 + 255) / 256);
+  const unsigned cvt_grid = (unsigned)((n8 + 255) / 256);
   hipError_t err;
   if (head_dim == 128)
-    bwd_pre_kernel<128><<<pre_grid, 256, 0, stream>>>(a.o, a.dout, a.delta, a.dq_acc, rows);
+    bwd_pre_kernel<128><<<pre_grid, 256, 0, stream>>>(a.o, a.dout, a.delta, a.dq_acc, acc_rows,
+                                                      a.Sq, Sqp);
   else
-    bwd_pre_kernel<64><<<pre_grid, 256, 0, stream>>>(a.o, a.dout, a.delta, a.dq_acc, rows);
+    bwd_pre_kernel<64><<<pre_grid, 256, 0, stream>>>(a.o, a.dout, a.delta, a.dq_acc, acc_rows,
+                                                     a.Sq, Sqp);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ev.begin && (err = hipEventRecord(ev.begin, stream)) != hipSuccess) return err;
   if (grid > 0) {
@@ -450,7 +585,12 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, hipStream_t
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (ev.end && (err = hipEventRecord(ev.end, stream)) != hipSuccess) return err;
-  dq_convert_kernel<<<pre_grid, 256, 0, stream>>>(a.dq_acc, a.dq, n8);
+  if (rows > 0) {
+    if (head_dim == 128)
+      dq_convert_kernel<128><<<cvt_grid, 256, 0, stream>>>(a.dq_acc, a.dq, n8, a.Sq, Sqp);
+    else
+      dq_convert_kernel<64><<<cvt_grid, 256, 0, stream>>>(a.dq_acc, a.dq, n8, a.Sq, Sqp);
+  }
   return hipGetLastError();
 }
 

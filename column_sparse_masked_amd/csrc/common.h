@@ -108,28 +108,37 @@ __device__ __forceinline__ void pin_vgpr(f32x16& x) { asm volatile("" : "+v"(x))
 __device__ __forceinline__ void pin_agpr(bf16x8& x) { asm volatile("" : "+a"(x)); }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100,
+              kSchedDsWrite = 0x200;
 
-// Orders the MFMAs and LDS reads of the current scheduling region as
-// LEAD reads, then (MFMA, read) pairs, then the remaining MFMAs, so that
-// LEAD operand loads are in flight ahead of the matrix core.
-template <int N_MFMA, int N_READ, int LEAD>
-__device__ __forceinline__ void pipeline_mfma_reads() {
+// Orders the current scheduling region as: LEAD LDS reads, then N_MFMA steps
+// of (one MFMA, up to VALU vector-ALU instructions, up to WRITES LDS writes,
+// one LDS read while reads remain).  Operand reads thus run LEAD MFMAs ahead
+// of the matrix core, and independent vector work fills the MFMA shadows.
+template <int N_MFMA, int N_READ, int LEAD, int VALU, int WRITES>
+__device__ __forceinline__ void interleave_mfma() {
   static_assert(N_READ >= LEAD, "");
-#pragma unroll
-  for (int i = 0; i < LEAD; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LEAD, 0);
 #pragma unroll
   for (int i = 0; i < N_MFMA; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (VALU > 0) __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU, 0);
+    if (WRITES > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, WRITES, 0);
     if (i + LEAD < N_READ) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
   }
 }
 
-// Entry i of a uint16 tile list through an aligned 32-bit load, so that a
-// list walked by a whole workgroup is read with scalar loads.
+// Entry i of a uint16 tile list, read through the scalar cache: the list of
+// a work item is the same for the whole workgroup, so the aligned 32-bit word
+// holding the entry is fetched with a scalar load (constant address space).
+// Such loads are tracked by lgkmcnt, not vmcnt, so waiting for one does not
+// drain the vector memory queue.  The word may reach two bytes past the last
+// entry; the tile-info buffer always continues past a list (the work queues
+// follow it).
+typedef __attribute__((address_space(4))) const uint32_t const_u32;
 __device__ __forceinline__ int list_entry(const uint16_t* lst, int i) {
   const uintptr_t addr = reinterpret_cast<uintptr_t>(lst + i);
-  const uint32_t word = *reinterpret_cast<const uint32_t*>(addr & ~(uintptr_t)3);
+  const uint32_t word = *(const_u32*)(addr & ~(uintptr_t)3);
   return (int)((addr & 2) ? (word >> 16) : (word & 0xffffu));
 }
 

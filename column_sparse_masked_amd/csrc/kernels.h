@@ -50,7 +50,7 @@ struct BwdArgs {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  float* dq_acc;      // fp32 [B][H][Sq][D]
+  float* dq_acc;      // fp32 [B][H][nQ*BQ][D]: rows padded to whole query blocks
   float* delta;       // fp32 [B][H][Sq]
   int B, H, Hm, Sq, Sk, nQ, nK;
   float scale;        // softmax_scale

@@ -98,7 +98,8 @@ fm_status fm_tile_shape(const fm_problem* p, int32_t* block_q, int32_t* block_k)
 fm_status fm_tileinfo_layout_query(const fm_problem* p, fm_tileinfo_layout* out);
 
 /* Bytes of device workspace fm_attn_bwd needs: an fp32 dQ accumulator
- * [B][H][Sq][D] followed by fp32 [B][H][Sq] row terms (host only). */
+ * [B][H][Sq_pad][D], Sq_pad = Sq rounded up to whole query blocks of the tile
+ * shape, followed by fp32 [B][H][Sq] row terms (host only). */
 fm_status fm_bwd_workspace_bytes(const fm_problem* p, size_t* bytes);
 
 /* Number of compute units of the current device (queried once, then cached). */
