@@ -186,7 +186,7 @@ def main(argv=None):
         att.forward(tq, tk, tv, tb, o=o, lse=lse)
         if ev is not None:
             ev["s2"].record()
-            _lib.set_kernel_events(ev["bk0"], ev["bk1"])
+            _lib.set_kernel_events(ev["bk0"], ev["bk1"], ev["bq0"], ev["bq1"])
         att.backward(tq, tk, tv, o, tdo, lse, tb, dq=dq, dk=dk, dv=dv)
         if ev is not None:
             _lib.set_kernel_events(None, None)
@@ -197,7 +197,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     print(f"# warmup {args.warmup} steps done", file=sys.stderr, flush=True)
 
-    evs = [{n: new_event() for n in ("s0", "s1", "s2", "s3", "fk0", "fk1", "bk0", "bk1")}
+    evs = [{n: new_event() for n in ("s0", "s1", "s2", "s3", "fk0", "fk1", "bk0", "bk1", "bq0", "bq1")}
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -211,15 +211,18 @@ def main(argv=None):
         return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
 
     t_tile, t_fwd, t_bwd = avg_ms("s0", "s1"), avg_ms("s1", "s2"), avg_ms("s2", "s3")
-    k_fwd, k_bwd = avg_ms("fk0", "fk1"), avg_ms("bk0", "bk1")
+    k_fwd, k_bwd, k_dq = avg_ms("fk0", "fk1"), avg_ms("bk0", "bk1"), avg_ms("bq0", "bq1")
     ms_per_step = wall / args.steps * 1e3
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel: the longer of the forward and backward attention kernels
-    if k_bwd >= k_fwd:
-        kname, kflops, kms, srcs = "attn_bwd_kernel", f_bwd, k_bwd, ["bwd.hip", "common.h"]
-    else:
-        kname, kflops, kms, srcs = "attn_fwd_kernel", f_fwd, k_fwd, ["fwd.hip", "common.h"]
+    # Dominant kernel: the longest of the three attention kernels, credited
+    # with the products it computes itself: forward S, PV (4 D nnz); dK/dV
+    # kernel S, dP, dV, dK (8 D nnz); dQ kernel S, dP, dQ (6 D nnz).
+    f_dkdv, f_dq = 8.0 * w.D * nnz, 6.0 * w.D * nnz
+    kernels = [("attn_fwd_kernel", f_fwd, k_fwd, ["fwd.hip", "common.h"]),
+               ("attn_bwd_kernel", f_dkdv, k_bwd, ["bwd.hip", "common.h"]),
+               ("attn_bwd_dq_kernel", f_dq, k_dq, ["bwd_dq.hip", "common.h"])]
+    kname, kflops, kms, srcs = max(kernels, key=lambda x: x[2])
     achieved = kflops / (kms * 1e-3) / 1e12
     tag = f"cfg{args.config}_seed{w.seed}"
     roofline = {
@@ -255,7 +258,8 @@ def main(argv=None):
         "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "stages_ms": {"tile_bounds": round(t_tile, 4), "fwd": round(t_fwd, 4), "bwd": round(t_bwd, 4)},
         "tflops_fwd_kernel": round(f_fwd / (k_fwd * 1e-3) / 1e12, 2),
-        "tflops_bwd_kernel": round(f_bwd / (k_bwd * 1e-3) / 1e12, 2),
+        "kernel_ms": {"fwd": round(k_fwd, 4), "bwd_dkdv": round(k_bwd, 4), "bwd_dq": round(k_dq, 4)},
+        "tflops_bwd_kernels_mask_effective": round(f_bwd / ((k_bwd + k_dq) * 1e-3) / 1e12, 2),
         "tflops_without_tile_pass": round((f_fwd + f_bwd) / ((t_fwd + t_bwd) * 1e-3) / 1e12, 2),
         "roofline": roofline,
         "cpu_baseline": None,

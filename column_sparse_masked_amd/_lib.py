@@ -169,17 +169,18 @@ def alloc_buffers(p: Problem, device) -> Buffers:
     return Buffers(ti, ws, L)
 
 
-lib.fm_set_kernel_events.argtypes = [_vp, _vp]
+lib.fm_set_kernel_events.argtypes = [_vp, _vp, _vp, _vp]
 lib.fm_set_kernel_events.restype = ctypes.c_int
 
 
-def set_kernel_events(begin, end):
+def set_kernel_events(begin, end, begin2=None, end2=None):
     """Record the torch.cuda.Event pair ``begin``/``end`` around the main
     attention kernel of the following fm_attn_fwd / fm_attn_bwd calls on this
-    thread; ``None, None`` turns it off.  The events must already exist on the
-    device (torch creates them at their first record)."""
-    if begin is None and end is None:
-        _check(lib.fm_set_kernel_events(None, None), "fm_set_kernel_events")
-        return
-    _check(lib.fm_set_kernel_events(ctypes.c_void_p(begin.cuda_event), ctypes.c_void_p(end.cuda_event)),
+    thread (the forward kernel; the backward's dK/dV kernel) and
+    ``begin2``/``end2`` around the backward's dQ kernel; all ``None`` turns it
+    off.  The events must already exist on the device (torch creates them at
+    their first record)."""
+    def ptr(e):
+        return None if e is None else ctypes.c_void_p(e.cuda_event)
+    _check(lib.fm_set_kernel_events(ptr(begin), ptr(end), ptr(begin2), ptr(end2)),
            "fm_set_kernel_events")

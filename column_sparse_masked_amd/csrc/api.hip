@@ -19,13 +19,6 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// rows of the fp32 dQ accumulator: every (batch, head) gets whole query
-// blocks, so that the backward's atomics need no row bound check
-size_t acc_rows(const fm_problem* p) {
-  const size_t nQ = ((size_t)p->seqlen_q + fm::BQ - 1) / fm::BQ;
-  return (size_t)p->batch * p->heads * nQ * fm::BQ;
-}
-
 fm_status check_problem(const fm_problem* p) {
   if (!p) return FM_ERR_NULL;
   if (p->batch < 0 || p->heads < 1 || p->mask_heads < 1 || p->seqlen_q < 0 || p->seqlen_k < 0)
@@ -144,7 +137,7 @@ fm_status fm_bwd_workspace_bytes(const fm_problem* p, size_t* bytes) {
   if (st != FM_OK) return st;
   if (!bytes) return FM_ERR_NULL;
   const size_t rows = (size_t)p->batch * p->heads * p->seqlen_q;
-  *bytes = align256(acc_rows(p) * p->head_dim * sizeof(float)) + align256(rows * sizeof(float));
+  *bytes = align256(rows * sizeof(float));
   return FM_OK;
 }
 
@@ -156,10 +149,13 @@ fm_status fm_device_cu_count(int32_t* cus) {
   return st;
 }
 
-fm_status fm_set_kernel_events(void* begin, void* end) {
-  if ((begin == nullptr) != (end == nullptr)) return FM_ERR_NULL;
+fm_status fm_set_kernel_events(void* begin, void* end, void* begin2, void* end2) {
+  if ((begin == nullptr) != (end == nullptr) || (begin2 == nullptr) != (end2 == nullptr))
+    return FM_ERR_NULL;
   g_events.begin = static_cast<hipEvent_t>(begin);
   g_events.end = static_cast<hipEvent_t>(end);
+  g_events.begin2 = static_cast<hipEvent_t>(begin2);
+  g_events.end2 = static_cast<hipEvent_t>(end2);
   return FM_OK;
 }
 
@@ -262,7 +258,6 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   }
   int cus = 0;
   if ((st = cu_count(&cus)) != FM_OK) return st;
-  const size_t rows = (size_t)p->batch * p->heads * p->seqlen_q;
   fm::BwdArgs a;
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
@@ -274,12 +269,14 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   a.list_k = at<uint16_t>(tileinfo, L.list_k);
   a.cnt_k = at<int>(tileinfo, L.cnt_k);
   a.queue = at<uint32_t>(tileinfo, L.bwd_queue);
+  a.list_q = at<uint16_t>(tileinfo, L.list_q);
+  a.cnt_q = at<int>(tileinfo, L.cnt_q);
+  a.queue_q = at<uint32_t>(tileinfo, L.fwd_queue);
   a.counters = at<uint32_t>(tileinfo, L.counters);
   a.dq = static_cast<__bf16*>(dq);
   a.dk = static_cast<__bf16*>(dk);
   a.dv = static_cast<__bf16*>(dv);
-  a.dq_acc = static_cast<float*>(workspace);
-  a.delta = at<float>(workspace, align256(acc_rows(p) * p->head_dim * sizeof(float)));
+  a.delta = static_cast<float*>(workspace);
   a.B = p->batch; a.H = p->heads; a.Hm = p->mask_heads;
   a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
   a.scale = p->softmax_scale;
@@ -287,7 +284,10 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   const long items = (long)p->batch * p->heads * L.nK;
   const long slots = (long)cus * fm::bwd_blocks_per_cu(p->head_dim);
   const int grid = (int)(items < slots ? items : slots);
-  return fm::launch_attn_bwd(a, p->head_dim, grid, s, g_events) == hipSuccess ? FM_OK : FM_ERR_HIP;
+  const long dq_items = (long)p->batch * p->heads * L.nQ;
+  const int dq_grid = (int)(dq_items < cus ? dq_items : cus);
+  return fm::launch_attn_bwd(a, p->head_dim, grid, dq_grid, s, g_events) == hipSuccess ? FM_OK
+                                                                                        : FM_ERR_HIP;
 }
 
 }  // extern "C"

@@ -1,7 +1,7 @@
-// Backward of column-sparse masked attention (bf16 MFMA, fp32 accumulate).
+// Backward of column-sparse masked attention (bf16 MFMA, fp32 accumulate):
+// the key-stationary half.
 //
-//   bwd_pre_kernel   Delta_i = sum_d dO_id O_id (fp32) and a zeroed fp32 dQ
-//                    accumulator;
+//   bwd_pre_kernel   Delta_i = sum_d dO_id O_id (fp32);
 //   attn_bwd_kernel  persistent, key-block stationary: each workgroup takes an
 //                    item (batch*head, key block), keeps that block's K and V
 //                    in registers (32 keys per wave) and its dK, dV
@@ -9,17 +9,18 @@
 //                    blocks that see the key block (the tiles the mask does not
 //                    skip), 64 query rows at a time:
 //                        S = Q K^T, P = exp(S - LSE) (interval mask on partial
-//                        tiles only), dP = dO V^T, dS = P (dP - Delta),
-//                        dV += P^T dO, dK += dS^T Q,
-//                        dQ += dS K   (fp32 atomics into the accumulator);
-//   dq_convert_kernel  dQ = bf16(accumulator), round to nearest even.
+//                        tiles only), dP = dO V^T, dS = P (dP - Delta) scale,
+//                        dV += P^T dO, dK += dS^T Q;
+//   attn_bwd_dq_kernel (its own file) then computes dQ query-stationary.
+// dQ is not accumulated here: fp32 atomic adds into a shared accumulator run
+// at a fraction of the rate of plain stores on this GPU, and at this kernel's
+// speed they, not the matrix cores, would set its pace.
 // With S = Q K^T computed as C[i][j] a lane holds one key and several query
 // rows, which is exactly the A-operand shape of P^T dO and dS^T Q.  Each chunk
 // of Q and dO is therefore staged twice, row-major (A operands of S and dP)
-// and transposed (B operands of dV and dK), and K is staged transposed once
-// per item (B operand of dQ), so that every MFMA operand read from LDS is one
-// 16-byte load.  The next chunk is fetched into registers while the current
-// one computes, and the dQ atomics of a chunk are issued after those loads.
+// and transposed (B operands of dV and dK), so that every MFMA operand read
+// from LDS is one 16-byte load.  The next chunk is fetched into registers
+// while the current one computes.
 #include <climits>
 #include <type_traits>
 
@@ -32,38 +33,25 @@ constexpr int QC = 64;   // query rows per backward chunk
 constexpr int CPB = BQ / QC;   // chunks per query block
 
 // ---------------------------------------------------------------- prologue
-// Delta and a zeroed accumulator.  The accumulator has Sqp >= Sq rows per
-// (batch, head) (whole query blocks); thread groups of D/8 walk its rows and
-// the real ones (i < Sq) also get their Delta.
+// Delta of every row; thread groups of D/8 threads per row.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o,
                                                       const bf16* __restrict__ dout,
-                                                      float* __restrict__ delta,
-                                                      float* __restrict__ dq_acc, long acc_rows,
-                                                      int Sq, int Sqp) {
+                                                      float* __restrict__ delta, long rows) {
   constexpr int TPR = D / 8;   // threads per row, 8 elements each
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long arow = gid / TPR;   // accumulator row
+  const long row = gid / TPR;
   const int c = (int)(gid % TPR);
-  const long bh = arow / Sqp;
-  const int i = (int)(arow % Sqp);
-  const bool real = arow < acc_rows && i < Sq;
-  const long row = bh * Sq + i;
   float sum = 0.f;
-  if (real) {
+  if (row < rows) {
     const bf16x8 ov = reinterpret_cast<const bf16x8*>(o)[row * TPR + c];
     const bf16x8 dv = reinterpret_cast<const bf16x8*>(dout)[row * TPR + c];
 #pragma unroll
     for (int e = 0; e < 8; ++e) sum += (float)ov[e] * (float)dv[e];
   }
-  if (arow < acc_rows) {
-    float4* z = reinterpret_cast<float4*>(dq_acc + arow * D + 8 * c);
-    z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-    z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-  if (real && c == 0) delta[row] = sum;
+  if (row < rows && c == 0) delta[row] = sum;
 }
 
 // ---------------------------------------------------------------- main
@@ -71,18 +59,14 @@ template <int D>
 struct alignas(16) BwdSmem {
   static constexpr int QST = D + 8;    // Q / dO row stride (elements)
   static constexpr int QTS = QC + 8;   // Q^T / dO^T row stride; rows in vt_pos order
-  static constexpr int KTS = BK + 8;   // K^T row stride; keys in natural order
-  static constexpr int DSS = BK + 8;   // dS row stride
   // small and many-times-indexed arrays first, so that their addresses fit
   // the 16-bit immediate offset of LDS instructions
   float lse2[QC];   // LSE * log2(e); +inf for rows past the end
   float delta[QC];
-  bf16 ds[QC * DSS];
   bf16 q[QC * QST];
   bf16 dout[QC * QST];
   bf16 qt[D * QTS];
   bf16 dot[D * QTS];
-  bf16 kt[D * KTS];
   uint32_t item;
 };
 
@@ -154,7 +138,7 @@ __device__ __forceinline__ void load_chunk(ChunkStage<D>& r, BufRsrc qb, BufRsrc
 
 template <int D, typename Smem>
 __device__ __forceinline__ void store_chunk(const ChunkStage<D>& r, Smem& sm, int q0, int Sq,
-                                            unsigned t) {
+                                            float scale, unsigned t) {
   using C = ChunkStage<D>;
   constexpr int QST = Smem::QST, QTS = Smem::QTS;
 #pragma unroll
@@ -176,38 +160,11 @@ __device__ __forceinline__ void store_chunk(const ChunkStage<D>& r, Smem& sm, in
     FM_T_ROW(4); FM_T_ROW(5); FM_T_ROW(6); FM_T_ROW(7);
 #undef FM_T_ROW
   }
-  // LSE * log2(e), +inf for rows past the end (P = 0 there); Delta as is
+  // LSE * log2(e), +inf for rows past the end (P = 0 there); Delta * scale
   if (t < QC)
     sm.lse2[t] = q0 + (int)t < Sq ? r.row_term * kLog2e : INFINITY;
   else if (t < 2 * QC)
-    sm.delta[t - QC] = r.row_term;
-}
-
-// K^T of a key block into LDS (once per item): thread t transposes 4*NV
-// consecutive keys x 8 head-dim columns, as the forward does for V.
-template <int D, typename Smem>
-__device__ __forceinline__ void stage_kt(BufRsrc kb, int k0, Smem& sm, unsigned t) {
-  constexpr int CPR = D / 8, NV = (BK / 4) * CPR / 256, KTS = Smem::KTS;
-  const int key = 4 * NV * (int)((t & 7u) + 8u * (t / (8u * CPR)));
-  const int c = (int)((t >> 3) % CPR);
-  bf16x8 v[4 * NV];
-  const uint32_t base = ((uint32_t)(k0 + key) * CPR + c) * 16u;
-#pragma unroll
-  for (int q = 0; q < 4 * NV; ++q) v[q] = buf_load16(kb, base + (uint32_t)q * (D * 2));
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    bf16* dst = sm.kt + (8 * c) * KTS + key + 4 * i;
-    const bf16x16 p01 = __builtin_shufflevector(v[4 * i], v[4 * i + 1], 0, 8, 1, 9, 2, 10, 3, 11, 4,
-                                                12, 5, 13, 6, 14, 7, 15);
-    const bf16x16 p23 = __builtin_shufflevector(v[4 * i + 2], v[4 * i + 3], 0, 8, 1, 9, 2, 10, 3, 11,
-                                                4, 12, 5, 13, 6, 14, 7, 15);
-#define FM_T_ROW(e)                                                                       \
-  *reinterpret_cast<bf16x4*>(dst + (e) * KTS) =                                           \
-      __builtin_shufflevector(p01, p23, 2 * (e), 2 * (e) + 1, 16 + 2 * (e), 17 + 2 * (e))
-    FM_T_ROW(0); FM_T_ROW(1); FM_T_ROW(2); FM_T_ROW(3);
-    FM_T_ROW(4); FM_T_ROW(5); FM_T_ROW(6); FM_T_ROW(7);
-#undef FM_T_ROW
-  }
+    sm.delta[t - QC] = r.row_term * scale;
 }
 
 template <int D>
@@ -215,7 +172,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bwd_kernel(const BwdArgs a) {
   constexpr int NS = D / 16, ND = D / 32;
   using Smem = BwdSmem<D>;
-  constexpr int QST = Smem::QST, QTS = Smem::QTS, KTS = Smem::KTS, DSS = Smem::DSS;
+  constexpr int QST = Smem::QST, QTS = Smem::QTS;
   __shared__ Smem sm;
 
   const unsigned t = threadIdx.x;
@@ -285,7 +242,6 @@ void attn_bwd_kernel(const BwdArgs a) {
 
     const int nchunks = CPB * cnt;   // each query block is CPB chunks of QC rows
     if (nchunks > 0) {
-      stage_kt<D>(kbase, k0, sm, t);
       // chunk c starts at row block_row(c) * BQ + (c % CPB) * QC
       auto chunk_q0 = [&](int c) __attribute__((always_inline)) {
         const int e = list_at(c / CPB);
@@ -294,21 +250,11 @@ void attn_bwd_kernel(const BwdArgs a) {
       ChunkStage<D> cs;
       int e_cur = list_at(0);
       load_chunk<D>(cs, qbase, obase, lbase, dbase, chunk_q0(0), t);
-      store_chunk<D>(cs, sm, chunk_q0(0), Sq, t);
+      store_chunk<D>(cs, sm, chunk_q0(0), Sq, a.scale, t);
       __syncthreads();
-      // B operands of dQ = dS K for this wave's head-dim columns 32 (w % ND)..:
-      // the same for every chunk of the item, so read from K^T once
-      bf16x8 ktr[BK / 16];
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks)
-        ktr[ks] = as_bf16x8(&sm.kt[(32 * (w % ND) + li) * KTS + 16 * ks + 8 * hh]);
-
       // Per chunk c (its Q, dO, Q^T, dO^T and row terms in LDS):
-      //   chunk c+1 -> registers; S, dP, P, dS (-> LDS), dV, dK | barrier |
-      //   chunk c+1 -> LDS; dQ = dS K -> atomics | barrier
-      // The loads of chunk c+1 are issued after the atomics of chunk c-1, so
-      // waiting for them also waits for those atomics, which had the whole
-      // previous dQ step and this chunk's work to complete.
+      //   chunk c+1 -> registers; S, dP, P, dS, dV, dK | barrier |
+      //   chunk c+1 -> LDS | barrier
       for (int c = 0; c < nchunks; ++c) {
         const int q0 = min(e_cur & kListIndex, a.nQ - 1) * BQ + (c % CPB) * QC;
         const bool need_mask = (e_cur & kListPartial) || ragged_k;
@@ -323,9 +269,9 @@ void attn_bwd_kernel(const BwdArgs a) {
         // the matrix cores work on the other:
         //   (a)  S, dP of half 0
         //   (b1) S of half 1          |  P of half 0
-        //   (b2) dP of half 1         |  dS of half 0 (-> LDS)
+        //   (b2) dP of half 1         |  dS of half 0
         //   (c1) dV from half 0       |  P of half 1
-        //   (c2) dK from half 0       |  dS of half 1 (-> LDS)
+        //   (c2) dK from half 0       |  dS of half 1
         //   (d)  dV, dK from half 1
         // On partial tiles P is masked between the P and dS steps (a separate,
         // uniform branch that only rewrites P in place).
@@ -382,13 +328,13 @@ void attn_bwd_kernel(const BwdArgs a) {
               pf[ib][v] = __builtin_bit_cast(float, __builtin_bit_cast(int, pf[ib][v]) & keep);
             }
           };
-          // dS = P (dP - Delta) into the MFMA operand and the LDS tile; P packed
+          // scale * dS = P (scale dP - scale Delta) into the MFMA operand (dK
+          // then needs no scaling); P packed
           auto ds_of = [&](const f32x16& dpv, int ib, int v) __attribute__((always_inline)) {
             const float p = pf[ib][v];
-            const float dsv = p * (dpv[v] - f4(drow[v >> 2], v & 3));
+            const float dsv = p * fmaf(dpv[v], a.scale, -f4(drow[v >> 2], v & 3));
             pb[ib][v >> 3][v & 7] = (bf16)p;
             dsb[ib][v >> 3][v & 7] = (bf16)dsv;
-            sm.ds[(32 * ib + 8 * (v >> 2) + 4 * hh + (v & 3)) * DSS + 32 * w + li] = (bf16)dsv;
           };
           constexpr int EPK = 16 / NS;   // elements per MFMA in (b1), (b2)
           constexpr int EPC = 16 / ND;   // elements per MFMA in (c1), (c2)
@@ -420,7 +366,7 @@ void attn_bwd_kernel(const BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < EPK; ++e) ds_of(dp0, 0, EPK * kk + e);
           }
-          interleave_mfma<NS, NS, 3, 4 * EPK, EPK>();
+          interleave_mfma<NS, NS, 3, 4 * EPK, 0>();
           __builtin_amdgcn_sched_barrier(0);
           // (c1)
           read_rows(1);
@@ -448,7 +394,7 @@ void attn_bwd_kernel(const BwdArgs a) {
 #pragma unroll
               for (int e = 0; e < EPC / 2; ++e) ds_of(dp1, 1, (EPC / 2) * (2 * d + t2) + e);
             }
-          interleave_mfma<2 * ND, 2 * ND, 3, 4 * EPC / 2, EPC / 2>();
+          interleave_mfma<2 * ND, 2 * ND, 3, 4 * EPC / 2, 0>();
           __builtin_amdgcn_sched_barrier(0);
           // (d)
 #pragma unroll
@@ -465,50 +411,15 @@ void attn_bwd_kernel(const BwdArgs a) {
           pin_agpr(dv[d]);
           pin_agpr(dk[d]);
         }
-        __syncthreads();   // dS is in LDS; every wave is done with this chunk's Q and dO
-        if (has_next) store_chunk<D>(cs, sm, chunk_q0(c + 1), Sq, t);
+        __syncthreads();   // every wave is done with this chunk's Q and dO
+        if (has_next) store_chunk<D>(cs, sm, chunk_q0(c + 1), Sq, a.scale, t);
 
-        // ---- dQ[q0.., :] += scale dS K: wave w takes head-dim columns
-        //      32 (w % ND) .. +32 of the chunk rows 32 ib .. +32 for ib = w / ND, +4/ND, ...
-        {
-          constexpr int NB = (QC / 32) * ND / 4;   // (ib, d) blocks per wave
-          const int d = w % ND;
-          f32x16 acc[NB];
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < BK / 16; ++ks) {
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-              const int ib = (w + 4 * j) / ND;
-              acc[j] = mfma32(as_bf16x8(&sm.ds[(32 * ib + li) * DSS + 16 * ks + 8 * hh]), ktr[ks], acc[j]);
-            }
-          }
-          // The accumulator has whole query blocks of rows, so no row needs a
-          // bound check.  Addresses: uniform base + 32-bit lane offset (kept
-          // opaque so that the per-row offsets are not hoisted out of the
-          // loop and kept live) + a constant per row.
-          char* const dq0 = reinterpret_cast<char*>(a.dq_acc + ((long)bh * a.nQ * BQ + q0) * D);
-          const uint32_t lane_off = opaque((uint32_t)(4 * hh * D + 32 * d + li) * 4u);
-#pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            const int ib = (w + 4 * j) / ND;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const uint32_t row = 32 * ib + 8 * (v >> 2) + (v & 3);
-              unsafeAtomicAdd(reinterpret_cast<float*>(dq0 + (lane_off + row * (D * 4))),
-                              acc[j][v] * a.scale);
-            }
-          }
-        }
-        __syncthreads();   // every wave is done with dS; the next chunk is in LDS
+        __syncthreads();   // the next chunk is in LDS
         e_cur = e_next;
       }
     }
 
-    // ---- write dK (scaled) and dV: lane holds column 32d + li, keys 8r + 4hh + q ----
+    // ---- write dK and dV: lane holds column 32d + li, keys 8r + 4hh + q ----
     {
       // uniform base + opaque 32-bit lane offset + constant: no per-element
       // 64-bit address is computed ahead and kept live through the loops
@@ -521,7 +432,7 @@ void attn_bwd_kernel(const BwdArgs a) {
           const int jl = 32 * w + 8 * (v >> 2) + 4 * hh + (v & 3);
           if (k0 + jl < Sk) {
             const uint32_t off = lane_off + (uint32_t)((8 * (v >> 2) + (v & 3)) * D + 32 * d);
-            a.dk[base + off] = (bf16)(dk[d][v] * a.scale);
+            a.dk[base + off] = (bf16)dk[d][v];
             a.dv[base + off] = (bf16)dv[d][v];
           }
         }
@@ -538,44 +449,20 @@ void attn_bwd_kernel(const BwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- epilogue
-// dQ = bf16(accumulator) for the real rows; 8 elements per thread.
-template <int D>
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc,
-                                                         bf16* __restrict__ dq, long n8, int Sq,
-                                                         int Sqp) {
-  constexpr int TPR = D / 8;
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const long row = i / TPR;
-  const long arow = (row / Sq) * Sqp + row % Sq;
-  const float4* src = reinterpret_cast<const float4*>(acc + arow * D + 8 * (i % TPR));
-  const float4 x = src[0];
-  const float4 y = src[1];
-  bf16x8 r;
-  r[0] = (bf16)x.x; r[1] = (bf16)x.y; r[2] = (bf16)x.z; r[3] = (bf16)x.w;
-  r[4] = (bf16)y.x; r[5] = (bf16)y.y; r[6] = (bf16)y.z; r[7] = (bf16)y.w;
-  reinterpret_cast<bf16x8*>(dq)[i] = r;
-}
-
 int bwd_blocks_per_cu(int) { return 1; }
 
-hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, hipStream_t stream,
-                           const KernelEvents& ev) {
+hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, int dq_grid,
+                           hipStream_t stream, const KernelEvents& ev) {
   const long rows = (long)a.B * a.H * a.Sq;
-  const int Sqp = a.nQ * BQ;
-  const long acc_rows = (long)a.B * a.H * Sqp;
-  const long n8 = rows * head_dim / 8;
-  const unsigned pre_grid = (unsigned)((acc_rows * head_dim / 8 + 255) / 256);
-  const unsigned cvt_grid = (unsigned)((n8 + 255) / 256);
   hipError_t err;
-  if (head_dim == 128)
-    bwd_pre_kernel<128><<<pre_grid, 256, 0, stream>>>(a.o, a.dout, a.delta, a.dq_acc, acc_rows,
-                                                      a.Sq, Sqp);
-  else
-    bwd_pre_kernel<64><<<pre_grid, 256, 0, stream>>>(a.o, a.dout, a.delta, a.dq_acc, acc_rows,
-                                                     a.Sq, Sqp);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (rows > 0) {
+    const unsigned pre_grid = (unsigned)((rows * head_dim / 8 + 255) / 256);
+    if (head_dim == 128)
+      bwd_pre_kernel<128><<<pre_grid, 256, 0, stream>>>(a.o, a.dout, a.delta, rows);
+    else
+      bwd_pre_kernel<64><<<pre_grid, 256, 0, stream>>>(a.o, a.dout, a.delta, rows);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   if (ev.begin && (err = hipEventRecord(ev.begin, stream)) != hipSuccess) return err;
   if (grid > 0) {
     if (head_dim == 128)
@@ -585,13 +472,10 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, hipStream_t
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (ev.end && (err = hipEventRecord(ev.end, stream)) != hipSuccess) return err;
-  if (rows > 0) {
-    if (head_dim == 128)
-      dq_convert_kernel<128><<<cvt_grid, 256, 0, stream>>>(a.dq_acc, a.dq, n8, a.Sq, Sqp);
-    else
-      dq_convert_kernel<64><<<cvt_grid, 256, 0, stream>>>(a.dq_acc, a.dq, n8, a.Sq, Sqp);
-  }
-  return hipGetLastError();
+  if (ev.begin2 && (err = hipEventRecord(ev.begin2, stream)) != hipSuccess) return err;
+  if ((err = launch_attn_bwd_dq(a, head_dim, dq_grid, stream)) != hipSuccess) return err;
+  if (ev.end2 && (err = hipEventRecord(ev.end2, stream)) != hipSuccess) return err;
+  return hipSuccess;
 }
 
 }  // namespace fm

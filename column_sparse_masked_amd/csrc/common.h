@@ -15,7 +15,7 @@ constexpr int kListIndex = 0x7fff;
 
 // counters[] slots inside the tileinfo buffer
 constexpr int kCtrFwdItems = 0, kCtrBwdItems = 1, kCtrFwdNext = 2, kCtrBwdNext = 3,
-              kCtrFwdExit = 4, kCtrBwdExit = 5;
+              kCtrFwdExit = 4, kCtrBwdExit = 5, kCtrDqNext = 6, kCtrDqExit = 7;
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -108,8 +108,8 @@ __device__ __forceinline__ void pin_vgpr(f32x16& x) { asm volatile("" : "+v"(x))
 __device__ __forceinline__ void pin_agpr(bf16x8& x) { asm volatile("" : "+a"(x)); }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100,
-              kSchedDsWrite = 0x200;
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedVmem = 0x010,
+              kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
 
 // Orders the current scheduling region as: LEAD LDS reads, then N_MFMA steps
 // of (one MFMA, up to VALU vector-ALU instructions, up to WRITES LDS writes,

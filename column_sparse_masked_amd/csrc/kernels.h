@@ -43,14 +43,16 @@ struct BwdArgs {
   const __bf16* dout;
   const float* lse;
   const int4* bounds;
-  const uint16_t* list_k;
+  const uint16_t* list_k;    // key-stationary walk (dK, dV)
   const int* cnt_k;
   const uint32_t* queue;
+  const uint16_t* list_q;    // query-stationary walk (dQ)
+  const int* cnt_q;
+  const uint32_t* queue_q;
   uint32_t* counters;
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  float* dq_acc;      // fp32 [B][H][nQ*BQ][D]: rows padded to whole query blocks
   float* delta;       // fp32 [B][H][Sq]
   int B, H, Hm, Sq, Sk, nQ, nK;
   float scale;        // softmax_scale
@@ -59,18 +61,21 @@ struct BwdArgs {
 
 hipError_t launch_tile_bounds(const TileArgs& a, hipStream_t stream);
 // Optional events recorded right before / after the main attention kernel
-// (null: not recorded).
+// (the forward kernel, the backward's dK/dV kernel) and around the backward's
+// dQ kernel (null: not recorded).
 struct KernelEvents {
   hipEvent_t begin = nullptr, end = nullptr;
+  hipEvent_t begin2 = nullptr, end2 = nullptr;
 };
 
 hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream,
                            const KernelEvents& ev);
-hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, hipStream_t stream,
-                           const KernelEvents& ev);
+hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, int dq_grid,
+                           hipStream_t stream, const KernelEvents& ev);
+hipError_t launch_attn_bwd_dq(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
 
 // Workgroups per compute unit the persistent kernels are sized for.
 int fwd_blocks_per_cu(int head_dim);
-int bwd_blocks_per_cu(int head_dim);
+int bwd_blocks_per_cu(int head_dim);   // the dQ kernel: one workgroup per CU
 
 }  // namespace fm

@@ -233,6 +233,8 @@ __global__ __launch_bounds__(kQueueThreads) void queue_kernel(
     counters[kCtrBwdNext] = 0;
     counters[kCtrFwdExit] = 0;
     counters[kCtrBwdExit] = 0;
+    counters[kCtrDqNext] = 0;
+    counters[kCtrDqExit] = 0;
   }
 }
 

@@ -97,9 +97,8 @@ fm_status fm_tile_shape(const fm_problem* p, int32_t* block_q, int32_t* block_k)
 /* Size and layout of the tileinfo buffer for problem p (host only). */
 fm_status fm_tileinfo_layout_query(const fm_problem* p, fm_tileinfo_layout* out);
 
-/* Bytes of device workspace fm_attn_bwd needs: an fp32 dQ accumulator
- * [B][H][Sq_pad][D], Sq_pad = Sq rounded up to whole query blocks of the tile
- * shape, followed by fp32 [B][H][Sq] row terms (host only). */
+/* Bytes of device workspace fm_attn_bwd needs: the fp32 [B][H][Sq] row terms
+ * Delta (host only). */
 fm_status fm_bwd_workspace_bytes(const fm_problem* p, size_t* bytes);
 
 /* Number of compute units of the current device (queried once, then cached). */
@@ -107,13 +106,15 @@ fm_status fm_device_cu_count(int32_t* cus);
 
 /* Benchmark hook.  While set, every fm_attn_fwd / fm_attn_bwd call made from
  * this host thread records the caller's hipEvent_t `begin` on its stream right
- * before launching its main attention kernel and `end` right after it, so that
- * hipEventElapsedTime(begin, end) spans that one kernel (the backward's
- * prologue and dQ conversion kernels fall outside).  Both events must have
- * been created with timing enabled.  fm_set_kernel_events(NULL, NULL) turns
- * the hook off; giving only one of the two is FM_ERR_NULL.  Nothing else about
- * the calls changes; a failed record makes the call return FM_ERR_HIP. */
-fm_status fm_set_kernel_events(void* begin, void* end);
+ * before launching its main attention kernel (the forward kernel; the
+ * backward's dK/dV kernel) and `end` right after it, and `begin2` / `end2`
+ * around the backward's dQ kernel, so that hipEventElapsedTime(begin, end)
+ * spans exactly one kernel (the backward's Delta prologue falls outside).
+ * Events must have been created with timing enabled.  All null turns the hook
+ * off; either pair may be null; giving only one event of a pair is
+ * FM_ERR_NULL.  Nothing else about the calls changes; a failed record makes
+ * the call return FM_ERR_HIP. */
+fm_status fm_set_kernel_events(void* begin, void* end, void* begin2, void* end2);
 
 /*
  * fm_tile_bounds - classify every (query block, key block) tile.
@@ -144,8 +145,9 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
  *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
  * `o` and `lse` are the forward's outputs.  `workspace` must hold
  * fm_bwd_workspace_bytes bytes, 16-byte aligned; its contents on entry do not
- * matter.  dQ is accumulated in fp32 with atomics, so its last bits can vary
- * from run to run; dK and dV are deterministic.
+ * matter.  Three kernels: Delta; dK and dV key-stationary over the tiles of
+ * each key block; dQ query-stationary over the tiles of each query block
+ * (S and dP recomputed, no atomics).  The results are deterministic.
  */
 fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
                       const void* o, const void* dout, const float* lse,
