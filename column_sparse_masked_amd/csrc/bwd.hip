@@ -55,14 +55,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
 }
 
 // ---------------------------------------------------------------- main
+// Row terms ride in the matrix products.  Each staged Q row carries, in the
+// 16 columns after its D values, the pair (hi, lo) of bf16 numbers whose sum
+// is -LSE / scale to about 16 bits (zeros elsewhere), and each dO row the pair
+// for -Delta.  With a constant B operand of ones in those two columns, one
+// more k-step of S = Q K^T and dP = dO V^T yields S - LSE / scale and
+// dP - Delta, so P = exp2(scale log2(e) S') and dS = scale P dP' need no
+// per-row value in the lanes, whose rows differ from lane to lane.
 template <int D>
 struct alignas(16) BwdSmem {
-  static constexpr int QST = D + 8;    // Q / dO row stride (elements)
+  static constexpr int QST = D + 24;   // Q / dO row stride: D values, 16 row-term columns, pad
   static constexpr int QTS = QC + 8;   // Q^T / dO^T row stride; rows in vt_pos order
-  // small and many-times-indexed arrays first, so that their addresses fit
-  // the 16-bit immediate offset of LDS instructions
-  float lse2[QC];   // LSE * log2(e); +inf for rows past the end
-  float delta[QC];
   bf16 q[QC * QST];
   bf16 dout[QC * QST];
   bf16 qt[D * QTS];
@@ -160,11 +163,37 @@ __device__ __forceinline__ void store_chunk(const ChunkStage<D>& r, Smem& sm, in
     FM_T_ROW(4); FM_T_ROW(5); FM_T_ROW(6); FM_T_ROW(7);
 #undef FM_T_ROW
   }
-  // LSE * log2(e), +inf for rows past the end (P = 0 there); Delta * scale
-  if (t < QC)
-    sm.lse2[t] = q0 + (int)t < Sq ? r.row_term * kLog2e : INFINITY;
-  else if (t < 2 * QC)
-    sm.delta[t - QC] = r.row_term * scale;
+  // row terms: -LSE / scale into the Q row (-inf for rows past the end and
+  // rows no key sees, so P = 0 there), -Delta into the dO row, each as a
+  // (hi, lo) pair of bf16
+  if (t < 2 * QC) {
+    const bool is_q = t < QC;
+    const int row = (int)t % QC;
+    float x;
+    if (is_q) {
+      const bool live = q0 + row < Sq && r.row_term < INFINITY;
+      x = live ? -r.row_term / scale : -INFINITY;
+    } else {
+      x = -r.row_term;
+    }
+    const bf16 hi = (bf16)x;
+    const bf16 lo = (bf16)(x == -INFINITY ? 0.f : x - (float)hi);
+    bf16* dst = (is_q ? sm.q : sm.dout) + row * QST + D;
+    dst[0] = hi;
+    dst[1] = lo;
+  }
+}
+
+// Columns D .. D+15 of every staged Q and dO row start as zero (the row-term
+// pair is written into the first two for each chunk).
+template <int D, typename Smem>
+__device__ __forceinline__ void zero_row_terms(Smem& sm, unsigned t) {
+  constexpr int QST = Smem::QST;
+  if (t < 2 * QC) {
+    bf16* dst = (t < QC ? sm.q : sm.dout) + (int)(t % QC) * QST + D;
+    *reinterpret_cast<bf16x8*>(dst) = zero_bf16x8();
+    *reinterpret_cast<bf16x8*>(dst + 8) = zero_bf16x8();
+  }
 }
 
 template <int D>
@@ -182,6 +211,7 @@ void attn_bwd_kernel(const BwdArgs a) {
   const uint32_t n_items = min(a.counters[kCtrBwdItems], max_items);
   const int Sq = a.Sq, Sk = a.Sk;
 
+  zero_row_terms<D>(sm, t);   // made visible by the first barrier below
   for (;;) {
     if (t == 0) sm.item = atomicAdd(&a.counters[kCtrBwdNext], 1u);
     __syncthreads();
@@ -284,14 +314,12 @@ void attn_bwd_kernel(const BwdArgs a) {
           }
           bf16x8 pb[2][2], dsb[2][2];
           float pf[2][16];                 // P in fp32 between its step and dS's
-          float4 lrow[4], drow[4];         // LSE*log2(e) and Delta of the lane's rows
-          auto read_rows = [&](int ib) __attribute__((always_inline)) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              lrow[r] = *reinterpret_cast<const float4*>(&sm.lse2[32 * ib + 8 * r + 4 * hh]);
-              drow[r] = *reinterpret_cast<const float4*>(&sm.delta[32 * ib + 8 * r + 4 * hh]);
-            }
-          };
+          // B operand of the row-term k-step: ones in columns D, D+1
+          bf16x8 ones = zero_bf16x8();
+          if (hh == 0) {
+            ones[0] = (bf16)1.0f;
+            ones[1] = (bf16)1.0f;
+          }
           auto q_op = [&](int ib, int kk) __attribute__((always_inline)) {
             return as_bf16x8(&sm.q[(32 * ib + li) * QST + 16 * kk + 8 * hh]);
           };
@@ -304,12 +332,9 @@ void attn_bwd_kernel(const BwdArgs a) {
           auto qt_op = [&](int ib, int d, int t2) __attribute__((always_inline)) {
             return as_bf16x8(&sm.qt[(32 * d + li) * QTS + 32 * ib + 16 * t2 + 8 * hh]);
           };
-          auto f4 = [](const float4& x, int q) __attribute__((always_inline)) {
-            return q == 0 ? x.x : q == 1 ? x.y : q == 2 ? x.z : x.w;
-          };
-          // P = exp2(S scale log2(e) - LSE log2(e))
+          // P = exp2(S' scale log2(e)), S' = S - LSE / scale
           auto p_of = [&](const f32x16& sv, int v) __attribute__((always_inline)) {
-            return fast_exp2(fmaf(sv[v], a.scale_log2, -f4(lrow[v >> 2], v & 3)));
+            return fast_exp2(sv[v] * a.scale_log2);
           };
           // partial tile: P = 0 where the lane's key hides the row.  Bit
           // 8r + q of `hidden` covers row 32 ib + 8 r + 4 hh + q: the union of
@@ -328,11 +353,11 @@ void attn_bwd_kernel(const BwdArgs a) {
               pf[ib][v] = __builtin_bit_cast(float, __builtin_bit_cast(int, pf[ib][v]) & keep);
             }
           };
-          // scale * dS = P (scale dP - scale Delta) into the MFMA operand (dK
-          // then needs no scaling); P packed
+          // scale * dS = scale P (dP - Delta) into the MFMA operand (dK then
+          // needs no scaling); P packed
           auto ds_of = [&](const f32x16& dpv, int ib, int v) __attribute__((always_inline)) {
             const float p = pf[ib][v];
-            const float dsv = p * fmaf(dpv[v], a.scale, -f4(drow[v >> 2], v & 3));
+            const float dsv = (p * a.scale) * dpv[v];   // dP' = dP - Delta
             pb[ib][v >> 3][v & 7] = (bf16)p;
             dsb[ib][v >> 3][v & 7] = (bf16)dsv;
           };
@@ -340,36 +365,38 @@ void attn_bwd_kernel(const BwdArgs a) {
           constexpr int EPC = 16 / ND;   // elements per MFMA in (c1), (c2)
 
           // (a): operand reads run 6 ahead of the MFMAs
+          s0 = mfma32(q_op(0, NS), ones, s0);
+          dp0 = mfma32(o_op(0, NS), ones, dp0);
 #pragma unroll
           for (int kk = 0; kk < NS; ++kk) {
             s0 = mfma32(q_op(0, kk), kf[kk], s0);
             dp0 = mfma32(o_op(0, kk), vf[kk], dp0);
           }
-          read_rows(0);
-          interleave_mfma<2 * NS, 2 * NS + 8, 6, 0, 0>();
+          interleave_mfma<2 * NS + 2, 2 * NS + 2, 6, 0, 0>();
           __builtin_amdgcn_sched_barrier(0);
           // (b1)
+          s1 = mfma32(q_op(1, NS), ones, s1);
 #pragma unroll
           for (int kk = 0; kk < NS; ++kk) {
             s1 = mfma32(q_op(1, kk), kf[kk], s1);
 #pragma unroll
             for (int e = 0; e < EPK; ++e) pf[0][EPK * kk + e] = p_of(s0, EPK * kk + e);
           }
-          interleave_mfma<NS, NS, 3, 3 * EPK, 0>();
+          interleave_mfma<NS + 1, NS + 1, 3, 3 * EPK, 0>();
           __builtin_amdgcn_sched_barrier(0);
           if (need_mask) mask_p(0);
           __builtin_amdgcn_sched_barrier(0);
           // (b2)
+          dp1 = mfma32(o_op(1, NS), ones, dp1);
 #pragma unroll
           for (int kk = 0; kk < NS; ++kk) {
             dp1 = mfma32(o_op(1, kk), vf[kk], dp1);
 #pragma unroll
             for (int e = 0; e < EPK; ++e) ds_of(dp0, 0, EPK * kk + e);
           }
-          interleave_mfma<NS, NS, 3, 4 * EPK, 0>();
+          interleave_mfma<NS + 1, NS + 1, 3, 4 * EPK, 0>();
           __builtin_amdgcn_sched_barrier(0);
           // (c1)
-          read_rows(1);
 #pragma unroll
           for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -381,7 +408,7 @@ void attn_bwd_kernel(const BwdArgs a) {
                 pf[1][v] = p_of(s1, v);
               }
             }
-          interleave_mfma<2 * ND, 2 * ND + 8, 4, 3 * EPC / 2, 0>();
+          interleave_mfma<2 * ND, 2 * ND, 4, 3 * EPC / 2, 0>();
           __builtin_amdgcn_sched_barrier(0);
           if (need_mask) mask_p(1);
           __builtin_amdgcn_sched_barrier(0);
