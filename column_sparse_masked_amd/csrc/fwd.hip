@@ -31,7 +31,9 @@ struct alignas(16) FwdSmem {
   static constexpr int VTS = BK + 8;   // V^T row stride (elements)
   bf16 k[BK * KST];                    // K tile, one key per row
   bf16 vt[D * VTS];                    // V^T tile, one head-dim column per row, keys in vt_pos order
-  int4 bnd[2][BK];                     // bounds of key blocks t (even/odd), for partial tiles only
+  // partial tiles (key blocks t even / odd): bit i of hid[.][g][j] says
+  // whether key j hides row 32 g + i of the query block
+  uint32_t hid[2][BQ / 32][BK];
   uint32_t item;
 };
 
@@ -117,6 +119,18 @@ __device__ __forceinline__ int4 load_bnd(BufRsrc bb, int k0, int Sk, int t) {
   return (k0 + t < Sk) ? make_int4(x[0], x[1], x[2], x[3]) : make_int4(INT_MIN, INT_MAX, 0, 0);
 }
 
+// Hidden-row words of one key: word g has bit i set when the key's bounds
+// hide row q0 + 32 g + i (the union of its two intervals, clipped).
+__device__ __forceinline__ void hidden_rows(const int4 bd, int q0, uint32_t (&wd)[BQ / 32]) {
+#pragma unroll
+  for (int g = 0; g < BQ / 32; ++g) {
+    const int base = q0 + 32 * g;
+    auto clip = [&](int y) { return min(max(y, base), base + 32) - base; };
+    auto rows = [](int lo, int hi) { return hi > lo ? (~0u >> (32 - hi)) & (~0u << lo) : 0u; };
+    wd[g] = rows(clip(bd.x), clip(bd.y)) | rows(clip(bd.z), clip(bd.w));
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const FwdArgs a) {
@@ -194,7 +208,12 @@ void attn_fwd_kernel(const FwdArgs a) {
         if (block_masked(e_cur, k0) && t < BK) breg = load_bnd(bbase, k0, Sk, t);
         store_k<D>(st, sm.k, t);
         store_vt<D>(st, sm.vt, t);
-        if (block_masked(e_cur, k0) && t < BK) sm.bnd[0][t] = breg;
+        if (block_masked(e_cur, k0) && t < BK) {
+          uint32_t wd[BQ / 32];
+          hidden_rows(breg, qb * BQ, wd);
+#pragma unroll
+          for (int g = 0; g < BQ / 32; ++g) sm.hid[0][g][t] = wd[g];
+        }
       }
       if (cnt > 1) load_k<D>(st, kbase, block_start(e_next), t);
       __syncthreads();
@@ -223,14 +242,20 @@ void attn_fwd_kernel(const FwdArgs a) {
             s[jb] = mfma32(as_bf16x8(&sm.k[(32 * jb + li) * KST + 16 * kk + 8 * hh]), qf[kk], s[jb]);
         }
         if (need_mask) {
-          const int4* bl = &sm.bnd[tt & 1][4 * hh];
+          // words of 4 consecutive keys for this wave's 32 rows; bit li is
+          // this lane's row
+          const uint32_t* hw = &sm.hid[tt & 1][w][4 * hh];
 #pragma unroll
           for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int4 bd = bl[32 * jb + 8 * (v >> 2) + (v & 3)];
-              const bool masked = ((bd.x <= qrow) & (qrow < bd.y)) | ((bd.z <= qrow) & (qrow < bd.w));
-              s[jb][v] = masked ? -INFINITY : s[jb][v];
+            for (int r = 0; r < 4; ++r) {
+              const uint4 h4 = *reinterpret_cast<const uint4*>(&hw[32 * jb + 8 * r]);
+              const uint32_t hq[4] = {h4.x, h4.y, h4.z, h4.w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int v = 4 * r + q;
+                s[jb][v] = (hq[q] >> li) & 1u ? -INFINITY : s[jb][v];
+              }
             }
         }
         __syncthreads();   // every wave is done with this block's K
@@ -287,8 +312,13 @@ void attn_fwd_kernel(const FwdArgs a) {
         // the barrier and keeps all 64 P values alive into the next loads
         asm volatile("" : "+v"(rs));
         l_run += rs;
-        // the other bounds buffer was last read before the first barrier of block t-1
-        if (nm_next && t < BK) sm.bnd[(tt + 1) & 1][t] = breg;
+        // the other mask buffer was last read before the first barrier of block t-1
+        if (nm_next && t < BK) {
+          uint32_t wd[BQ / 32];
+          hidden_rows(breg, qb * BQ, wd);
+#pragma unroll
+          for (int g = 0; g < BQ / 32; ++g) sm.hid[(tt + 1) & 1][g][t] = wd[g];
+        }
 
         __syncthreads();   // every wave is done with this block's V^T; K_{t+1} is in LDS
         if (has_next) {
