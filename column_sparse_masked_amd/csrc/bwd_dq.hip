@@ -94,29 +94,38 @@ __device__ __forceinline__ void dq_load(DqStage<D>& r, BufRsrc kb, BufRsrc vb, i
   }
 }
 
+// K and V row-major (A operands of S^T and dP^T)
 template <int D>
-__device__ __forceinline__ void dq_store(const DqStage<D>& r, DqSmem<D>& sm, unsigned t) {
+__device__ __forceinline__ void dq_store_rows(const DqStage<D>& r, DqSmem<D>& sm, unsigned t) {
   using S = DqStage<D>;
-  constexpr int KST = DqSmem<D>::KST, KTS = DqSmem<D>::KTS;
+  constexpr int KST = DqSmem<D>::KST;
 #pragma unroll
   for (int j = 0; j < S::NU; ++j) {
-    const bool is_k = S::tensor(t, j) == 0;
-    bf16* rm = (is_k ? sm.u.kv.k : sm.u.kv.v) + opaque(S::key(t, j) * KST + 8 * S::col(t, j));
+    bf16* rm = (S::tensor(t, j) == 0 ? sm.u.kv.k : sm.u.kv.v) + opaque(S::key(t, j) * KST + 8 * S::col(t, j));
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) *reinterpret_cast<bf16x8*>(rm + rr * KST) = r.v[j][rr];
-    if (is_k) {
-      bf16* tp = sm.kt + opaque((8 * S::col(t, j)) * KTS + kt_pos(S::key(t, j)));
-      const bf16x16 p01 = __builtin_shufflevector(r.v[j][0], r.v[j][1], 0, 8, 1, 9, 2, 10, 3, 11,
-                                                  4, 12, 5, 13, 6, 14, 7, 15);
-      const bf16x16 p23 = __builtin_shufflevector(r.v[j][2], r.v[j][3], 0, 8, 1, 9, 2, 10, 3, 11,
-                                                  4, 12, 5, 13, 6, 14, 7, 15);
+  }
+}
+
+// K transposed (A operand of dQ^T)
+template <int D>
+__device__ __forceinline__ void dq_store_kt(const DqStage<D>& r, DqSmem<D>& sm, unsigned t) {
+  using S = DqStage<D>;
+  constexpr int KTS = DqSmem<D>::KTS;
+#pragma unroll
+  for (int j = 0; j < S::NU; ++j) {
+    if (S::tensor(t, j) != 0) continue;
+    bf16* tp = sm.kt + opaque((8 * S::col(t, j)) * KTS + kt_pos(S::key(t, j)));
+    const bf16x16 p01 = __builtin_shufflevector(r.v[j][0], r.v[j][1], 0, 8, 1, 9, 2, 10, 3, 11,
+                                                4, 12, 5, 13, 6, 14, 7, 15);
+    const bf16x16 p23 = __builtin_shufflevector(r.v[j][2], r.v[j][3], 0, 8, 1, 9, 2, 10, 3, 11,
+                                                4, 12, 5, 13, 6, 14, 7, 15);
 #define FM_KT_ROW(e)                                                                      \
   *reinterpret_cast<bf16x4*>(tp + (e) * KTS) =                                            \
       __builtin_shufflevector(p01, p23, 2 * (e), 2 * (e) + 1, 16 + 2 * (e), 17 + 2 * (e))
-      FM_KT_ROW(0); FM_KT_ROW(1); FM_KT_ROW(2); FM_KT_ROW(3);
-      FM_KT_ROW(4); FM_KT_ROW(5); FM_KT_ROW(6); FM_KT_ROW(7);
+    FM_KT_ROW(0); FM_KT_ROW(1); FM_KT_ROW(2); FM_KT_ROW(3);
+    FM_KT_ROW(4); FM_KT_ROW(5); FM_KT_ROW(6); FM_KT_ROW(7);
 #undef FM_KT_ROW
-    }
   }
 }
 
@@ -207,15 +216,20 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
         uint32_t wd[BQ / 32];
         const bool m = block_masked(e_cur, k0) && t < BK;
         if (m) hidden_words(k0, wd);
-        dq_store<D>(st, sm, t);
+        dq_store_rows<D>(st, sm, t);
+        dq_store_kt<D>(st, sm, t);
         if (m)
 #pragma unroll
           for (int g = 0; g < BQ / 32; ++g) sm.hid[g][t] = wd[g];
       }
+      if (cnt > 1) dq_load<D>(st, kbase, vbase, block_start(list_entry(lst, 1)), t);
       __syncthreads();
 
-      // Per key block: next block -> registers | compute | barrier | next
-      // block -> LDS | barrier.
+      // Per key block t (K, V, hid of t and K^T of t in LDS; t+1 in registers):
+      //   S^T, dP^T, dS^T of both 32-key sub-blocks | barrier | K, V, hid of
+      //   t+1 -> LDS; dQ^T += K^T dS^T | barrier | K^T of t+1 -> LDS, t+2 ->
+      //   registers.  K, V of t+1 are read after the second barrier, K^T of
+      //   t+1 after the next first barrier.
       for (int tt = 0; tt < cnt; ++tt) {
         const int k0 = block_start(e_cur);
         const bool need_mask = block_masked(e_cur, k0);
@@ -223,8 +237,8 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
         const int e_next = has_next ? list_entry(lst, tt + 1) : e_cur;
         const int k0n = block_start(e_next);
         const bool m_next = has_next && block_masked(e_next, k0n) && t < BK;
-        if (has_next) dq_load<D>(st, kbase, vbase, k0n, t);
 
+        bf16x8 dsb[2][2];   // dS^T of sub-blocks jj, k-halves t2 (B operands of dQ^T)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const int jb = 2 * kh + jj;   // 32-key sub-block of the tile
@@ -242,42 +256,47 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
             dp = mfma32(as_bf16x8(&sm.u.kv.v[off]), of[kk], dp);
           }
           // ---- dS^T = P (dP scale - Delta scale), P = exp2(S scale log2 e - LSE log2 e) ----
-          uint4 hw[4];
           if (need_mask) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              hw[r] = *reinterpret_cast<const uint4*>(&sm.hid[qw][32 * jb + 8 * r + 4 * hh]);
+            for (int r = 0; r < 4; ++r) {
+              const uint4 h4 = *reinterpret_cast<const uint4*>(&sm.hid[qw][32 * jb + 8 * r + 4 * hh]);
+              const uint32_t hq[4] = {h4.x, h4.y, h4.z, h4.w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                s[4 * r + q] = (hq[q] >> li) & 1u ? -INFINITY : s[4 * r + q];
+            }
           }
-          bf16x8 dsb[2];
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            float p = fast_exp2(fmaf(s[v], a.scale_log2, -lse2));
-            if (need_mask) {
-              const uint4 h4 = hw[v >> 2];
-              const uint32_t wv = (v & 3) == 0 ? h4.x : (v & 3) == 1 ? h4.y : (v & 3) == 2 ? h4.z : h4.w;
-              p = (wv >> li) & 1u ? 0.f : p;
-            }
-            dsb[v >> 3][v & 7] = (bf16)(p * fmaf(dp[v], a.scale, -dls));
+            const float p = fast_exp2(fmaf(s[v], a.scale_log2, -lse2));
+            dsb[jj][v >> 3][v & 7] = (bf16)(p * fmaf(dp[v], a.scale, -dls));
           }
-          // ---- dQ^T += K^T dS^T ----
+        }
+        __syncthreads();   // every wave is done with this block's K, V and hid
+        if (has_next) {
+          uint32_t wd[BQ / 32];
+          if (m_next) hidden_words(k0n, wd);
+          dq_store_rows<D>(st, sm, t);
+          if (m_next)
+#pragma unroll
+            for (int g = 0; g < BQ / 32; ++g) sm.hid[g][t] = wd[g];
+        }
+        // ---- dQ^T += K^T dS^T ----
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int jb = 2 * kh + jj;
 #pragma unroll
           for (int d = 0; d < ND; ++d)
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2)
               acc[d] = mfma32(as_bf16x8(&sm.kt[(32 * d + li) * KTS + 32 * jb + 16 * t2 + 8 * hh]),
-                              dsb[t2], acc[d]);
+                              dsb[jj][t2], acc[d]);
         }
-
-        __syncthreads();   // every wave is done with this block's K, V, K^T, hid
+        __syncthreads();   // every wave is done with this block's K^T
         if (has_next) {
-          uint32_t wd[BQ / 32];
-          if (m_next) hidden_words(k0n, wd);
-          dq_store<D>(st, sm, t);
-          if (m_next)
-#pragma unroll
-            for (int g = 0; g < BQ / 32; ++g) sm.hid[g][t] = wd[g];
+          dq_store_kt<D>(st, sm, t);
+          if (tt + 2 < cnt) dq_load<D>(st, kbase, vbase, block_start(list_entry(lst, tt + 2)), t);
         }
-        __syncthreads();   // the next block is in LDS
         e_cur = e_next;
       }
     }
