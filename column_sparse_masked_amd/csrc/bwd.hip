@@ -2,12 +2,12 @@
 // the key-stationary half.
 //
 //   bwd_pre_kernel   Delta_i = sum_d dO_id O_id (fp32);
-//   attn_bwd_kernel  persistent, key-block stationary: each workgroup takes an
-//                    item (batch*head, key block), keeps that block's K and V
-//                    in registers (32 keys per wave) and its dK, dV
-//                    accumulators in registers, and walks the list of query
-//                    blocks that see the key block (the tiles the mask does not
-//                    skip), 64 query rows at a time:
+//   attn_bwd_kernel  persistent, key-block stationary: each workgroup (8 waves)
+//                    takes an item (batch*head, key block), keeps that block's
+//                    K and V rows and its dK, dV accumulators in registers, and
+//                    walks the list of query blocks that see the key block
+//                    (the tiles the mask does not skip), 64 query rows at a
+//                    time:
 //                        S = Q K^T, P = exp(S - LSE) (interval mask on partial
 //                        tiles only), dP = dO V^T, dS = P (dP - Delta) scale,
 //                        dV += P^T dO, dK += dS^T Q;
@@ -22,7 +22,6 @@
 // from LDS is one 16-byte load.  The next chunk is fetched into registers
 // while the current one computes.
 #include <climits>
-#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"

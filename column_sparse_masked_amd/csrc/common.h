@@ -56,24 +56,6 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 
 namespace fm {
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-
-// Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
-// lane i receives, as element e (0..3), the 16-bit value number (i % 4) of the
-// 8-byte chunk addressed by lane 4*e + i/4.  If lane 4*e + c of a group points
-// at row r_e, columns c0 + 4c of a row-major tile, lane i of the group gets
-// rows r_0..r_3 of column c0 + i: four k-values of a "column" operand.
-__device__ __forceinline__ i16x4 lds_read_tr(const bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(const_cast<bf16*>(p)));
-}
-
-__device__ __forceinline__ bf16x8 cat_bf16(i16x4 lo, i16x4 hi) {
-  i16x8 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, r);
-}
-
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
 
@@ -95,37 +77,6 @@ __device__ __forceinline__ bf16x8 buf_load16(BufRsrc r, uint32_t byte_offset) {
 __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   asm volatile("" : "+v"(x));
   return x;
-}
-
-// Register-class pins (no instruction is emitted): keep an MFMA accumulator
-// that is only ever fed back into MFMAs in the AGPR file, and a result the
-// vector ALU reads next in the VGPR file, so that the allocator does not
-// shuttle whole tiles between the two files.
-__device__ __forceinline__ void pin_agpr(f32x16& x) { asm volatile("" : "+a"(x)); }
-__device__ __forceinline__ void pin_vgpr(f32x16& x) { asm volatile("" : "+v"(x)); }
-// MFMA reads its A/B operands from either file: an operand held for a whole
-// loop (K, V rows of a key block) can live in the AGPRs.
-__device__ __forceinline__ void pin_agpr(bf16x8& x) { asm volatile("" : "+a"(x)); }
-
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedVmem = 0x010,
-              kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
-
-// Orders the current scheduling region as: LEAD LDS reads, then N_MFMA steps
-// of (one MFMA, up to VALU vector-ALU instructions, up to WRITES LDS writes,
-// one LDS read while reads remain).  Operand reads thus run LEAD MFMAs ahead
-// of the matrix core, and independent vector work fills the MFMA shadows.
-template <int N_MFMA, int N_READ, int LEAD, int VALU, int WRITES>
-__device__ __forceinline__ void interleave_mfma() {
-  static_assert(N_READ >= LEAD, "");
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LEAD, 0);
-#pragma unroll
-  for (int i = 0; i < N_MFMA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    if (VALU > 0) __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU, 0);
-    if (WRITES > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, WRITES, 0);
-    if (i + LEAD < N_READ) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-  }
 }
 
 // Entry i of a uint16 tile list, read through the scalar cache: the list of
