@@ -292,27 +292,23 @@ void attn_bwd_kernel(const BwdArgs a) {
         const int e = list_at(c / CPB);
         return min(e & kListIndex, a.nQ - 1) * BQ + (c % CPB) * QC;
       };
-      ChunkStage<D> cs;
-      int e_cur = list_at(0);
-      load_chunk<D>(cs, qbase, obase, lbase, dbase, chunk_q0(0), t);
-      store_rowmajor<D>(cs, sm, chunk_q0(0), Sq, a.scale, t);
-      store_transposed<D>(cs, sm, t);
-      if (nchunks > 1) load_chunk<D>(cs, qbase, obase, lbase, dbase, chunk_q0(1), t);
-      __syncthreads();
-
-      // Per chunk c (row-major and transposed Q, dO of chunk c in LDS; chunk
-      // c+1 in registers):
-      //   S, dP of half m; P, dS -> LDS | barrier | row-major c+1 -> LDS;
-      //   dV, dK of head-dim half m | barrier | transposed c+1 -> LDS,
-      //   chunk c+2 -> registers
-      // Row-major c+1 is read after the second barrier, transposed c+1 after
-      // the next first barrier.
-      for (int c = 0; c < nchunks; ++c) {
-        const int q0 = min(e_cur & kListIndex, a.nQ - 1) * BQ + (c % CPB) * QC;
-        const bool need_mask = (e_cur & kListPartial) || ragged_k;
+      // Per chunk c (row-major Q, dO of chunk c in LDS; chunk c in registers
+      // `cur`, chunk c+1 arriving in `nxt`):
+      //   transposed c -> LDS, chunk c+2 -> `cur`; S, dP of half m; P, dS ->
+      //   LDS | barrier | row-major c+1 -> LDS; dV, dK of head-dim half m |
+      //   barrier
+      // Each store runs alongside the products of the other copy: the
+      // transposed copy is read only by dV, dK (after the first barrier), the
+      // row-major copy only by S, dP (after the second).  Loads run about a
+      // chunk and a half ahead of their first store.
+      auto step = [&](int c, ChunkStage<D>& cur, ChunkStage<D>& nxt) __attribute__((always_inline)) {
+        const int e = list_at(c / CPB);
+        const int q0 = min(e & kListIndex, a.nQ - 1) * BQ + (c % CPB) * QC;
+        const bool need_mask = (e & kListPartial) || ragged_k;
         const bool has_next = c + 1 < nchunks;
-        int e_next = e_cur;
-        if (has_next && (c + 1) % CPB == 0) e_next = list_at((c + 1) / CPB);
+
+        store_transposed<D>(cur, sm, t);
+        if (c + 2 < nchunks) load_chunk<D>(cur, qbase, obase, lbase, dbase, chunk_q0(c + 2), t);
 
         // ---- S, dP of rows 32 m + 8 r + 4 hh + q (element 4r+q), key li ----
         f32x16 s, dp;
@@ -357,8 +353,8 @@ void attn_bwd_kernel(const BwdArgs a) {
           sm.pds[g][m][0][t2][lane] = pb[t2];
           sm.pds[g][m][1][t2][lane] = dsb[t2];
         }
-        __syncthreads();   // P, dS of both halves in LDS; row-major Q, dO of chunk c read
-        if (has_next) store_rowmajor<D>(cs, sm, chunk_q0(c + 1), Sq, a.scale, t);
+        __syncthreads();   // P, dS and transposed c in LDS; row-major c read
+        if (has_next) store_rowmajor<D>(nxt, sm, chunk_q0(c + 1), Sq, a.scale, t);
 
         // ---- dV += P^T dO, dK += dS^T Q over the chunk, head-dim half m ----
 #pragma unroll
@@ -383,12 +379,18 @@ void attn_bwd_kernel(const BwdArgs a) {
               dk[dd] = mfma32(dh[t2], as_bf16x8(&sm.qt[off]), dk[dd]);
             }
         }
-        __syncthreads();   // transposed Q, dO of chunk c and P, dS read
-        if (has_next) {
-          store_transposed<D>(cs, sm, t);
-          if (c + 2 < nchunks) load_chunk<D>(cs, qbase, obase, lbase, dbase, chunk_q0(c + 2), t);
-        }
-        e_cur = e_next;
+        __syncthreads();   // row-major c+1 in LDS; transposed c and P, dS read
+      };
+
+      ChunkStage<D> r0, r1;
+      load_chunk<D>(r0, qbase, obase, lbase, dbase, chunk_q0(0), t);
+      store_rowmajor<D>(r0, sm, chunk_q0(0), Sq, a.scale, t);
+      if (nchunks > 1) load_chunk<D>(r1, qbase, obase, lbase, dbase, chunk_q0(1), t);
+      __syncthreads();
+      // two chunks per trip, so that the register sets stay statically named
+      for (int c = 0; c < nchunks; c += 2) {
+        step(c, r0, r1);
+        if (c + 1 < nchunks) step(c + 1, r1, r0);
       }
     }
 
