@@ -76,7 +76,7 @@ struct alignas(16) BwdSmem {
   static constexpr int QTS = QC + 8;   // Q^T / dO^T row stride; rows in qt_pos order
   bf16 q[QC * QST];
   bf16 dout[QC * QST];
-  bf16 qt[D * QTS];
+  bf16 qt[D * QTS];    // head-dim row d at physical row trow(d)
   bf16 dot[D * QTS];
   // P and scale*dS of (key group g, half m) in the A-operand layout of the
   // dV / dK products: [g][m][0 = P, 1 = dS][t2][lane]
@@ -183,13 +183,17 @@ __device__ __forceinline__ void store_transposed(const ChunkStage<D>& r, Smem& s
   using C = ChunkStage<D>;
   constexpr int QTS = Smem::QTS;
   if (!C::active(t)) return;
-  bf16* tp = (C::tensor(t) == 0 ? sm.qt : sm.dot) + opaque((8 * C::col(t)) * QTS + qt_pos(C::row(t)));
+  // rows 8 c + e of the transposed tile, c = this thread's column chunk, at
+  // physical rows trow(8 c + e) = 8 c + (e + rot) mod 8
+  const int c = C::col(t);
+  const int rot = trow(8 * c) - 8 * c;
+  bf16* tp = (C::tensor(t) == 0 ? sm.qt : sm.dot) + opaque((8 * c) * QTS + qt_pos(C::row(t)));
   const bf16x16 p01 =
       __builtin_shufflevector(r.v[0], r.v[1], 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15);
   const bf16x16 p23 =
       __builtin_shufflevector(r.v[2], r.v[3], 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15);
 #define FM_T_ROW(e)                                                                       \
-  *reinterpret_cast<bf16x4*>(tp + (e) * QTS) =                                            \
+  *reinterpret_cast<bf16x4*>(tp + (((e) + rot) & 7) * QTS) =                              \
       __builtin_shufflevector(p01, p23, 2 * (e), 2 * (e) + 1, 16 + 2 * (e), 17 + 2 * (e))
   FM_T_ROW(0); FM_T_ROW(1); FM_T_ROW(2); FM_T_ROW(3);
   FM_T_ROW(4); FM_T_ROW(5); FM_T_ROW(6); FM_T_ROW(7);
@@ -374,7 +378,7 @@ void attn_bwd_kernel(const BwdArgs a) {
           for (int dd = 0; dd < NDH; ++dd)
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2) {
-              const int off = (D / 2 * m + 32 * dd + li) * QTS + 32 * hf + 16 * t2 + 8 * hh;
+              const int off = trow(D / 2 * m + 32 * dd + li) * QTS + 32 * hf + 16 * t2 + 8 * hh;
               dv[dd] = mfma32(ph[t2], as_bf16x8(&sm.dot[off]), dv[dd]);
               dk[dd] = mfma32(dh[t2], as_bf16x8(&sm.qt[off]), dk[dd]);
             }

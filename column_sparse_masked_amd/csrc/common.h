@@ -45,6 +45,15 @@ __device__ __forceinline__ int perm16(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
+// Physical row of row d of a transposed LDS tile (rows indexed by the head
+// dimension).  Staging lanes store rows 8 apart at the same column; rotating
+// the rows of every group of 8 by 2 (d/8 + d/32) spreads those stores over
+// distinct banks, while 16 consecutive rows (one MFMA operand read) still map
+// to 16 distinct rows of the same group of 16.
+__device__ __forceinline__ int trow(int d) {
+  return (d & ~7) | (((d & 7) + 2 * (d >> 3) + 2 * (d >> 5)) & 7);
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   bf16x8 z;
 #pragma unroll
