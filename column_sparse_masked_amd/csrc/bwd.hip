@@ -305,14 +305,26 @@ void attn_bwd_kernel(const BwdArgs a) {
       // transposed copy is read only by dV, dK (after the first barrier), the
       // row-major copy only by S, dP (after the second).  Loads run about a
       // chunk and a half ahead of their first store.
+      // List entries of chunks c, c+1, c+2 (ec, ec1, ec2), one new scalar
+      // load per step issued a step before its use: a scalar load's result is
+      // waited for with lgkmcnt(0), which also waits for every LDS access in
+      // flight; at the top of a step, right after a barrier, there are none.
+      auto entry = [&](int c) { return c < nchunks ? list_at(c / CPB) : 0; };
+      int ec = entry(0), ec1 = entry(1), ec2 = entry(2);
       auto step = [&](int c, ChunkStage<D>& cur, ChunkStage<D>& nxt) __attribute__((always_inline)) {
-        const int e = list_at(c / CPB);
+        asm volatile("" ::"s"(ec), "s"(ec1), "s"(ec2));
+        const int e = ec;
         const int q0 = min(e & kListIndex, a.nQ - 1) * BQ + (c % CPB) * QC;
         const bool need_mask = (e & kListPartial) || ragged_k;
         const bool has_next = c + 1 < nchunks;
+        const int q0n = min(ec1 & kListIndex, a.nQ - 1) * BQ + ((c + 1) % CPB) * QC;
+        const int q0n2 = min(ec2 & kListIndex, a.nQ - 1) * BQ + ((c + 2) % CPB) * QC;
+        ec = ec1;
+        ec1 = ec2;
+        ec2 = entry(c + 3);
 
         store_transposed<D>(cur, sm, t);
-        if (c + 2 < nchunks) load_chunk<D>(cur, qbase, obase, lbase, dbase, chunk_q0(c + 2), t);
+        if (c + 2 < nchunks) load_chunk<D>(cur, qbase, obase, lbase, dbase, q0n2, t);
 
         // ---- S, dP of rows 32 m + 8 r + 4 hh + q (element 4r+q), key li ----
         f32x16 s, dp;
@@ -358,7 +370,7 @@ void attn_bwd_kernel(const BwdArgs a) {
           sm.pds[g][m][1][t2][lane] = dsb[t2];
         }
         __syncthreads();   // P, dS and transposed c in LDS; row-major c read
-        if (has_next) store_rowmajor<D>(nxt, sm, chunk_q0(c + 1), Sq, a.scale, t);
+        if (has_next) store_rowmajor<D>(nxt, sm, q0n, Sq, a.scale, t);
 
         // ---- dV += P^T dO, dK += dS^T Q over the chunk, head-dim half m ----
 #pragma unroll
