@@ -106,7 +106,11 @@ struct ChunkStage {
   bf16x8 v[4];
   float row_term;
 
-  static __device__ __forceinline__ bool active(unsigned t) { return t < 2u * NPAIR; }
+  // (constant true when every thread has a unit, so that no branch surrounds
+  // the loads and stores)
+  static __device__ __forceinline__ bool active(unsigned t) {
+    return 2 * NPAIR == kBwdThreads || t < 2u * NPAIR;
+  }
   // 0 = Q, 1 = dO; the same in every lane of a wave (NPAIR is a multiple of 64)
   static __device__ __forceinline__ int tensor(unsigned t) {
     return __builtin_amdgcn_readfirstlane((int)(t / NPAIR));
@@ -129,10 +133,14 @@ __device__ __forceinline__ void load_chunk(ChunkStage<D>& r, BufRsrc qb, BufRsrc
   using C = ChunkStage<D>;
   // The row term first (the oldest load of the chunk).  Wave 0 carries LSE,
   // wave 1 Delta (QC is the wave size); rows past the end read 0 (buffer
-  // range check) and are fixed on store.
+  // range check) and are fixed on store.  The other waves issue the load too,
+  // through an empty range (zeros, no memory access): with the same loads in
+  // every wave and no branch around them, the compiler counts the loads in
+  // flight exactly and waits for a chunk without waiting for the next one.
   static_assert(QC == 64, "one wave per row term");
-  if (t < 2 * QC) {
-    const BufRsrc src = __builtin_amdgcn_readfirstlane((int)(t < QC)) ? lb : db;   // per wave
+  {
+    const int wv = __builtin_amdgcn_readfirstlane((int)(t / QC));
+    const BufRsrc src = wv == 0 ? lb : wv == 1 ? db : make_rsrc(nullptr, 0u);
     r.row_term = __builtin_bit_cast(
         float, __builtin_amdgcn_raw_buffer_load_b32(src, (q0 + (int)(t % QC)) * 4, 0, 0));
   }
@@ -318,13 +326,16 @@ void attn_bwd_kernel(const BwdArgs a) {
         const bool need_mask = (e & kListPartial) || ragged_k;
         const bool has_next = c + 1 < nchunks;
         const int q0n = min(ec1 & kListIndex, a.nQ - 1) * BQ + ((c + 1) % CPB) * QC;
-        const int q0n2 = min(ec2 & kListIndex, a.nQ - 1) * BQ + ((c + 2) % CPB) * QC;
+        // past the last chunk: rows at Sq, which the loads' range check
+        // turns into zeros without memory accesses
+        const int q0n2 = c + 2 < nchunks ? min(ec2 & kListIndex, a.nQ - 1) * BQ + ((c + 2) % CPB) * QC
+                                         : Sq;
         ec = ec1;
         ec1 = ec2;
         ec2 = entry(c + 3);
 
         store_transposed<D>(cur, sm, t);
-        if (c + 2 < nchunks) load_chunk<D>(cur, qbase, obase, lbase, dbase, q0n2, t);
+        load_chunk<D>(cur, qbase, obase, lbase, dbase, q0n2, t);
 
         // ---- S, dP of rows 32 m + 8 r + 4 hh + q (element 4r+q), key li ----
         f32x16 s, dp;
@@ -401,6 +412,11 @@ void attn_bwd_kernel(const BwdArgs a) {
       ChunkStage<D> r0, r1;
       load_chunk<D>(r0, qbase, obase, lbase, dbase, chunk_q0(0), t);
       store_rowmajor<D>(r0, sm, chunk_q0(0), Sq, a.scale, t);
+      // K, V are in registers by now (loaded before chunk 0, which the store
+      // waited for); an explicit wait says so to the compiler, which would
+      // otherwise wait for them, and with them for the loads of later chunks,
+      // inside every step
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       if (nchunks > 1) load_chunk<D>(r1, qbase, obase, lbase, dbase, chunk_q0(1), t);
       __syncthreads();
       // two chunks per trip, so that the register sets stay statically named

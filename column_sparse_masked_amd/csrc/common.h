@@ -26,6 +26,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// s_waitcnt operand that waits for every vector memory load of the wave and
+// for nothing else (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // D = A(32x16) * B(16x32) + C on the matrix cores.  Lane l supplies
 //   A[l%32][8*(l/32) .. +8]   and   B[8*(l/32) .. +8][l%32],
