@@ -70,18 +70,23 @@ constexpr int kBwdThreads = 512;
 // more k-step of S = Q K^T and dP = dO V^T yields S - LSE / scale and
 // dP - Delta, so P = exp2(scale log2(e) S') and dS = scale P dP' need no
 // per-row value in the lanes, whose rows differ from lane to lane.
+// The LDS of a workgroup is three separate arrays (row-major staging,
+// transposed staging, P / dS exchange) rather than one structure, so that the
+// compiler can tell apart accesses to different arrays and move the stores
+// of one past the reads of another.  BwdSmem points into them.
 template <int D>
-struct alignas(16) BwdSmem {
+struct BwdSmem {
   static constexpr int QST = D + 24;   // Q / dO row stride: D values, 16 row-term columns, pad
   static constexpr int QTS = QC + 8;   // Q^T / dO^T row stride; rows in qt_pos order
-  bf16 q[QC * QST];
-  bf16 dout[QC * QST];
-  bf16 qt[D * QTS];    // head-dim row d at physical row trow(d)
-  bf16 dot[D * QTS];
+  static constexpr int RM = QC * QST;  // elements of one row-major tile
+  static constexpr int TR = D * QTS;   // elements of one transposed tile
+  bf16* q;      // [QC * QST]
+  bf16* dout;   // [QC * QST]
+  bf16* qt;     // [D * QTS], head-dim row d at physical row trow(d)
+  bf16* dot;    // [D * QTS]
   // P and scale*dS of (key group g, half m) in the A-operand layout of the
-  // dV / dK products: [g][m][0 = P, 1 = dS][t2][lane]
-  bf16x8 pds[4][2][2][2][64];
-  uint32_t item;
+  // dV / dK products: pds[g][m][0 = P, 1 = dS][t2][lane]
+  bf16x8 (*pds)[2][2][2][64];
 };
 
 // Place of row x (0 <= x < QC) inside a Q^T / dO^T row: bits 2 and 3 of the
@@ -147,7 +152,7 @@ __device__ __forceinline__ void load_chunk(ChunkStage<D>& r, BufRsrc qb, BufRsrc
   if (C::active(t)) {
     const BufRsrc src = C::tensor(t) == 0 ? qb : ob;
     const uint32_t base =
-        opaque(((uint32_t)C::row(t) * C::CPR + C::col(t)) * 16u) + (uint32_t)q0 * (D * 2);
+        opaque(((uint32_t)C::row(t) * C::CPR + C::col(t)) * 16u, q0) + (uint32_t)q0 * (D * 2);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) r.v[rr] = buf_load16(src, base + (uint32_t)rr * (D * 2));
   }
@@ -155,12 +160,12 @@ __device__ __forceinline__ void load_chunk(ChunkStage<D>& r, BufRsrc qb, BufRsrc
 
 // Row-major Q and dO (A operands of S and dP) and the row terms.
 template <int D, typename Smem>
-__device__ __forceinline__ void store_rowmajor(const ChunkStage<D>& r, Smem& sm, int q0, int Sq,
+__device__ __forceinline__ void store_rowmajor(const ChunkStage<D>& r, const Smem& sm, int q0, int Sq,
                                                float scale, unsigned t) {
   using C = ChunkStage<D>;
   constexpr int QST = Smem::QST;
   if (C::active(t)) {
-    bf16* rm = (C::tensor(t) == 0 ? sm.q : sm.dout) + opaque(C::row(t) * QST + 8 * C::col(t));
+    bf16* rm = (C::tensor(t) == 0 ? sm.q : sm.dout) + opaque(C::row(t) * QST + 8 * C::col(t), q0);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) *reinterpret_cast<bf16x8*>(rm + rr * QST) = r.v[rr];
   }
@@ -185,33 +190,49 @@ __device__ __forceinline__ void store_rowmajor(const ChunkStage<D>& r, Smem& sm,
   }
 }
 
-// Transposed Q and dO (B operands of dK and dV).
+// Transposed Q and dO (B operands of dK and dV), one row of 4 elements at a
+// time so that the stores can be spread between other work.  The thread's
+// unit covers rows 8 c + e (e = 0..7) of the transposed tile, c = its column
+// chunk, at physical rows trow(8 c + e) = 8 c + (e + rot) mod 8.  salt: a
+// scalar that changes from chunk to chunk (keeps the lane addresses inside
+// the loop).
 template <int D, typename Smem>
-__device__ __forceinline__ void store_transposed(const ChunkStage<D>& r, Smem& sm, unsigned t) {
+struct TransposedStore {
   using C = ChunkStage<D>;
-  constexpr int QTS = Smem::QTS;
-  if (!C::active(t)) return;
-  // rows 8 c + e of the transposed tile, c = this thread's column chunk, at
-  // physical rows trow(8 c + e) = 8 c + (e + rot) mod 8
-  const int c = C::col(t);
-  const int rot = trow(8 * c) - 8 * c;
-  bf16* tp = (C::tensor(t) == 0 ? sm.qt : sm.dot) + opaque((8 * c) * QTS + qt_pos(C::row(t)));
-  const bf16x16 p01 =
-      __builtin_shufflevector(r.v[0], r.v[1], 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15);
-  const bf16x16 p23 =
-      __builtin_shufflevector(r.v[2], r.v[3], 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15);
-#define FM_T_ROW(e)                                                                       \
-  *reinterpret_cast<bf16x4*>(tp + (((e) + rot) & 7) * QTS) =                              \
-      __builtin_shufflevector(p01, p23, 2 * (e), 2 * (e) + 1, 16 + 2 * (e), 17 + 2 * (e))
-  FM_T_ROW(0); FM_T_ROW(1); FM_T_ROW(2); FM_T_ROW(3);
-  FM_T_ROW(4); FM_T_ROW(5); FM_T_ROW(6); FM_T_ROW(7);
-#undef FM_T_ROW
+  bf16* tp;
+  int rot;
+  bf16x16 p01, p23;   // rows 0,1 and 2,3 of the unit, interleaved element by element
+
+  __device__ __forceinline__ TransposedStore(const ChunkStage<D>& r, const Smem& sm, int salt, unsigned t) {
+    const int c = C::col(t);
+    rot = trow(8 * c) - 8 * c;
+    tp = (C::tensor(t) == 0 ? sm.qt : sm.dot) + opaque((8 * c) * Smem::QTS + qt_pos(C::row(t)), salt);
+    p01 = __builtin_shufflevector(r.v[0], r.v[1], 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15);
+    p23 = __builtin_shufflevector(r.v[2], r.v[3], 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15);
+  }
+  // transposed row 8 c + e (e a constant after unrolling)
+  __device__ __forceinline__ void row(int e) const {
+    bf16x4 x;
+    x[0] = p01[2 * e];
+    x[1] = p01[2 * e + 1];
+    x[2] = p23[2 * e];
+    x[3] = p23[2 * e + 1];
+    *reinterpret_cast<bf16x4*>(tp + ((e + rot) & 7) * Smem::QTS) = x;
+  }
+};
+
+template <int D, typename Smem>
+__device__ __forceinline__ void store_transposed(const ChunkStage<D>& r, const Smem& sm, int salt, unsigned t) {
+  if (!ChunkStage<D>::active(t)) return;
+  const TransposedStore<D, Smem> ts(r, sm, salt, t);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ts.row(e);
 }
 
 // Columns D .. D+15 of every staged Q and dO row start as zero (the row-term
 // pair is written into the first two for each chunk).
 template <int D, typename Smem>
-__device__ __forceinline__ void zero_row_terms(Smem& sm, unsigned t) {
+__device__ __forceinline__ void zero_row_terms(const Smem& sm, unsigned t) {
   constexpr int QST = Smem::QST;
   if (t < 2 * QC) {
     bf16* dst = (t < QC ? sm.q : sm.dout) + (int)(t % QC) * QST + D;
@@ -227,7 +248,11 @@ void attn_bwd_kernel(const BwdArgs a) {
   constexpr int NDH = D / 64;       // 32-wide head-dim blocks per half of D
   using Smem = BwdSmem<D>;
   constexpr int QST = Smem::QST, QTS = Smem::QTS;
-  __shared__ Smem sm;
+  __shared__ __attribute__((aligned(16))) bf16 lds_rm[2 * Smem::RM];
+  __shared__ __attribute__((aligned(16))) bf16 lds_t[2 * Smem::TR];
+  __shared__ bf16x8 lds_pds[4][2][2][2][64];
+  __shared__ uint32_t lds_item;
+  const Smem sm{lds_rm, lds_rm + Smem::RM, lds_t, lds_t + Smem::TR, lds_pds};
 
   const unsigned t = threadIdx.x;
   const int lane = (int)(t & 63), w = (int)(t >> 6);
@@ -239,9 +264,9 @@ void attn_bwd_kernel(const BwdArgs a) {
 
   zero_row_terms<D>(sm, t);   // made visible by the first barrier below
   for (;;) {
-    if (t == 0) sm.item = atomicAdd(&a.counters[kCtrBwdNext], 1u);
+    if (t == 0) lds_item = atomicAdd(&a.counters[kCtrBwdNext], 1u);
     __syncthreads();
-    const uint32_t idx = __builtin_amdgcn_readfirstlane(sm.item);
+    const uint32_t idx = __builtin_amdgcn_readfirstlane(lds_item);
     if (idx >= n_items) break;
     // values loaded from memory are not known to be uniform: broadcast them,
     // so that the buffer resources built from them stay in scalar registers
@@ -334,24 +359,55 @@ void attn_bwd_kernel(const BwdArgs a) {
         ec1 = ec2;
         ec2 = entry(c + 3);
 
-        store_transposed<D>(cur, sm, t);
-        load_chunk<D>(cur, qbase, obase, lbase, dbase, q0n2, t);
-
-        // ---- S, dP of rows 32 m + 8 r + 4 hh + q (element 4r+q), key li ----
+        // ---- S, dP of rows 32 m + 8 r + 4 hh + q (element 4r+q), key li;
+        // the row-term k-step first ----
         f32x16 s, dp;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           s[v] = 0.f;
           dp[v] = 0.f;
         }
-        {
-          const int rbase = (32 * m + li) * QST + 8 * hh;
-          s = mfma32(as_bf16x8(&sm.q[rbase + 16 * NS]), ones, s);
-          dp = mfma32(as_bf16x8(&sm.dout[rbase + 16 * NS]), ones, dp);
+        const bf16* qrow = sm.q + (32 * m + li) * QST + 8 * hh;
+        const bf16* drow = sm.dout + (32 * m + li) * QST + 8 * hh;
+        if constexpr (D == 128) {
+          // Hand-scheduled: between the product pairs go the transposed
+          // stores of chunk c (two rows per pair), then the loads of chunk
+          // c+2 into the registers those stores have read; operands are read
+          // two k-steps ahead.  The fences keep the compiler from gathering
+          // the stores in front of the products.
+          const TransposedStore<D, Smem> ts(cur, sm, q0, t);
+          bf16x8 qa[NS + 1], da[NS + 1];   // operand of k-step i: row term (i = 0), then i - 1
+          auto read_ops = [&](int i) __attribute__((always_inline)) {
+            const int kk = i == 0 ? NS : i - 1;
+            qa[i] = as_bf16x8(qrow + 16 * kk);
+            da[i] = as_bf16x8(drow + 16 * kk);
+          };
+          read_ops(0);
+          read_ops(1);
+          ts.row(0);
+          ts.row(1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i <= NS; ++i) {
+            s = mfma32(qa[i], i == 0 ? ones : kf[i - 1], s);
+            dp = mfma32(da[i], i == 0 ? ones : vf[i - 1], dp);
+            if (i + 2 <= NS) read_ops(i + 2);
+            if (i < 3) {
+              ts.row(2 * i + 2);
+              ts.row(2 * i + 3);
+            }
+            if (i == 3) load_chunk<D>(cur, qbase, obase, lbase, dbase, q0n2, t);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          store_transposed<D>(cur, sm, q0, t);
+          load_chunk<D>(cur, qbase, obase, lbase, dbase, q0n2, t);
+          s = mfma32(as_bf16x8(qrow + 16 * NS), ones, s);
+          dp = mfma32(as_bf16x8(drow + 16 * NS), ones, dp);
 #pragma unroll
           for (int kk = 0; kk < NS; ++kk) {
-            s = mfma32(as_bf16x8(&sm.q[rbase + 16 * kk]), kf[kk], s);
-            dp = mfma32(as_bf16x8(&sm.dout[rbase + 16 * kk]), vf[kk], dp);
+            s = mfma32(as_bf16x8(qrow + 16 * kk), kf[kk], s);
+            dp = mfma32(as_bf16x8(drow + 16 * kk), vf[kk], dp);
           }
         }
         if (need_mask) {
@@ -381,30 +437,65 @@ void attn_bwd_kernel(const BwdArgs a) {
           sm.pds[g][m][1][t2][lane] = dsb[t2];
         }
         __syncthreads();   // P, dS and transposed c in LDS; row-major c read
-        if (has_next) store_rowmajor<D>(nxt, sm, q0n, Sq, a.scale, t);
 
-        // ---- dV += P^T dO, dK += dS^T Q over the chunk, head-dim half m ----
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+        // ---- dV += P^T dO, dK += dS^T Q over the chunk, head-dim half m:
+        // this wave's own rows first (P, dS in registers), then the
+        // partner's (from LDS) ----
+        // B operand of (rows of half hf, head-dim block dd, k-half t2)
+        auto boff = [&](int hf, int dd, int t2) __attribute__((always_inline)) {
+          return trow(D / 2 * m + 32 * dd + li) * QTS + 32 * hf + 16 * t2 + 8 * hh;
+        };
+        const int mo = 1 - m;   // the partner's half
+        if constexpr (D == 128) {
+          // Hand-scheduled like S, dP: the row-major stores of chunk c+1
+          // between the product pairs, B operands read two pairs ahead.
+          // (Past the last chunk the stores write unused rows: harmless.)
+          constexpr int NP = 2 * NDH * 2;   // product pairs: (half, dd, t2)
+          bf16x8 bo[NP][2];                 // dO^T, Q^T operands of pair i
+          auto read_b = [&](int i) __attribute__((always_inline)) {
+            const int off = boff(i < NP / 2 ? m : mo, (i >> 1) % NDH, i & 1);
+            bo[i][0] = as_bf16x8(&sm.dot[off]);
+            bo[i][1] = as_bf16x8(&sm.qt[off]);
+          };
           bf16x8 ph[2], dh[2];
+          read_b(0);
+          read_b(1);
 #pragma unroll
           for (int t2 = 0; t2 < 2; ++t2) {
-            if (hf == m) {
-              ph[t2] = pb[t2];
-              dh[t2] = dsb[t2];
-            } else {
-              ph[t2] = sm.pds[g][hf][0][t2][lane];
-              dh[t2] = sm.pds[g][hf][1][t2][lane];
-            }
+            ph[t2] = sm.pds[g][mo][0][t2][lane];
+            dh[t2] = sm.pds[g][mo][1][t2][lane];
           }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int dd = 0; dd < NDH; ++dd)
+          for (int i = 0; i < NP; ++i) {
+            const int dd = (i >> 1) % NDH, t2 = i & 1;
+            const bool own = i < NP / 2;
+            dv[dd] = mfma32(own ? pb[t2] : ph[t2], bo[i][0], dv[dd]);
+            dk[dd] = mfma32(own ? dsb[t2] : dh[t2], bo[i][1], dk[dd]);
+            if (i + 2 < NP) read_b(i + 2);
+            if (i == 0) store_rowmajor<D>(nxt, sm, q0n, Sq, a.scale, t);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          if (has_next) store_rowmajor<D>(nxt, sm, q0n, Sq, a.scale, t);
+#pragma unroll
+          for (int o = 0; o < 2; ++o) {
+            const int hf = o == 0 ? m : mo;
+            bf16x8 ph[2], dh[2];
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2) {
-              const int off = trow(D / 2 * m + 32 * dd + li) * QTS + 32 * hf + 16 * t2 + 8 * hh;
-              dv[dd] = mfma32(ph[t2], as_bf16x8(&sm.dot[off]), dv[dd]);
-              dk[dd] = mfma32(dh[t2], as_bf16x8(&sm.qt[off]), dk[dd]);
+              ph[t2] = o == 0 ? pb[t2] : sm.pds[g][mo][0][t2][lane];
+              dh[t2] = o == 0 ? dsb[t2] : sm.pds[g][mo][1][t2][lane];
             }
+#pragma unroll
+            for (int dd = 0; dd < NDH; ++dd)
+#pragma unroll
+              for (int t2 = 0; t2 < 2; ++t2) {
+                const int off = boff(hf, dd, t2);
+                dv[dd] = mfma32(ph[t2], as_bf16x8(&sm.dot[off]), dv[dd]);
+                dk[dd] = mfma32(dh[t2], as_bf16x8(&sm.qt[off]), dk[dd]);
+              }
+          }
         }
         __syncthreads();   // row-major c+1 in LDS; transposed c and P, dS read
       };
@@ -444,7 +535,7 @@ void attn_bwd_kernel(const BwdArgs a) {
           }
         }
     }
-    __syncthreads();   // every thread has read sm.item and finished with LDS
+    __syncthreads();   // every thread has read lds_item and finished with LDS
   }
   if (t == 0) {
     __threadfence();

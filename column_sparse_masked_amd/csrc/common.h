@@ -90,6 +90,14 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+// The same inside a loop, tied to `salt`, a scalar that changes from one trip
+// to the next (which is what keeps the value from being hoisted).  This asm
+// has no side effects, so unlike the one above it does not stop the
+// scheduler from moving memory accesses past it.
+__device__ __forceinline__ uint32_t opaque(uint32_t x, int salt) {
+  asm("" : "+v"(x) : "s"(salt));
+  return x;
+}
 
 // Entry i of a uint16 tile list, read through the scalar cache: the list of
 // a work item is the same for the whole workgroup, so the aligned 32-bit word
