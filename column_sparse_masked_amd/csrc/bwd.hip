@@ -61,6 +61,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
 // taking the other half's P and dS from its partner through LDS.  Per wave
 // that is 64 accumulator registers for dK/dV (instead of 128), which leaves
 // room for two waves per SIMD.
+// Step c has two phases split by barriers:
+//   1. S, dP of chunk c; P, dS (to LDS for the partner); dV, dK over this
+//      wave's own half of the chunk's rows (P, dS still in registers);
+//   2. dV, dK over the partner's half (P, dS from LDS); the transposed and
+//      row-major copies of chunk c+1 stored from registers; chunk c+3 loaded.
+// The transposed copy is double-buffered so that phase 1 can read chunk c's
+// while phase 2 writes chunk c+1's.  Of the two waves on a SIMD the older
+// one reaches its exponentials first; the other's products then keep the
+// matrix cores busy, and in turn the older wave's own-half products run
+// while the other computes its exponentials.
 constexpr int kBwdThreads = 512;
 
 // Row terms ride in the matrix products.  Each staged Q row carries, in the
@@ -80,13 +90,15 @@ struct BwdSmem {
   static constexpr int QTS = QC + 8;   // Q^T / dO^T row stride; rows in qt_pos order
   static constexpr int RM = QC * QST;  // elements of one row-major tile
   static constexpr int TR = D * QTS;   // elements of one transposed tile
+  static_assert(stage_strides_ok(2 * QST, 2 * QTS), "strides the staging map needs");
   bf16* q;      // [QC * QST]
   bf16* dout;   // [QC * QST]
-  bf16* qt;     // [D * QTS], head-dim row d at physical row trow(d)
-  bf16* dot;    // [D * QTS]
+  bf16* tr;     // [2 buffers][Q^T, dO^T][D * QTS], one row per head-dim column
   // P and scale*dS of (key group g, half m) in the A-operand layout of the
   // dV / dK products: pds[g][m][0 = P, 1 = dS][t2][lane]
   bf16x8 (*pds)[2][2][2][64];
+  __device__ __forceinline__ bf16* qt(int buf) const { return tr + (2 * buf) * TR; }
+  __device__ __forceinline__ bf16* dot(int buf) const { return tr + (2 * buf + 1) * TR; }
 };
 
 // Place of row x (0 <= x < QC) inside a Q^T / dO^T row: bits 2 and 3 of the
@@ -96,18 +108,16 @@ __device__ __forceinline__ int qt_pos(int x) { return (x & ~15) | perm16(x & 15)
 
 // Global -> register staging of one chunk of QC query rows of Q and dO
 // (512 threads).  A unit is 4 consecutive rows (4m .. 4m+3) x 8 head-dim
-// columns (chunk c) of one of the two tensors.  Each group of 16 lanes takes 4
-// consecutive m by 4 consecutive c: with the row stride of 16 bytes past a
-// multiple of 256, the 16 row-major 16-byte stores of a group then cover all
-// LDS banks once.  A wave's 4 groups cover 16 chunks of 4 rows (whole 256-byte
-// rows for D = 128) so that the global loads stay row-contiguous.  Threads
-// < 2*QC also carry the LSE (first QC) or Delta (next QC) of one row.
+// columns (chunk c) of one of the two tensors, assigned by the staging map
+// (stage_row_unit, stage_chunk) that keeps both the row-major and the
+// transposed LDS stores free of bank conflicts.  Threads < 2*QC also carry
+// the LSE (first QC) or Delta (next QC) of one row.
 template <int D>
 struct ChunkStage {
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int NPAIR = (QC / 4) * CPR;   // units per tensor (a multiple of 64)
   static_assert(NPAIR % 64 == 0 && 2 * NPAIR <= kBwdThreads, "one unit per thread");
-  static_assert(CPR % 4 == 0 && QC % 16 == 0, "groups are 4 row-units x 4 chunks");
+  static_assert(CPR % 4 == 0 && QC == 64, "a wave's units are the 16 row-units x 4 chunks");
   bf16x8 v[4];
   float row_term;
 
@@ -120,15 +130,13 @@ struct ChunkStage {
   static __device__ __forceinline__ int tensor(unsigned t) {
     return __builtin_amdgcn_readfirstlane((int)(t / NPAIR));
   }
-  // unit p = (group G, lane-in-group l): chunk c = 4 (G % (CPR/4)) + l / 4,
-  // row-unit m = 4 (G / (CPR/4)) + l % 4
+  // unit p of the tensor: lane p % 64 of chunk quad p / 64
   static __device__ __forceinline__ int row(unsigned t) {
-    const unsigned p = t % NPAIR;
-    return 4 * (int)(4u * ((p >> 4) / (CPR / 4)) + (p & 3u));
+    return 4 * stage_row_unit((int)(t % NPAIR) & 63);
   }
   static __device__ __forceinline__ int col(unsigned t) {
-    const unsigned p = t % NPAIR;
-    return (int)(4u * ((p >> 4) % (CPR / 4)) + ((p >> 2) & 3u));
+    const int p = (int)(t % NPAIR);
+    return stage_chunk(p & 63, p >> 6);
   }
 };
 
@@ -190,23 +198,21 @@ __device__ __forceinline__ void store_rowmajor(const ChunkStage<D>& r, const Sme
   }
 }
 
-// Transposed Q and dO (B operands of dK and dV), one row of 4 elements at a
-// time so that the stores can be spread between other work.  The thread's
-// unit covers rows 8 c + e (e = 0..7) of the transposed tile, c = its column
-// chunk, at physical rows trow(8 c + e) = 8 c + (e + rot) mod 8.  salt: a
-// scalar that changes from chunk to chunk (keeps the lane addresses inside
-// the loop).
+// Transposed Q and dO (B operands of dK and dV) into buffer `buf`, one row of
+// 4 elements at a time so that the stores can be spread between other work.
+// The thread's unit covers rows 8 c + e (e = 0..7) of the transposed tile, c
+// its column chunk.  salt: a scalar that changes from chunk to chunk (keeps
+// the lane addresses inside the loop).
 template <int D, typename Smem>
 struct TransposedStore {
   using C = ChunkStage<D>;
   bf16* tp;
-  int rot;
   bf16x16 p01, p23;   // rows 0,1 and 2,3 of the unit, interleaved element by element
 
-  __device__ __forceinline__ TransposedStore(const ChunkStage<D>& r, const Smem& sm, int salt, unsigned t) {
+  __device__ __forceinline__ TransposedStore(const ChunkStage<D>& r, const Smem& sm, int buf, int salt,
+                                             unsigned t) {
     const int c = C::col(t);
-    rot = trow(8 * c) - 8 * c;
-    tp = (C::tensor(t) == 0 ? sm.qt : sm.dot) + opaque((8 * c) * Smem::QTS + qt_pos(C::row(t)), salt);
+    tp = (C::tensor(t) == 0 ? sm.qt(buf) : sm.dot(buf)) + opaque((8 * c) * Smem::QTS + qt_pos(C::row(t)), salt);
     p01 = __builtin_shufflevector(r.v[0], r.v[1], 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15);
     p23 = __builtin_shufflevector(r.v[2], r.v[3], 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15);
   }
@@ -217,14 +223,15 @@ struct TransposedStore {
     x[1] = p01[2 * e + 1];
     x[2] = p23[2 * e];
     x[3] = p23[2 * e + 1];
-    *reinterpret_cast<bf16x4*>(tp + ((e + rot) & 7) * Smem::QTS) = x;
+    *reinterpret_cast<bf16x4*>(tp + e * Smem::QTS) = x;
   }
 };
 
 template <int D, typename Smem>
-__device__ __forceinline__ void store_transposed(const ChunkStage<D>& r, const Smem& sm, int salt, unsigned t) {
+__device__ __forceinline__ void store_transposed(const ChunkStage<D>& r, const Smem& sm, int buf, int salt,
+                                                 unsigned t) {
   if (!ChunkStage<D>::active(t)) return;
-  const TransposedStore<D, Smem> ts(r, sm, salt, t);
+  const TransposedStore<D, Smem> ts(r, sm, buf, salt, t);
 #pragma unroll
   for (int e = 0; e < 8; ++e) ts.row(e);
 }
@@ -249,10 +256,14 @@ void attn_bwd_kernel(const BwdArgs a) {
   using Smem = BwdSmem<D>;
   constexpr int QST = Smem::QST, QTS = Smem::QTS;
   __shared__ __attribute__((aligned(16))) bf16 lds_rm[2 * Smem::RM];
-  __shared__ __attribute__((aligned(16))) bf16 lds_t[2 * Smem::TR];
+  __shared__ __attribute__((aligned(16))) bf16 lds_t[4 * Smem::TR];
   __shared__ bf16x8 lds_pds[4][2][2][2][64];
   __shared__ uint32_t lds_item;
-  const Smem sm{lds_rm, lds_rm + Smem::RM, lds_t, lds_t + Smem::TR, lds_pds};
+  Smem sm;
+  sm.q = lds_rm;
+  sm.dout = lds_rm + Smem::RM;
+  sm.tr = lds_t;
+  sm.pds = lds_pds;
 
   const unsigned t = threadIdx.x;
   const int lane = (int)(t & 63), w = (int)(t >> 6);
@@ -324,43 +335,48 @@ void attn_bwd_kernel(const BwdArgs a) {
 
     const int nchunks = CPB * cnt;   // each query block is CPB chunks of QC rows
     if (nchunks > 0) {
-      // chunk c starts at row block_row(c) * BQ + (c % CPB) * QC
-      auto chunk_q0 = [&](int c) __attribute__((always_inline)) {
-        const int e = list_at(c / CPB);
+      // List word of chunk c (c clamped to the last chunk: entries past the
+      // end are loaded but not used) and the first row of chunk c.
+      auto lword = [&](int c) __attribute__((always_inline)) {
+        const int j = min(c, nchunks - 1) / CPB + rot;
+        return list_word(lst, j < cnt ? j : j - cnt);
+      };
+      auto row0 = [&](int e, int c) __attribute__((always_inline)) {
         return min(e & kListIndex, a.nQ - 1) * BQ + (c % CPB) * QC;
       };
-      // Per chunk c (row-major Q, dO of chunk c in LDS; chunk c in registers
-      // `cur`, chunk c+1 arriving in `nxt`):
-      //   transposed c -> LDS, chunk c+2 -> `cur`; S, dP of half m; P, dS ->
-      //   LDS | barrier | row-major c+1 -> LDS; dV, dK of head-dim half m |
-      //   barrier
-      // Each store runs alongside the products of the other copy: the
-      // transposed copy is read only by dV, dK (after the first barrier), the
-      // row-major copy only by S, dP (after the second).  Loads run about a
-      // chunk and a half ahead of their first store.
-      // List entries of chunks c, c+1, c+2 (ec, ec1, ec2), one new scalar
-      // load per step issued a step before its use: a scalar load's result is
-      // waited for with lgkmcnt(0), which also waits for every LDS access in
-      // flight; at the top of a step, right after a barrier, there are none.
-      auto entry = [&](int c) { return c < nchunks ? list_at(c / CPB) : 0; };
-      int ec = entry(0), ec1 = entry(1), ec2 = entry(2);
-      auto step = [&](int c, ChunkStage<D>& cur, ChunkStage<D>& nxt) __attribute__((always_inline)) {
-        asm volatile("" ::"s"(ec), "s"(ec1), "s"(ec2));
-        const int e = ec;
-        const int q0 = min(e & kListIndex, a.nQ - 1) * BQ + (c % CPB) * QC;
-        const bool need_mask = (e & kListPartial) || ragged_k;
-        const bool has_next = c + 1 < nchunks;
-        const int q0n = min(ec1 & kListIndex, a.nQ - 1) * BQ + ((c + 1) % CPB) * QC;
+      // List words of chunks c .. c+3 at the top of step c.  Step c loads the
+      // word of chunk c+4 at its end: a scalar load's result is waited for
+      // with lgkmcnt(0), which also waits for every LDS access in flight, and
+      // the barrier that ends the step waits for all of them anyway.
+      ListWord lw0 = lword(0), lw1 = lword(1), lw2 = lword(2), lw3 = lword(3);
+      const int bq0 = row0(list_value(lw0), 0);
+
+      // B operand of the dV (tensor 0) / dK (tensor 1) product of rows of
+      // half hf, head-dim block dd, k-half t2, from transposed buffer buf
+      auto boff = [&](int hf, int dd, int t2) __attribute__((always_inline)) {
+        return (D / 2 * m + 32 * dd + li) * QTS + 32 * hf + 16 * t2 + 8 * hh;
+      };
+      const int mo = 1 - m;   // the partner's half
+
+      // X: registers holding chunk c+1 (loaded two steps earlier)
+      auto step = [&](int c, ChunkStage<D>& X) __attribute__((always_inline)) {
+        asm volatile("" ::"s"(lw0.word), "s"(lw1.word), "s"(lw2.word), "s"(lw3.word));
+        const int e0 = list_value(lw0);
+        const int q0 = row0(e0, c);
+        const bool need_mask = (e0 & kListPartial) || ragged_k;
+        const int q0n = row0(list_value(lw1), c + 1);
         // past the last chunk: rows at Sq, which the loads' range check
         // turns into zeros without memory accesses
-        const int q0n2 = c + 2 < nchunks ? min(ec2 & kListIndex, a.nQ - 1) * BQ + ((c + 2) % CPB) * QC
-                                         : Sq;
-        ec = ec1;
-        ec1 = ec2;
-        ec2 = entry(c + 3);
+        const int q0l = c + 3 < nchunks ? row0(list_value(lw3), c + 3) : Sq;
+        lw0 = lw1;
+        lw1 = lw2;
+        lw2 = lw3;
+        const int bc = c & 1, bn = bc ^ 1;   // transposed buffers of chunks c and c+1
+        const bf16* qtc = sm.qt(bc);
+        const bf16* dotc = sm.dot(bc);
 
-        // ---- S, dP of rows 32 m + 8 r + 4 hh + q (element 4r+q), key li;
-        // the row-term k-step first ----
+        // ---- phase 1: S, dP of rows 32 m + 8 r + 4 hh + q (element 4r+q),
+        // key li, the row-term k-step first ----
         f32x16 s, dp;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -370,12 +386,7 @@ void attn_bwd_kernel(const BwdArgs a) {
         const bf16* qrow = sm.q + (32 * m + li) * QST + 8 * hh;
         const bf16* drow = sm.dout + (32 * m + li) * QST + 8 * hh;
         if constexpr (D == 128) {
-          // Hand-scheduled: between the product pairs go the transposed
-          // stores of chunk c (two rows per pair), then the loads of chunk
-          // c+2 into the registers those stores have read; operands are read
-          // two k-steps ahead.  The fences keep the compiler from gathering
-          // the stores in front of the products.
-          const TransposedStore<D, Smem> ts(cur, sm, q0, t);
+          // operands read two k-steps ahead; the fences keep that order
           bf16x8 qa[NS + 1], da[NS + 1];   // operand of k-step i: row term (i = 0), then i - 1
           auto read_ops = [&](int i) __attribute__((always_inline)) {
             const int kk = i == 0 ? NS : i - 1;
@@ -384,24 +395,15 @@ void attn_bwd_kernel(const BwdArgs a) {
           };
           read_ops(0);
           read_ops(1);
-          ts.row(0);
-          ts.row(1);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int i = 0; i <= NS; ++i) {
             s = mfma32(qa[i], i == 0 ? ones : kf[i - 1], s);
             dp = mfma32(da[i], i == 0 ? ones : vf[i - 1], dp);
             if (i + 2 <= NS) read_ops(i + 2);
-            if (i < 3) {
-              ts.row(2 * i + 2);
-              ts.row(2 * i + 3);
-            }
-            if (i == 3) load_chunk<D>(cur, qbase, obase, lbase, dbase, q0n2, t);
             __builtin_amdgcn_sched_barrier(0);
           }
         } else {
-          store_transposed<D>(cur, sm, q0, t);
-          load_chunk<D>(cur, qbase, obase, lbase, dbase, q0n2, t);
           s = mfma32(as_bf16x8(qrow + 16 * NS), ones, s);
           dp = mfma32(as_bf16x8(drow + 16 * NS), ones, dp);
 #pragma unroll
@@ -436,84 +438,107 @@ void attn_bwd_kernel(const BwdArgs a) {
           sm.pds[g][m][0][t2][lane] = pb[t2];
           sm.pds[g][m][1][t2][lane] = dsb[t2];
         }
-        __syncthreads();   // P, dS and transposed c in LDS; row-major c read
-
-        // ---- dV += P^T dO, dK += dS^T Q over the chunk, head-dim half m:
-        // this wave's own rows first (P, dS in registers), then the
-        // partner's (from LDS) ----
-        // B operand of (rows of half hf, head-dim block dd, k-half t2)
-        auto boff = [&](int hf, int dd, int t2) __attribute__((always_inline)) {
-          return trow(D / 2 * m + 32 * dd + li) * QTS + 32 * hf + 16 * t2 + 8 * hh;
-        };
-        const int mo = 1 - m;   // the partner's half
+        // ---- dV += P^T dO, dK += dS^T Q, head-dim half m, own rows ----
+        constexpr int NP = NDH * 2;   // product pairs per half: (dd, t2)
         if constexpr (D == 128) {
-          // Hand-scheduled like S, dP: the row-major stores of chunk c+1
-          // between the product pairs, B operands read two pairs ahead.
-          // (Past the last chunk the stores write unused rows: harmless.)
-          constexpr int NP = 2 * NDH * 2;   // product pairs: (half, dd, t2)
-          bf16x8 bo[NP][2];                 // dO^T, Q^T operands of pair i
+          bf16x8 bo[NP][2];
           auto read_b = [&](int i) __attribute__((always_inline)) {
-            const int off = boff(i < NP / 2 ? m : mo, (i >> 1) % NDH, i & 1);
-            bo[i][0] = as_bf16x8(&sm.dot[off]);
-            bo[i][1] = as_bf16x8(&sm.qt[off]);
+            const int off = boff(m, i >> 1, i & 1);
+            bo[i][0] = as_bf16x8(dotc + off);
+            bo[i][1] = as_bf16x8(qtc + off);
           };
-          bf16x8 ph[2], dh[2];
           read_b(0);
           read_b(1);
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2) {
-            ph[t2] = sm.pds[g][mo][0][t2][lane];
-            dh[t2] = sm.pds[g][mo][1][t2][lane];
-          }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int i = 0; i < NP; ++i) {
-            const int dd = (i >> 1) % NDH, t2 = i & 1;
-            const bool own = i < NP / 2;
-            dv[dd] = mfma32(own ? pb[t2] : ph[t2], bo[i][0], dv[dd]);
-            dk[dd] = mfma32(own ? dsb[t2] : dh[t2], bo[i][1], dk[dd]);
+            dv[i >> 1] = mfma32(pb[i & 1], bo[i][0], dv[i >> 1]);
+            dk[i >> 1] = mfma32(dsb[i & 1], bo[i][1], dk[i >> 1]);
             if (i + 2 < NP) read_b(i + 2);
-            if (i == 0) store_rowmajor<D>(nxt, sm, q0n, Sq, a.scale, t);
             __builtin_amdgcn_sched_barrier(0);
           }
         } else {
-          if (has_next) store_rowmajor<D>(nxt, sm, q0n, Sq, a.scale, t);
 #pragma unroll
-          for (int o = 0; o < 2; ++o) {
-            const int hf = o == 0 ? m : mo;
-            bf16x8 ph[2], dh[2];
+          for (int dd = 0; dd < NDH; ++dd)
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2) {
-              ph[t2] = o == 0 ? pb[t2] : sm.pds[g][mo][0][t2][lane];
-              dh[t2] = o == 0 ? dsb[t2] : sm.pds[g][mo][1][t2][lane];
+              const int off = boff(m, dd, t2);
+              dv[dd] = mfma32(pb[t2], as_bf16x8(dotc + off), dv[dd]);
+              dk[dd] = mfma32(dsb[t2], as_bf16x8(qtc + off), dk[dd]);
             }
-#pragma unroll
-            for (int dd = 0; dd < NDH; ++dd)
-#pragma unroll
-              for (int t2 = 0; t2 < 2; ++t2) {
-                const int off = boff(hf, dd, t2);
-                dv[dd] = mfma32(ph[t2], as_bf16x8(&sm.dot[off]), dv[dd]);
-                dk[dd] = mfma32(dh[t2], as_bf16x8(&sm.qt[off]), dk[dd]);
-              }
-          }
         }
-        __syncthreads();   // row-major c+1 in LDS; transposed c and P, dS read
+        __syncthreads();   // P, dS in LDS; row-major c read
+
+        // ---- phase 2: dV, dK over the partner's rows; chunk c+1 staged
+        // (past the last chunk the stores write unused rows: harmless);
+        // chunk c+3 loaded into the registers the stores have read ----
+        bf16x8 ph[2], dh[2];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          ph[t2] = sm.pds[g][mo][0][t2][lane];
+          dh[t2] = sm.pds[g][mo][1][t2][lane];
+        }
+        if constexpr (D == 128) {
+          const TransposedStore<D, Smem> ts(X, sm, bn, q0n, t);
+          bf16x8 bo[NP][2];
+          auto read_b = [&](int i) __attribute__((always_inline)) {
+            const int off = boff(mo, i >> 1, i & 1);
+            bo[i][0] = as_bf16x8(dotc + off);
+            bo[i][1] = as_bf16x8(qtc + off);
+          };
+          read_b(0);
+          read_b(1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < NP; ++i) {
+            dv[i >> 1] = mfma32(ph[i & 1], bo[i][0], dv[i >> 1]);
+            dk[i >> 1] = mfma32(dh[i & 1], bo[i][1], dk[i >> 1]);
+            if (i + 2 < NP) read_b(i + 2);
+            ts.row(2 * i);
+            ts.row(2 * i + 1);
+            if (i == 1) store_rowmajor<D>(X, sm, q0n, Sq, a.scale, t);
+            if (i == NP - 1) {
+              load_chunk<D>(X, qbase, obase, lbase, dbase, q0l, t);
+              lw3 = lword(c + 4);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int dd = 0; dd < NDH; ++dd)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+              const int off = boff(mo, dd, t2);
+              dv[dd] = mfma32(ph[t2], as_bf16x8(dotc + off), dv[dd]);
+              dk[dd] = mfma32(dh[t2], as_bf16x8(qtc + off), dk[dd]);
+            }
+          store_transposed<D>(X, sm, bn, q0n, t);
+          store_rowmajor<D>(X, sm, q0n, Sq, a.scale, t);
+          load_chunk<D>(X, qbase, obase, lbase, dbase, q0l, t);
+          lw3 = lword(c + 4);
+        }
+        __syncthreads();   // chunk c+1 in LDS; transposed c and P, dS read
       };
 
+      // chunk 0 staged directly; chunk 1 -> r1, chunk 2 -> r0
       ChunkStage<D> r0, r1;
-      load_chunk<D>(r0, qbase, obase, lbase, dbase, chunk_q0(0), t);
-      store_rowmajor<D>(r0, sm, chunk_q0(0), Sq, a.scale, t);
-      // K, V are in registers by now (loaded before chunk 0, which the store
+      load_chunk<D>(r0, qbase, obase, lbase, dbase, bq0, t);
+      store_transposed<D>(r0, sm, 0, bq0, t);
+      store_rowmajor<D>(r0, sm, bq0, Sq, a.scale, t);
+      // K, V are in registers by now (loaded before chunk 0, which the stores
       // waited for); an explicit wait says so to the compiler, which would
       // otherwise wait for them, and with them for the loads of later chunks,
       // inside every step
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      if (nchunks > 1) load_chunk<D>(r1, qbase, obase, lbase, dbase, chunk_q0(1), t);
+      load_chunk<D>(r1, qbase, obase, lbase, dbase, nchunks > 1 ? row0(list_value(lw1), 1) : Sq, t);
+      load_chunk<D>(r0, qbase, obase, lbase, dbase, nchunks > 2 ? row0(list_value(lw2), 2) : Sq, t);
       __syncthreads();
-      // two chunks per trip, so that the register sets stay statically named
+      // two chunks per trip (nchunks is even), so that the register sets stay
+      // statically named
+      static_assert(CPB % 2 == 0, "an even number of chunks per item");
       for (int c = 0; c < nchunks; c += 2) {
-        step(c, r0, r1);
-        if (c + 1 < nchunks) step(c + 1, r1, r0);
+        step(c, r1);
+        step(c + 1, r0);
       }
     }
 

@@ -34,6 +34,7 @@ template <int D>
 struct DqSmem {
   static constexpr int KST = D + 8;    // K, V row stride (elements): conflict-free row reads
   static constexpr int KTS = BK + 8;   // K^T row stride; keys in perm16 order
+  static_assert(stage_strides_ok(2 * KST, 2 * KTS), "strides the staging map needs");
   static constexpr int RED = 4 * (D / 32) * 16 * 64;   // fp32 dQ^T of 4 waves (final sum)
   union {
     struct {
@@ -56,28 +57,31 @@ __device__ __forceinline__ int kt_pos(int x) { return (x & ~15) | perm16(x & 15)
 
 // Global -> register staging of a key block's K and V (512 threads).  A unit
 // is 4 consecutive keys (4 m .. 4 m + 3) x 8 head-dim columns (chunk c) of one
-// tensor; every group of 16 lanes takes 4 consecutive m by 4 consecutive c,
-// so that its row-major 16-byte LDS stores cover all banks once.  K units
-// are also stored transposed.
+// tensor; the units of a wave are 16 row-units by 4 chunks of the staging map
+// (stage_row_unit, stage_chunk), which keeps the row-major stores and the
+// transposed stores of K free of bank conflicts.
 template <int D>
 struct DqStage {
   static constexpr int CPR = D / 8;
   static constexpr int NPT = (BK / 4) * CPR;              // units per tensor
   static constexpr int NU = 2 * NPT / kDqThreads;          // units per thread
   static_assert(NPT % 64 == 0 && (2 * NPT) % kDqThreads == 0, "unit tensor is wave-uniform");
+  static_assert(CPR % 4 == 0 && (BK / 4) % 16 == 0, "a wave's units are 16 row-units x 4 chunks");
   bf16x8 v[NU][4];
 
   static __device__ __forceinline__ unsigned unit(unsigned t, int j) { return t + kDqThreads * j; }
   static __device__ __forceinline__ int tensor(unsigned t, int j) {   // 0 = K, 1 = V
     return __builtin_amdgcn_readfirstlane((int)(unit(t, j) / NPT));
   }
+  // unit p of the tensor: wave p / 64 takes row-units 16 (p / 64 / (CPR/4)) ..
+  // + 16 and chunk quad (p / 64) % (CPR/4)
   static __device__ __forceinline__ int key(unsigned t, int j) {
-    const unsigned p = unit(t, j) % NPT;
-    return 4 * (int)(4u * ((p >> 4) / (CPR / 4)) + (p & 3u));
+    const int p = (int)(unit(t, j) % NPT);
+    return 4 * (16 * ((p >> 6) / (CPR / 4)) + stage_row_unit(p & 63));
   }
   static __device__ __forceinline__ int col(unsigned t, int j) {
-    const unsigned p = unit(t, j) % NPT;
-    return (int)(4u * ((p >> 4) % (CPR / 4)) + ((p >> 2) & 3u));
+    const int p = (int)(unit(t, j) % NPT);
+    return stage_chunk(p & 63, (p >> 6) % (CPR / 4));
   }
 };
 

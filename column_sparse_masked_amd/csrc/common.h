@@ -48,13 +48,33 @@ __device__ __forceinline__ int perm16(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
-// Physical row of row d of a transposed LDS tile (rows indexed by the head
-// dimension).  Staging lanes store rows 8 apart at the same column; rotating
-// the rows of every group of 8 by 2 (d/8 + d/32) spreads those stores over
-// distinct banks, while 16 consecutive rows (one MFMA operand read) still map
-// to 16 distinct rows of the same group of 16.
-__device__ __forceinline__ int trow(int d) {
-  return (d & ~7) | (((d & 7) + 2 * (d >> 3) + 2 * (d >> 5)) & 7);
+// Staging map of a tile of rows x 16-byte column chunks that is stored in LDS
+// both row-major (one 16-byte store per row of a unit) and transposed (one
+// 8-byte store of a unit's 4 rows per column).  A unit is 4 rows x 1 chunk;
+// the 64 lanes of a wave take 16 row-units by the 4 chunks of chunk quad q:
+//     row-unit  l % 16,     chunk  4 q + ((l % 16) / 2 + l / 16) % 4.
+// This GPU's LDS serves 8-byte accesses 16 lanes at a time and 16-byte stores
+// 8 lanes at a time; two of those lanes conflict when they touch the same
+// bank at different addresses, banks repeating every 128 bytes.
+//   transposed stores: the 16 lanes have 16 distinct row-units, i.e. 16
+//     distinct 8-byte places within a transposed row; with 8 transposed rows
+//     a multiple of 128 bytes long, the lanes' rows (8 apart) start on the
+//     same bank, so the places do not collide;
+//   row-major stores: the 8 lanes have row-units of both parities and all 4
+//     chunks, one lane per (parity, chunk); with 4 rows = 64 (mod 128) bytes
+//     that is 8 distinct 16-byte places.
+// (A permutation of rows instead of this map would also spread the
+// transposed stores, but 16-byte reads are served 16 lanes at a time at full
+// rate only when address bits 4-5 follow lane bits 0-1, which permuted rows
+// break for the operand reads of the transposed tile.)
+__device__ __forceinline__ int stage_row_unit(int lane) { return lane & 15; }
+__device__ __forceinline__ int stage_chunk(int lane, int quad) {
+  return 4 * quad + ((((lane & 15) >> 1) + (lane >> 4)) & 3);
+}
+// Byte strides that the map needs: 4 row-major rows = 64 (mod 128), 8
+// transposed rows = 0 (mod 128).
+constexpr bool stage_strides_ok(int row_bytes, int trow_bytes) {
+  return (4 * row_bytes) % 128 == 64 && (8 * trow_bytes) % 128 == 0;
 }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
@@ -112,6 +132,18 @@ __device__ __forceinline__ int list_entry(const uint16_t* lst, int i) {
   const uint32_t word = *(const_u32*)(addr & ~(uintptr_t)3);
   return (int)((addr & 2) ? (word >> 16) : (word & 0xffffu));
 }
+
+// The same in two parts: the scalar load of the word holding entry i, and the
+// shift that extracts the entry, so that the wait for the load can be placed
+// where the entry is used rather than where it is loaded.
+struct ListWord {
+  uint32_t word, shift;
+};
+__device__ __forceinline__ ListWord list_word(const uint16_t* lst, int i) {
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(lst + i);
+  return {*(const_u32*)(addr & ~(uintptr_t)3), (uint32_t)(addr & 2) * 8u};
+}
+__device__ __forceinline__ int list_value(ListWord x) { return (int)((x.word >> x.shift) & 0xffffu); }
 
 __device__ __forceinline__ const bf16x8& as_bf16x8(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
