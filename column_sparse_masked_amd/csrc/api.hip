@@ -181,12 +181,6 @@ fm_status fm_tile_bounds(const fm_problem* p, const int32_t* bounds, void* tilei
   a.counters = at<uint32_t>(tileinfo, L.counters);
   a.B = p->batch; a.H = p->heads; a.Hm = p->mask_heads;
   a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
-  if (p->batch == 0 || (L.nQ == 0 && L.nK == 0)) {
-    // nothing to classify; still leave empty queues behind
-    if (hipMemsetAsync(a.counters, 0, 16 * sizeof(uint32_t), (hipStream_t)stream) != hipSuccess)
-      return FM_ERR_HIP;
-    return FM_OK;
-  }
   return fm::launch_tile_bounds(a, (hipStream_t)stream) == hipSuccess ? FM_OK : FM_ERR_HIP;
 }
 

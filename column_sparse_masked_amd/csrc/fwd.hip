@@ -218,10 +218,11 @@ void attn_fwd_kernel(const FwdArgs a) {
       if (cnt > 1) load_k<D>(st, kbase, block_start(e_next), t);
       __syncthreads();
 
-      // Per key block t (K_t, V^T_t, bounds_t in LDS; K_{t+1} in registers):
-      //   S_t, interval mask | barrier | K_{t+1} -> LDS; bounds_{t+1}, V_{t+1}
-      //   -> registers; softmax and PV_t; bounds_{t+1} -> LDS | barrier |
-      //   V_{t+1} -> LDS, K_{t+2} -> registers.
+      // Per key block t (K_t, bounds_t in LDS; V^T_t being stored, K_{t+1}
+      // in registers), keys in halves h0, h1:
+      //   S_t(h0) | barrier | softmax, PV_t(h0); S_t(h1) | barrier | K_{t+1}
+      //   -> LDS; bounds_{t+1}, V_{t+1} -> registers; softmax, PV_t(h1);
+      //   bounds_{t+1} -> LDS | barrier | V_{t+1} -> LDS, K_{t+2} -> registers.
       for (int tt = 0; tt < cnt; ++tt) {
         const int k0 = block_start(e_cur);
         const bool need_mask = block_masked(e_cur, k0);
@@ -231,33 +232,96 @@ void attn_fwd_kernel(const FwdArgs a) {
         // list entry of block t+2, consumed after the second barrier
         const uint32_t e2_pending = (tt + 2 < cnt) ? list_at(tt + 2) : 0u;
 
-        // ---- S^T = K Q^T : lane holds query column li, keys 32*jb + 8r + 4hh + q ----
-        f32x16 s[4];
+        // The block is taken as two halves of 64 keys: S of a half, then its
+        // softmax and PV, so that S needs 32 accumulator registers rather
+        // than 64 (which leaves room to read the S operands ahead) and the
+        // exponentials of the first half run beside the products of the
+        // second.  Three barriers per block: V^T of the block, stored by
+        // every thread after the previous block's last barrier, is complete
+        // before the first half's PV (barrier 0); K is free once the second
+        // half's S is done (barrier 1); V^T once its PV is done (barrier 2).
+        float rs = 0.f;   // row sum of this block's P
+        auto half_s = [&](int hk, f32x16 (&s)[2]) __attribute__((always_inline)) {
+          // ---- S^T = K Q^T : lane holds query column li, keys 32*jb + 8r + 4hh + q ----
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) s[jb][v] = 0.f;
+            for (int v = 0; v < 16; ++v) s[j][v] = 0.f;
+          // k-step major: the two accumulators advance together
 #pragma unroll
           for (int kk = 0; kk < NS; ++kk)
-            s[jb] = mfma32(as_bf16x8(&sm.k[(32 * jb + li) * KST + 16 * kk + 8 * hh]), qf[kk], s[jb]);
-        }
-        if (need_mask) {
-          // words of 4 consecutive keys for this wave's 32 rows; bit li is
-          // this lane's row
-          const uint32_t* hw = &sm.hid[tt & 1][w][4 * hh];
 #pragma unroll
-          for (int jb = 0; jb < 4; ++jb)
+            for (int j = 0; j < 2; ++j)
+              s[j] = mfma32(as_bf16x8(&sm.k[(32 * (2 * hk + j) + li) * KST + 16 * kk + 8 * hh]), qf[kk], s[j]);
+          if (need_mask) {
+            // words of 4 consecutive keys for this wave's 32 rows; bit li is
+            // this lane's row
+            const uint32_t* hw = &sm.hid[tt & 1][w][4 * hh];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const uint4 h4 = *reinterpret_cast<const uint4*>(&hw[32 * jb + 8 * r]);
-              const uint32_t hq[4] = {h4.x, h4.y, h4.z, h4.w};
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const int v = 4 * r + q;
-                s[jb][v] = (hq[q] >> li) & 1u ? -INFINITY : s[jb][v];
+              for (int r = 0; r < 4; ++r) {
+                const uint4 h4 = *reinterpret_cast<const uint4*>(&hw[32 * (2 * hk + j) + 8 * r]);
+                const uint32_t hq[4] = {h4.x, h4.y, h4.z, h4.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const int v = 4 * r + q;
+                  s[j][v] = (hq[q] >> li) & 1u ? -INFINITY : s[j][v];
+                }
               }
+          }
+        };
+        auto half_pv = [&](int hk, f32x16 (&s)[2]) __attribute__((always_inline)) {
+          // ---- online softmax in the log2 domain ----
+          // The running maximum m_run is only moved when a row's maximum
+          // exceeds it by more than 8 (P <= 2^8 otherwise): O and l are sums
+          // taken against the same reference, so their ratio is unchanged,
+          // and most halves skip the rescale of the accumulators.
+          float mx = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[j][v]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float m_tile = mx * a.scale_log2;
+          if (__any(m_tile > m_run + 8.f)) {
+            const float m_new = fmaxf(m_run, m_tile);
+            const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[d][v] *= alpha;
+            l_run *= alpha;
+            rs *= alpha;
+            m_run = m_new;
+          }
+          const float base = (m_run == -INFINITY) ? 0.f : m_run;
+          // ---- P (8 keys at a time, rounded to bf16) and O^T += V^T P^T ----
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+              bf16x8 pb;
+#pragma unroll
+              for (int e8 = 0; e8 < 8; ++e8) {
+                const float pv = fast_exp2(fmaf(s[j][8 * t2 + e8], a.scale_log2, -base));
+                rs += pv;
+                pb[e8] = (bf16)pv;
+              }
+#pragma unroll
+              for (int d = 0; d < ND; ++d)
+                acc[d] = mfma32(as_bf16x8(&sm.vt[(32 * d + li) * VTS + 32 * (2 * hk + j) + 16 * t2 + 8 * hh]),
+                                pb, acc[d]);
             }
+        };
+        {
+          f32x16 s0[2];
+          half_s(0, s0);
+          __syncthreads();   // V^T of this block is in LDS
+          half_pv(0, s0);
         }
+        f32x16 s1[2];
+        half_s(1, s1);
         __syncthreads();   // every wave is done with this block's K
         int4 breg = make_int4(0, 0, 0, 0);
         if (has_next) {
@@ -265,51 +329,9 @@ void attn_fwd_kernel(const FwdArgs a) {
           if (nm_next && t < BK) breg = load_bnd(bbase, k0n, Sk, t);
           load_v<D>(st, vbase, k0n, t);
         }
-
-        // ---- online softmax in the log2 domain ----
-        // The running maximum m_run is only moved when a row's tile maximum
-        // exceeds it by more than 8 (P <= 2^8 otherwise): O and l are sums
-        // taken against the same reference, so their ratio is unchanged, and
-        // most tiles skip the rescale of the accumulators.
-        float mx = -INFINITY;
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[jb][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_tile = mx * a.scale_log2;
-        if (__any(m_tile > m_run + 8.f)) {
-          const float m_new = fmaxf(m_run, m_tile);
-          const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-#pragma unroll
-          for (int d = 0; d < ND; ++d)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[d][v] *= alpha;
-          l_run *= alpha;
-          m_run = m_new;
-        }
-        const float base = (m_run == -INFINITY) ? 0.f : m_run;
-
-        // ---- P (8 keys at a time, rounded to bf16) and O^T += V^T P^T ----
-        float rs = 0.f;
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2) {
-            bf16x8 pb;
-#pragma unroll
-            for (int e8 = 0; e8 < 8; ++e8) {
-              const float pv = fast_exp2(fmaf(s[jb][8 * t2 + e8], a.scale_log2, -base));
-              rs += pv;
-              pb[e8] = (bf16)pv;
-            }
-#pragma unroll
-            for (int d = 0; d < ND; ++d)
-              acc[d] = mfma32(as_bf16x8(&sm.vt[(32 * d + li) * VTS + 32 * jb + 16 * t2 + 8 * hh]),
-                              pb, acc[d]);
-          }
+        half_pv(1, s1);
         // keep the row sum here: left to itself the compiler sinks it past
-        // the barrier and keeps all 64 P values alive into the next loads
+        // the barrier and keeps the P values alive into the next loads
         asm volatile("" : "+v"(rs));
         l_run += rs;
         // the other mask buffer was last read before the first barrier of block t-1

@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kQueueThreads) void queue_kernel(
     int nK) {
   __shared__ int hist[kBuckets];
   __shared__ int scratch[kQueueThreads / 64 + 1];
-  sort_items(cnt_q, fwd_q, B, H, Hm, nQ, hist, scratch);
+  if (nQ > 0) sort_items(cnt_q, fwd_q, B, H, Hm, nQ, hist, scratch);
   if (nK > 0) sort_items(cnt_k, bwd_q, B, H, Hm, nK, hist, scratch);
   if (threadIdx.x == 0) {
     counters[kCtrFwdItems] = (uint32_t)((long)B * H * nQ);
@@ -240,11 +240,16 @@ __global__ __launch_bounds__(kQueueThreads) void queue_kernel(
 
 hipError_t launch_tile_bounds(const TileArgs& a, hipStream_t stream) {
   const unsigned bhm = (unsigned)((long)a.B * a.Hm);
-  if (a.nK > 0) {
+  if (bhm > 0 && a.nK > 0) {
     kbsum_kernel<<<dim3(a.nK, bhm), BK, 0, stream>>>(a.bounds, a.kbsum, a.Sq, a.Sk, a.nK);
   }
-  classify_kernel<<<dim3(a.nQ + a.nK, bhm), 256, 0, stream>>>(a.kbsum, a.cls, a.cnt_q, a.cnt_k,
-                                                              a.list_q, a.list_k, a.Sq, a.nQ, a.nK);
+  if (bhm > 0 && a.nQ + a.nK > 0) {
+    classify_kernel<<<dim3(a.nQ + a.nK, bhm), 256, 0, stream>>>(a.kbsum, a.cls, a.cnt_q, a.cnt_k,
+                                                                a.list_q, a.list_k, a.Sq, a.nQ, a.nK);
+  }
+  // always, also for empty problems: it leaves (empty) queues and zeroed
+  // counters behind, with a kernel rather than a memset, which stays correct
+  // when a caller replays the calls as a captured graph
   queue_kernel<<<1, kQueueThreads, 0, stream>>>(a.cnt_q, a.cnt_k, a.fwd_queue, a.bwd_queue,
                                                 a.counters, a.B, a.H, a.Hm, a.nQ, a.nK);
   return hipGetLastError();

@@ -85,6 +85,20 @@ def test_empty_key_set():
     assert got["dk"].size == 0
 
 
+def test_empty_problem_zeroes_counters():
+    """Sq = Sk = 0: the tile pass launches only its queue kernel, which must
+    still zero the counters of a tileinfo holding garbage."""
+    import torch
+    from column_sparse_masked_amd.api import MaskedAttention, to_device_bounds
+    w = M.custom(M.empty_bounds(0, 0), B=1, H=2, Sq=0, D=64, seed=43)
+    say("[parity] empty problem")
+    att = MaskedAttention.for_workload(w)
+    att.buf.tileinfo.fill_(0xFF)
+    att.tile_bounds(to_device_bounds(w.bounds))
+    torch.cuda.synchronize()
+    assert att.read_tileinfo()["counters"].tolist() == [0] * 8 + [0xFFFFFFFF] * 8
+
+
 def test_empty_query_set():
     """Sq = 0: no rows; dK = dV = 0."""
     import torch
