@@ -6,7 +6,10 @@
 One step is the whole hot path over one batch: the tile pass
 (fm_tile_bounds), the forward (fm_attn_fwd) and the backward (fm_attn_bwd),
 all through the C ABI, on inputs already resident in device memory.  W untimed
-steps, then K timed steps bracketed by torch.cuda.synchronize().
+steps; K eager steps with the library's kernel-event hook (per-stage and
+per-kernel times); then the step captured once as a HIP graph, W untimed
+replays and K timed replays bracketed by torch.cuda.synchronize() (the replay
+must reproduce the eager outputs bit for bit, else the eager steps are timed).
 
 The throughput is mask-effective: forward 4*D*nnz and backward 10*D*nnz flops
 per (batch, head), nnz being the number of unmasked (query, key) pairs, so
@@ -197,6 +200,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     print(f"# warmup {args.warmup} steps done", file=sys.stderr, flush=True)
 
+    # Eager steps with the library's event hook: per-stage and per-kernel times.
     evs = [{n: new_event() for n in ("s0", "s1", "s2", "s3", "fk0", "fk1", "bk0", "bk1", "bq0", "bq1")}
            for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -204,8 +208,37 @@ def main(argv=None):
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    print(f"# timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+    wall_eager = time.perf_counter() - t0
+    ref = [x.clone() for x in (o, lse, dq, dk, dv)]
+
+    # The timed steps: one step captured as a HIP graph and replayed, which
+    # removes the launch gaps between the step's seven kernels.  A replay must
+    # reproduce the eager outputs bit for bit, else the eager time is used.
+    launch = "hip_graph"
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for x in (o, lse, dq, dk, dv):
+            x.view(torch.uint8).fill_(0xA5)
+        g.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+                   for a, b in zip((o, lse, dq, dk, dv), ref)):
+            raise RuntimeError("graph replay differs from the eager step")
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    except Exception as exc:   # graph capture unavailable: time the eager steps instead
+        print(f"# graph replay not used ({exc}); timing the eager steps", file=sys.stderr, flush=True)
+        launch, wall = "eager", wall_eager
+    print(f"# timed {args.steps} steps ({launch}) in {wall:.3f} s; eager {wall_eager:.3f} s",
+          file=sys.stderr, flush=True)
 
     def avg_ms(a, b):
         return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
@@ -254,7 +287,9 @@ def main(argv=None):
             "seed": w.seed, "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "D": w.D,
             "nnz_per_head_mean": nnz / (w.B * w.H),
             "mask_flops_fwd_bwd": f_fwd + f_bwd,
+            "step_launch": launch,
         },
+        "ms_per_step_eager": round(wall_eager / args.steps * 1e3, 4),
         "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "stages_ms": {"tile_bounds": round(t_tile, 4), "fwd": round(t_fwd, 4), "bwd": round(t_bwd, 4)},
         "tflops_fwd_kernel": round(f_fwd / (k_fwd * 1e-3) / 1e12, 2),
