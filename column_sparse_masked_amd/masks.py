@@ -177,6 +177,57 @@ def blockwise_causal_bounds(S: int, block: int) -> np.ndarray:
     return b.astype(np.int32)
 
 
+def document_bounds(doc_lens) -> np.ndarray:
+    """Bidirectional attention inside each document: row i sees column j iff
+    both are in the same document.  Rows of earlier documents form the upper
+    interval, rows of later documents the lower one."""
+    S = int(sum(doc_lens))
+    starts, ends = _starts_ends(doc_lens)
+    b = np.empty((S, 4), dtype=np.int64)
+    b[:, LTS], b[:, LTE] = np.repeat(ends, doc_lens), S
+    b[:, UTS], b[:, UTE] = 0, np.repeat(starts, doc_lens)
+    return b.astype(np.int32)
+
+
+def global_sliding_bounds(S: int, n_global: int, window: int) -> np.ndarray:
+    """Bidirectional sliding window with global tokens: row i sees column j iff
+    |i - j| < window, or i < n_global, or j < n_global.  A global column is
+    never masked; any other column j is masked on the non-global rows above
+    the window, [n_global, j - window + 1), and on the rows below it,
+    [j + window, S).  The upper interval starts past row 0 here, unlike the
+    other families."""
+    j = np.arange(S, dtype=np.int64)
+    g = min(max(int(n_global), 0), S)
+    glob = j < g
+    b = np.empty((S, 4), dtype=np.int64)
+    b[:, LTS] = np.where(glob, S, np.minimum(j + window, S))
+    b[:, LTE] = S
+    b[:, UTS] = np.where(glob, 0, g)
+    b[:, UTE] = np.where(glob, 0, np.maximum(j - window + 1, g))
+    return b.astype(np.int32)
+
+
+def eviction_bounds(evict_row) -> np.ndarray:
+    """Causal attention in which key j is evicted from row evict_row[j] on:
+    row i sees column j iff j <= i < evict_row[j] (evict_row[j] >= j + 1 keeps
+    the diagonal; evict_row[j] = S never evicts)."""
+    e = np.asarray(evict_row, dtype=np.int64)
+    S = e.shape[0]
+    j = np.arange(S, dtype=np.int64)
+    if S and (e < j + 1).any():
+        raise ValueError("eviction row must come after the key's own row")
+    b = np.empty((S, 4), dtype=np.int64)
+    b[:, LTS], b[:, LTE] = np.minimum(e, S), S
+    b[:, UTS], b[:, UTE] = 0, j
+    return b.astype(np.int32)
+
+
+def random_eviction_rows(rng: np.random.Generator, S: int) -> np.ndarray:
+    """Eviction row of each key drawn uniformly from [j + 1, S]."""
+    j = np.arange(S, dtype=np.int64)
+    return j + 1 + np.floor(rng.random(S) * (S - j)).astype(np.int64)
+
+
 def empty_bounds(Sk: int, Sq: int) -> np.ndarray:
     """No element masked (both intervals empty)."""
     b = np.empty((Sk, 4), dtype=np.int32)
@@ -332,6 +383,27 @@ def block_causal(B=1, H=4, S=4096, D=128, block=512, seed=6) -> Workload:
     rng = np.random.default_rng(seed)
     return _finish("block_causal", rng, B, H, S, S, D,
                    blockwise_causal_bounds(S, block), seed, {"block": block})
+
+
+def document(B=1, H=4, S=4096, D=128, n_docs=6, seed=7) -> Workload:
+    rng = np.random.default_rng(seed)
+    lens = composition(rng, S, n_docs)
+    return _finish("document", rng, B, H, S, S, D, document_bounds(lens), seed,
+                   {"doc_lens": lens})
+
+
+def global_sliding(B=1, H=4, S=4096, D=128, n_global=64, window=512, seed=8) -> Workload:
+    rng = np.random.default_rng(seed)
+    return _finish("global_sliding", rng, B, H, S, S, D,
+                   global_sliding_bounds(S, n_global, window), seed,
+                   {"n_global": n_global, "window": window})
+
+
+def random_eviction(B=1, H=4, S=4096, D=128, seed=10) -> Workload:
+    rng = np.random.default_rng(seed)
+    rows = random_eviction_rows(rng, S)
+    return _finish("random_eviction", rng, B, H, S, S, D, eviction_bounds(rows), seed,
+                   {"evict_row": rows})
 
 
 CONFIGS = {

@@ -2,6 +2,7 @@
 
 Small problems: every output compared in full.  They span several 128x128
 tiles, ragged tails, both head sizes, shared and per-head masks, Sq != Sk,
+every mask family of the bound builders,
 out-of-range bounds and the degenerate cases (no mask, everything masked,
 fully masked rows, empty key or query sets).
 """
@@ -46,6 +47,17 @@ def _cases():
                                                         rank=1, seed=9, lo=64, hi=2048),
         "block_causal_S900_D64": lambda: M.custom(M.blockwise_causal_bounds(900, 100), B=1, H=2,
                                                   Sq=900, D=64, seed=24),
+        "document_bidir_S1100_D128": lambda: M.custom(
+            M.document_bounds(M.composition(np.random.default_rng(4), 1100, 5)),
+            B=1, H=2, Sq=1100, D=128, seed=33),
+        "global_sliding_S1200_g70_w150": lambda: M.custom(M.global_sliding_bounds(1200, 70, 150), B=2, H=2,
+                                                          Sq=1200, D=128, seed=34),
+        "random_eviction_S1000_D64": lambda: M.custom(
+            M.eviction_bounds(M.random_eviction_rows(np.random.default_rng(6), 1000)),
+            B=1, H=2, Sq=1000, D=64, seed=35),
+        "document_workload_S2048": lambda: M.document(H=2, S=2048),
+        "global_sliding_workload_S2048": lambda: M.global_sliding(H=2, S=2048, window=300),
+        "random_eviction_workload_S2048": lambda: M.random_eviction(H=2, S=2048),
         "per_head_random_Sq333_Sk517_D64": lambda: M.custom(
             None, B=2, H=3, Sq=333, D=64, seed=25,
             per_head_bounds=np.random.default_rng(5).integers(-20, 353, size=(2, 3, 517, 4)).astype(np.int32)),

@@ -50,6 +50,15 @@ def _bounds_for(name, args):
     if name == "block_causal":
         b = M.blockwise_causal_bounds(int(args["S"]), int(args["block"]))
         return b, np.arange(b.shape[0])
+    if name == "document":
+        b = M.document_bounds(_ints(args["docs"]))
+        return b, np.arange(b.shape[0])
+    if name == "global_sliding":
+        b = M.global_sliding_bounds(int(args["S"]), int(args["global"]), int(args["window"]))
+        return b, np.arange(b.shape[0])
+    if name == "eviction":
+        b = M.eviction_bounds(_ints(args["ends"]))
+        return b, np.arange(b.shape[0])
     if name == "cp_local":
         docs = _ints(args["docs"])
         S, world, rank = sum(docs), int(args["world"]), int(args["rank"])
@@ -142,6 +151,40 @@ def test_block_causal_definition(S, blk):
     want = (j // blk) <= (i // blk)
     got = ~dense_mask(M.blockwise_causal_bounds(S, blk), np.arange(S))
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("S", SIZES)
+def test_document_definition(S):
+    rng = np.random.default_rng(300 + S)
+    for _ in range(5):
+        lens = M.composition(rng, S, int(rng.integers(1, min(S, 6) + 1)))
+        d = _doc_ids(lens)
+        i, j = np.meshgrid(np.arange(S), np.arange(S), indexing="ij")
+        got = ~dense_mask(M.document_bounds(lens), np.arange(S))
+        assert np.array_equal(got, d[i] == d[j])
+
+
+@pytest.mark.parametrize("S", SIZES)
+@pytest.mark.parametrize("g,w", [(0, 1), (0, 3), (1, 2), (3, 1), (5, 4), (200, 2), (2, 1000)])
+def test_global_sliding_definition(S, g, w):
+    i, j = np.meshgrid(np.arange(S), np.arange(S), indexing="ij")
+    want = (np.abs(i - j) < w) | (i < g) | (j < g)
+    got = ~dense_mask(M.global_sliding_bounds(S, g, w), np.arange(S))
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("S", SIZES)
+def test_eviction_definition(S):
+    rng = np.random.default_rng(400 + S)
+    for _ in range(5):
+        e = M.random_eviction_rows(rng, S)
+        assert (e >= np.arange(S) + 1).all() and (e <= S).all()
+        i, j = np.meshgrid(np.arange(S), np.arange(S), indexing="ij")
+        want = (j <= i) & (i < e[j])
+        got = ~dense_mask(M.eviction_bounds(e), np.arange(S))
+        assert np.array_equal(got, want)
+    with pytest.raises(ValueError):
+        M.eviction_bounds(np.arange(S))   # key j evicted at its own row
 
 
 @pytest.mark.parametrize("S,world", [(16, 2), (64, 4), (128, 8), (96, 4)])

@@ -71,7 +71,8 @@ def test_causal_equals_sdpa_is_causal():
         np.testing.assert_allclose(a, r.numpy(), rtol=1e-10, atol=1e-11)
 
 
-@pytest.mark.parametrize("family", ["causal_document", "sliding", "share_question", "prefix", "block"])
+@pytest.mark.parametrize("family", ["causal_document", "sliding", "share_question", "prefix", "block",
+                                    "document", "global_sliding", "eviction"])
 def test_masked_equals_sdpa_with_dense_mask(family):
     rng = np.random.default_rng(11)
     S, D = 333, 16
@@ -83,8 +84,14 @@ def test_masked_equals_sdpa_with_dense_mask(family):
         b = M.share_question_bounds(60, M.composition(rng, S - 60, 4))
     elif family == "prefix":
         b = M.prefix_document_bounds(M.composition(rng, S, 3), 0.3)
-    else:
+    elif family == "block":
         b = M.blockwise_causal_bounds(S, 64)
+    elif family == "document":
+        b = M.document_bounds(M.composition(rng, S, 4))
+    elif family == "global_sliding":
+        b = M.global_sliding_bounds(S, 17, 30)
+    else:
+        b = M.eviction_bounds(M.random_eviction_rows(rng, S))
     q, k, v, do = (_rand(rng, S, D) for _ in range(4))
     scale = 1 / math.sqrt(D)
     o, _, dq, dk, dv = _oracle_head(q, k, v, do, b, scale)
