@@ -19,9 +19,13 @@ BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["tiles.hip", "fwd.hip", "bwd.hip", "bwd_dq.hip", "api.hip"]
 ARCH = os.environ.get("FM_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed fp32 VALU instructions are turned off for all device code.
+# Packed fp32 VALU instructions are turned off for all device code.  The
+# atomic optimizer is off: it turns a one-lane atomic with a uniform address
+# into a wave-wide one whose result every lane needs at once, which makes the
+# kernels wait for their work-queue ticket right where they take it.
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
 def _run(cmd):

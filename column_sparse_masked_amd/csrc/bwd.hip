@@ -248,6 +248,51 @@ __device__ __forceinline__ void zero_row_terms(const Smem& sm, unsigned t) {
   }
 }
 
+// One key-stationary work item (batch*head, key block): what the kernel needs
+// of it in scalar registers.
+struct BwdItem {
+  uint32_t idx;           // queue position (>= the item count: no item)
+  int kb, k0, cnt, rot, nchunks;
+  long bh, bhm;
+  const uint16_t* lst;    // the key block's list of non-skipped query blocks
+  BufRsrc qbase, obase, kbase, vbase, lbase, dbase;
+
+  // List word of chunk c (clamped to the last chunk: entries past the end
+  // are loaded but not used).  Each item starts its walk at block kb % cnt
+  // (and wraps): neighbouring key blocks, which run at the same time, then
+  // read different query blocks.
+  __device__ __forceinline__ ListWord lword(int c) const {
+    const int j = min(c, nchunks - 1) / CPB + rot;
+    return list_word(lst, j < cnt ? j : j - cnt);
+  }
+};
+
+template <int D>
+__device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, const uint32_t (&hdr)[4]) {
+  // values read from LDS are not known to be uniform: broadcast them, so that
+  // the buffer resources built from them stay in scalar registers
+  BwdItem x;
+  x.idx = __builtin_amdgcn_readfirstlane(hdr[0]);
+  const uint32_t it = __builtin_amdgcn_readfirstlane(hdr[1]);
+  x.cnt = __builtin_amdgcn_readfirstlane((int)hdr[2]);
+  x.nchunks = CPB * x.cnt;   // each query block is CPB chunks of QC rows
+  x.bh = it / a.nK;
+  x.kb = (int)(it % a.nK);
+  x.k0 = x.kb * BK;
+  x.rot = x.cnt > 0 ? x.kb % x.cnt : 0;
+  const int b = (int)(x.bh / a.H), h = (int)(x.bh % a.H);
+  x.bhm = (long)b * a.Hm + (a.Hm == 1 ? 0 : h);
+  x.lst = a.list_k + (x.bhm * a.nK + x.kb) * (long)a.nQ;
+  const int Sq = a.Sq, Sk = a.Sk;
+  x.qbase = make_rsrc(a.q + x.bh * Sq * (long)D, (uint32_t)Sq * D * 2u);
+  x.obase = make_rsrc(a.dout + x.bh * Sq * (long)D, (uint32_t)Sq * D * 2u);
+  x.kbase = make_rsrc(a.k + x.bh * Sk * (long)D, (uint32_t)Sk * D * 2u);
+  x.vbase = make_rsrc(a.v + x.bh * Sk * (long)D, (uint32_t)Sk * D * 2u);
+  x.lbase = make_rsrc(a.lse + x.bh * Sq, (uint32_t)Sq * 4u);
+  x.dbase = make_rsrc(a.delta + x.bh * Sq, (uint32_t)Sq * 4u);
+  return x;
+}
+
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_kernel(const BwdArgs a) {
@@ -258,7 +303,7 @@ void attn_bwd_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 lds_rm[2 * Smem::RM];
   __shared__ __attribute__((aligned(16))) bf16 lds_t[4 * Smem::TR];
   __shared__ bf16x8 lds_pds[4][2][2][2][64];
-  __shared__ uint32_t lds_item;
+  __shared__ uint32_t lds_hdr[2][4];   // headers of this and the next item
   Smem sm;
   sm.q = lds_rm;
   sm.dout = lds_rm + Smem::RM;
@@ -271,60 +316,77 @@ void attn_bwd_kernel(const BwdArgs a) {
   const int g = w & 3, m = w >> 2;   // key group; chunk half (S, dP) and head-dim half (dK, dV)
   const uint32_t max_items = (uint32_t)((long)a.B * a.H * a.nK);
   const uint32_t n_items = min(a.counters[kCtrBwdItems], max_items);
+  // row stride (elements) of the dK / dV tile staged in LDS for the stores
+  constexpr int EST = D + 8;
+  static_assert(2 * BK * EST <= 4 * Smem::TR, "the dK / dV tile fits the transposed staging buffers");
   const int Sq = a.Sq, Sk = a.Sk;
 
-  zero_row_terms<D>(sm, t);   // made visible by the first barrier below
-  for (;;) {
-    if (t == 0) lds_item = atomicAdd(&a.counters[kCtrBwdNext], 1u);
-    __syncthreads();
-    const uint32_t idx = __builtin_amdgcn_readfirstlane(lds_item);
-    if (idx >= n_items) break;
-    // values loaded from memory are not known to be uniform: broadcast them,
-    // so that the buffer resources built from them stay in scalar registers
-    const uint32_t it = __builtin_amdgcn_readfirstlane(min(a.queue[idx], max_items - 1));
-    const long bh = it / a.nK;
-    const int kb = (int)(it % a.nK);
-    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-    const long bhm = (long)b * a.Hm + (a.Hm == 1 ? 0 : h);
-    const int cnt = __builtin_amdgcn_readfirstlane(min(a.cnt_k[bhm * a.nK + kb], a.nQ));
-    const uint16_t* lst = a.list_k + (bhm * a.nK + kb) * (long)a.nQ;
-    const int k0 = kb * BK;
-    const bool ragged_k = k0 + BK > Sk;
-    const BufRsrc qbase = make_rsrc(a.q + bh * Sq * (long)D, (uint32_t)Sq * D * 2u);
-    const BufRsrc obase = make_rsrc(a.dout + bh * Sq * (long)D, (uint32_t)Sq * D * 2u);
-    const BufRsrc kbase = make_rsrc(a.k + bh * Sk * (long)D, (uint32_t)Sk * D * 2u);
-    const BufRsrc vbase = make_rsrc(a.v + bh * Sk * (long)D, (uint32_t)Sk * D * 2u);
-    const BufRsrc lbase = make_rsrc(a.lse + bh * Sq, (uint32_t)Sq * 4u);
-    const BufRsrc dbase = make_rsrc(a.delta + bh * Sq, (uint32_t)Sq * 4u);
-    // Each item starts its walk at block kb % cnt (and wraps): neighbouring
-    // key blocks, which run at the same time, then read different query blocks.
-    const int rot = cnt > 0 ? kb % cnt : 0;
-    auto list_at = [&](int i) {
-      const int j = i + rot;
-      return list_entry(lst, j < cnt ? j : j - cnt);
-    };
+  const ItemQueue iq{&a.counters[kCtrBwdNext], a.queue, a.cnt_k, n_items, max_items, a.nK, a.H, a.Hm, a.nQ};
+  zero_row_terms<D>(sm, t);
+  if (t == 0) iq.first(lds_hdr[0]);
+  __syncthreads();
 
-    // this lane's key: bounds (keys past the end are masked for every row),
-    // K and V rows as MFMA B operands
-    const int jrow = k0 + 32 * g + li;
-    int4 bd = make_int4(INT_MIN, INT_MAX, 0, 0);
-    if (jrow < Sk) bd = a.bounds[bhm * Sk + jrow];
-    bf16x8 kf[NS], vf[NS];
-    {
-      const uint32_t off = ((uint32_t)jrow * D + 8u * hh) * 2u;
+  // B operand of the row-term k-step: ones in columns D, D+1
+  bf16x8 ones = zero_bf16x8();
+  if (hh == 0) {
+    ones[0] = (bf16)1.0f;
+    ones[1] = (bf16)1.0f;
+  }
+  // first row of chunk c of a query block with list entry e
+  auto row0 = [&](int e, int c) __attribute__((always_inline)) {
+    return min(e & kListIndex, a.nQ - 1) * BQ + (c % CPB) * QC;
+  };
+
+  // An item's loads that do not wait for its LDS (the lane's key bounds, K
+  // and V rows as MFMA B operands, the first list words and the first chunk
+  // of Q and dO) are issued before the previous item's dK and dV are written,
+  // so that they are in flight during those stores.
+  ItemPrefetch pf;
+  i32x4 bd;        // the lane's key bounds (LTS, LTE, UTS, UTE)
+  bool key_live;   // the lane's key is < Sk
+  bf16x8 kf[NS], vf[NS];
+  ListWord lw0, lw1, lw2, lw3;
+  ChunkStage<D> r0, r1;
+  auto preload = [&](const BwdItem& x) __attribute__((always_inline)) {
+    // (a branch-free load: keys past the end read zeros here and are masked
+    // for every row where the bounds are used)
+    const int jrow = x.k0 + 32 * g + li;
+    bd = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(a.bounds + x.bhm * Sk, (uint32_t)Sk * 16u),
+                                               jrow * 16, 0, 0);
+    key_live = jrow < Sk;
+    const uint32_t off = ((uint32_t)jrow * D + 8u * hh) * 2u;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        kf[s] = buf_load16(kbase, off + 32u * s);
-        vf[s] = buf_load16(vbase, off + 32u * s);
-      }
+    for (int s = 0; s < NS; ++s) {
+      kf[s] = buf_load16(x.kbase, off + 32u * s);
+      vf[s] = buf_load16(x.vbase, off + 32u * s);
     }
-    // B operand of the row-term k-step: ones in columns D, D+1
-    bf16x8 ones = zero_bf16x8();
-    if (hh == 0) {
-      ones[0] = (bf16)1.0f;
-      ones[1] = (bf16)1.0f;
+    int bq0 = Sq;   // no chunk: rows at Sq read as zeros without memory accesses
+    if (x.nchunks > 0) {
+      lw0 = x.lword(0);
+      lw1 = x.lword(1);
+      lw2 = x.lword(2);
+      lw3 = x.lword(3);
+      bq0 = row0(list_value(lw0), 0);
     }
-    f32x16 dk[NDH], dv[NDH];   // keys 32 g + 8 r + 4 hh + q, columns D/2 m + 32 dd + li
+    load_chunk<D>(r0, x.qbase, x.obase, x.lbase, x.dbase, bq0, t);
+  };
+  BwdItem cur = bwd_item<D>(a, lds_hdr[0]);
+  if (cur.idx < n_items) {
+    pf.take(iq, t);   // the ticket of the next item, before the item's loads
+    preload(cur);
+  }
+
+  for (int n = 0;; ++n) {
+    if (cur.idx >= n_items) break;
+    // the step code below reads the item through these names
+    const int cnt = cur.cnt, nchunks = cur.nchunks, kb = cur.kb, k0 = cur.k0;
+    const bool ragged_k = k0 + BK > Sk;
+    const BufRsrc qbase = cur.qbase, obase = cur.obase, lbase = cur.lbase, dbase = cur.dbase;
+    (void)kb;
+    auto lword = [&](int c) __attribute__((always_inline)) { return cur.lword(c); };
+
+    // dK^T, dV^T: lane holds key 32 g + li, columns D/2 m + 32 dd + 8 r + 4 hh + q
+    f32x16 dk[NDH], dv[NDH];
 #pragma unroll
     for (int dd = 0; dd < NDH; ++dd)
 #pragma unroll
@@ -333,24 +395,7 @@ void attn_bwd_kernel(const BwdArgs a) {
         dv[dd][v] = 0.f;
       }
 
-    const int nchunks = CPB * cnt;   // each query block is CPB chunks of QC rows
     if (nchunks > 0) {
-      // List word of chunk c (c clamped to the last chunk: entries past the
-      // end are loaded but not used) and the first row of chunk c.
-      auto lword = [&](int c) __attribute__((always_inline)) {
-        const int j = min(c, nchunks - 1) / CPB + rot;
-        return list_word(lst, j < cnt ? j : j - cnt);
-      };
-      auto row0 = [&](int e, int c) __attribute__((always_inline)) {
-        return min(e & kListIndex, a.nQ - 1) * BQ + (c % CPB) * QC;
-      };
-      // List words of chunks c .. c+3 at the top of step c.  Step c loads the
-      // word of chunk c+4 at its end: a scalar load's result is waited for
-      // with lgkmcnt(0), which also waits for every LDS access in flight, and
-      // the barrier that ends the step waits for all of them anyway.
-      ListWord lw0 = lword(0), lw1 = lword(1), lw2 = lword(2), lw3 = lword(3);
-      const int bq0 = row0(list_value(lw0), 0);
-
       // B operand of the dV (tensor 0) / dK (tensor 1) product of rows of
       // half hf, head-dim block dd, k-half t2, from transposed buffer buf
       auto boff = [&](int hf, int dd, int t2) __attribute__((always_inline)) {
@@ -420,7 +465,8 @@ void attn_bwd_kernel(const BwdArgs a) {
             return hi > lo ? (~0u >> (32 - hi)) & (~0u << lo) : 0u;
           };
           const uint32_t hidden =
-              (rows(clip(bd.x), clip(bd.y)) | rows(clip(bd.z), clip(bd.w))) >> (4 * hh);
+              key_live ? (rows(clip(bd[0]), clip(bd[1])) | rows(clip(bd[2]), clip(bd[3]))) >> (4 * hh)
+                       : ~0u;
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             s[v] = (hidden >> (8 * (v >> 2) + (v & 3))) & 1u ? -INFINITY : s[v];
@@ -452,8 +498,8 @@ void attn_bwd_kernel(const BwdArgs a) {
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int i = 0; i < NP; ++i) {
-            dv[i >> 1] = mfma32(pb[i & 1], bo[i][0], dv[i >> 1]);
-            dk[i >> 1] = mfma32(dsb[i & 1], bo[i][1], dk[i >> 1]);
+            dv[i >> 1] = mfma32(bo[i][0], pb[i & 1], dv[i >> 1]);
+            dk[i >> 1] = mfma32(bo[i][1], dsb[i & 1], dk[i >> 1]);
             if (i + 2 < NP) read_b(i + 2);
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -463,8 +509,8 @@ void attn_bwd_kernel(const BwdArgs a) {
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2) {
               const int off = boff(m, dd, t2);
-              dv[dd] = mfma32(pb[t2], as_bf16x8(dotc + off), dv[dd]);
-              dk[dd] = mfma32(dsb[t2], as_bf16x8(qtc + off), dk[dd]);
+              dv[dd] = mfma32(as_bf16x8(dotc + off), pb[t2], dv[dd]);
+              dk[dd] = mfma32(as_bf16x8(qtc + off), dsb[t2], dk[dd]);
             }
         }
         __syncthreads();   // P, dS in LDS; row-major c read
@@ -491,8 +537,8 @@ void attn_bwd_kernel(const BwdArgs a) {
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int i = 0; i < NP; ++i) {
-            dv[i >> 1] = mfma32(ph[i & 1], bo[i][0], dv[i >> 1]);
-            dk[i >> 1] = mfma32(dh[i & 1], bo[i][1], dk[i >> 1]);
+            dv[i >> 1] = mfma32(bo[i][0], ph[i & 1], dv[i >> 1]);
+            dk[i >> 1] = mfma32(bo[i][1], dh[i & 1], dk[i >> 1]);
             if (i + 2 < NP) read_b(i + 2);
             ts.row(2 * i);
             ts.row(2 * i + 1);
@@ -509,20 +555,22 @@ void attn_bwd_kernel(const BwdArgs a) {
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2) {
               const int off = boff(mo, dd, t2);
-              dv[dd] = mfma32(ph[t2], as_bf16x8(dotc + off), dv[dd]);
-              dk[dd] = mfma32(dh[t2], as_bf16x8(qtc + off), dk[dd]);
+              dv[dd] = mfma32(as_bf16x8(dotc + off), ph[t2], dv[dd]);
+              dk[dd] = mfma32(as_bf16x8(qtc + off), dh[t2], dk[dd]);
             }
           store_transposed<D>(X, sm, bn, q0n, t);
           store_rowmajor<D>(X, sm, q0n, Sq, a.scale, t);
           load_chunk<D>(X, qbase, obase, lbase, dbase, q0l, t);
           lw3 = lword(c + 4);
         }
+        // the next item's header, one scalar load in each of the first two steps
+        if (c == 0) pf.fetch_entry(iq, lds_hdr[(n + 1) & 1]);
+        if (c == 1) pf.fetch_count(iq);
         __syncthreads();   // chunk c+1 in LDS; transposed c and P, dS read
       };
 
-      // chunk 0 staged directly; chunk 1 -> r1, chunk 2 -> r0
-      ChunkStage<D> r0, r1;
-      load_chunk<D>(r0, qbase, obase, lbase, dbase, bq0, t);
+      // chunk 0 (in r0) staged; chunk 1 -> r1, chunk 2 -> r0
+      const int bq0 = row0(list_value(lw0), 0);
       store_transposed<D>(r0, sm, 0, bq0, t);
       store_rowmajor<D>(r0, sm, bq0, Sq, a.scale, t);
       // K, V are in registers by now (loaded before chunk 0, which the stores
@@ -530,6 +578,7 @@ void attn_bwd_kernel(const BwdArgs a) {
       // otherwise wait for them, and with them for the loads of later chunks,
       // inside every step
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      pf.stash(lds_hdr[(n + 1) & 1], t);
       load_chunk<D>(r1, qbase, obase, lbase, dbase, nchunks > 1 ? row0(list_value(lw1), 1) : Sq, t);
       load_chunk<D>(r0, qbase, obase, lbase, dbase, nchunks > 2 ? row0(list_value(lw2), 2) : Sq, t);
       __syncthreads();
@@ -540,27 +589,62 @@ void attn_bwd_kernel(const BwdArgs a) {
         step(c, r1);
         step(c + 1, r0);
       }
+      pf.publish(iq, lds_hdr[(n + 1) & 1], t);
+    } else {
+      pf.finish_now(iq, lds_hdr[(n + 1) & 1], t);
     }
-
-    // ---- write dK and dV: lane holds column D/2 m + 32 dd + li, keys 32 g + 8r + 4hh + q ----
+    // ---- dK and dV of this item, then the next item's first loads ----
+    // The accumulators go to LDS as bf16 rows of dK and dV (one 8-byte store
+    // per 4 columns), so that the global stores are 16 bytes of a row per
+    // lane; the transposed staging buffers are free once the last step has
+    // passed its barrier.
     {
-      // uniform base + opaque 32-bit lane offset + constant: no per-element
-      // 64-bit address is computed ahead and kept live through the loops
-      const long base = (bh * Sk + k0) * D;
-      const uint32_t lane_off = opaque((uint32_t)((32 * g + 4 * hh) * D + D / 2 * m + li));
+      bf16* const tile = lds_t;   // [2 tensors][BK keys][EST]
+      const int krow = 32 * g + li;
 #pragma unroll
       for (int dd = 0; dd < NDH; ++dd)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int jl = 32 * g + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (k0 + jl < Sk) {
-            const uint32_t off = lane_off + (uint32_t)((8 * (v >> 2) + (v & 3)) * D + 32 * dd);
-            a.dk[base + off] = (bf16)dk[dd][v];
-            a.dv[base + off] = (bf16)dv[dd][v];
+        for (int r = 0; r < 4; ++r) {
+          const int col = D / 2 * m + 32 * dd + 8 * r + 4 * hh;
+          bf16x4 xk, xv;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            xk[q] = (bf16)dk[dd][4 * r + q];
+            xv[q] = (bf16)dv[dd][4 * r + q];
           }
+          *reinterpret_cast<bf16x4*>(&tile[krow * EST + col]) = xk;
+          *reinterpret_cast<bf16x4*>(&tile[(BK + krow) * EST + col]) = xv;
         }
     }
-    __syncthreads();   // every thread has read lds_item and finished with LDS
+    __syncthreads();   // the tile and the next item's header are in LDS
+    const BwdItem nxt = bwd_item<D>(a, lds_hdr[(n + 1) & 1]);
+    {
+      // rows past the end of the keys fall outside the buffer range: the
+      // stores are dropped
+      const uint32_t bytes = (uint32_t)Sk * D * 2u;
+      const BufRsrc kout = make_rsrc(a.dk + cur.bh * Sk * (long)D, bytes);
+      const BufRsrc vout = make_rsrc(a.dv + cur.bh * Sk * (long)D, bytes);
+      constexpr int CPR = D / 8;                  // 16-byte chunks per row
+      constexpr int PER = BK * CPR / kBwdThreads; // chunks per thread and tensor
+      static_assert(BK * CPR % kBwdThreads == 0, "whole chunks per thread");
+#pragma unroll
+      for (int tensor = 0; tensor < 2; ++tensor)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int i = (int)t + kBwdThreads * j;
+          const int row = i / CPR, ch = i % CPR;
+          const bf16x8 x = as_bf16x8(&lds_t[(tensor * BK + row) * EST + 8 * ch]);
+          const uint32_t off = ((uint32_t)(k0 + row) * D + 8u * ch) * 2u;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), tensor == 0 ? kout : vout,
+                                                 (int)off, 0, 0);
+        }
+    }
+    if (nxt.idx < n_items) {
+      pf.take(iq, t);
+      preload(nxt);
+    }
+    __syncthreads();   // every wave has read the tile: the staging buffers are free
+    cur = nxt;
   }
   if (t == 0) {
     __threadfence();

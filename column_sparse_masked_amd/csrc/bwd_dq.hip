@@ -47,7 +47,7 @@ struct DqSmem {
   // partial tiles: bit i of hid[g][j] says whether key j of the tile hides
   // row 32 g + i of the query block
   uint32_t hid[BQ / 32][BK];
-  uint32_t item;
+  uint32_t hdr[2][4];   // headers of this and the next work item
 };
 
 // Place of key x inside a K^T row: bits 2 and 3 of the offset within each
@@ -155,17 +155,20 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
   const uint32_t n_items = min(a.counters[kCtrFwdItems], max_items);
   const int Sq = a.Sq, Sk = a.Sk;
 
-  for (;;) {
-    if (t == 0) sm.item = atomicAdd(&a.counters[kCtrDqNext], 1u);
-    __syncthreads();
-    const uint32_t idx = __builtin_amdgcn_readfirstlane(sm.item);
+  const ItemQueue iq{&a.counters[kCtrDqNext], a.queue_q, a.cnt_q, n_items, max_items, a.nQ, a.H, a.Hm, a.nK};
+  if (t == 0) iq.first(sm.hdr[0]);
+  __syncthreads();
+  for (int n = 0;; ++n) {
+    const uint32_t idx = __builtin_amdgcn_readfirstlane(sm.hdr[n & 1][0]);
     if (idx >= n_items) break;
-    const uint32_t it = __builtin_amdgcn_readfirstlane(min(a.queue_q[idx], max_items - 1));
+    const uint32_t it = __builtin_amdgcn_readfirstlane(sm.hdr[n & 1][1]);
+    const int cnt = __builtin_amdgcn_readfirstlane((int)sm.hdr[n & 1][2]);
+    ItemPrefetch pf;
+    pf.take(iq, t);
     const long bh = it / a.nQ;
     const int qb = (int)(it % a.nQ);
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
     const long bhm = (long)b * a.Hm + (a.Hm == 1 ? 0 : h);
-    const int cnt = __builtin_amdgcn_readfirstlane(min(a.cnt_q[bhm * a.nQ + qb], a.nK));
     const uint16_t* lst = a.list_q + (bhm * a.nQ + qb) * (long)a.nK;
     const BufRsrc qbase = make_rsrc(a.q + bh * Sq * (long)D, (uint32_t)Sq * D * 2u);
     const BufRsrc obase = make_rsrc(a.dout + bh * Sq * (long)D, (uint32_t)Sq * D * 2u);
@@ -226,6 +229,7 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
           for (int g = 0; g < BQ / 32; ++g) sm.hid[g][t] = wd[g];
       }
+      pf.stash(sm.hdr[(n + 1) & 1], t);   // the stores above waited for loads issued after the ticket
       if (cnt > 1) dq_load<D>(st, kbase, vbase, block_start(list_entry(lst, 1)), t);
       __syncthreads();
 
@@ -296,6 +300,9 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
               acc[d] = mfma32(as_bf16x8(&sm.kt[(32 * d + li) * KTS + 32 * jb + 16 * t2 + 8 * hh]),
                               dsb[jj][t2], acc[d]);
         }
+        // the next item's header, one scalar load in each of the first two blocks
+        if (tt == 0) pf.fetch_entry(iq, sm.hdr[(n + 1) & 1]);
+        if (tt == 1) pf.fetch_count(iq);
         __syncthreads();   // every wave is done with this block's K^T
         if (has_next) {
           dq_store_kt<D>(st, sm, t);
@@ -303,6 +310,10 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
         }
         e_cur = e_next;
       }
+      if (cnt == 1) pf.fetch_count(iq);
+      pf.publish(iq, sm.hdr[(n + 1) & 1], t);
+    } else {
+      pf.finish_now(iq, sm.hdr[(n + 1) & 1], t);
     }
 
     // ---- dQ = sum of the two key halves' dQ^T, written once in bf16 ----
@@ -332,7 +343,7 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
           *reinterpret_cast<bf16x4*>(&drow[32 * d + 8 * r + 4 * hh]) = x;
         }
     }
-    __syncthreads();   // every thread has read sm.item and red
+    __syncthreads();   // every thread has read red; the next header is in LDS
   }
   // The last workgroup to leave resets the queue counters for the next call.
   if (t == 0) {

@@ -145,6 +145,97 @@ __device__ __forceinline__ ListWord list_word(const uint16_t* lst, int i) {
 }
 __device__ __forceinline__ int list_value(ListWord x) { return (int)((x.word >> x.shift) & 0xffffu); }
 
+// ---- work items, taken one ahead ----
+// The persistent kernels take items from a cost-sorted queue with an atomic
+// ticket.  Reading an item's header only when the item starts costs three
+// dependent memory round trips (ticket, queue entry, tile count) before the
+// item's first load can be issued.  Instead, wave 0 fetches the header of the
+// next item while the current one computes, one dependent step at a time at
+// points a block of work apart, and publishes it in LDS before the barrier
+// that ends the current item.
+typedef __attribute__((address_space(4))) const int const_i32;
+
+struct ItemQueue {
+  uint32_t* ticket;       // next queue position to hand out
+  const uint32_t* queue;  // item ids, heaviest first
+  const int* cnt;         // non-skipped tiles per (b * Hm + hm, block)
+  uint32_t n_items, max_items;
+  int nBlk, H, Hm, cap;   // blocks per head; heads; mask heads; tile count cap
+
+  // index of item `it` (= (b * H + h) * nBlk + blk) in `cnt`
+  __device__ __forceinline__ long cnt_index(uint32_t it) const {
+    const uint32_t bh = it / (uint32_t)nBlk, blk = it % (uint32_t)nBlk;
+    const uint32_t b = bh / (uint32_t)H, h = bh % (uint32_t)H;
+    return ((long)b * Hm + (Hm == 1 ? 0 : (long)h)) * nBlk + blk;
+  }
+  // The first item's header, read directly (thread 0, before the first item).
+  __device__ __forceinline__ void first(uint32_t (&hdr)[4]) const {
+    const uint32_t idx = atomicAdd(ticket, 1u);
+    uint32_t it = 0;
+    int c = 0;
+    if (idx < n_items) {
+      it = min(queue[idx], max_items - 1);
+      c = min(cnt[cnt_index(it)], cap);
+    }
+    hdr[0] = idx;
+    hdr[1] = it;
+    hdr[2] = (uint32_t)c;
+  }
+};
+
+// Fetch of the next item's header, in steps placed far apart in the current
+// item:
+//   take()         top of the item, before its first load: thread 0 takes
+//                  the ticket (a vector atomic, so it returns before any of
+//                  the item's loads and waiting for it costs nothing extra);
+//   stash()        after the item's first wait for its own loads: thread 0
+//                  puts the ticket into the next header slot in LDS;
+//   fetch_entry()  after a barrier, right before another: every wave reads
+//                  the ticket and issues the scalar load of the queue entry;
+//   fetch_count()  right before a later barrier: the scalar load of the
+//                  item's tile count;
+//   publish()      thread 0 writes the header; the barrier that ends the
+//                  current item makes it visible.
+// A scalar load is waited for together with every LDS access in flight, so
+// each one is issued right before a barrier and its value used only after
+// it.  Every wave runs the scalar steps itself (the values are the same), so
+// no branch on the wave index is needed.
+struct ItemPrefetch {
+  uint32_t ticket_v = 0;   // thread 0: the ticket
+  uint32_t idx = 0, item = 0;
+  int cnt = 0;
+
+  __device__ __forceinline__ void take(const ItemQueue& q, unsigned t) {
+    if (t == 0) ticket_v = atomicAdd(q.ticket, 1u);
+  }
+  __device__ __forceinline__ void stash(uint32_t (&hdr)[4], unsigned t) const {
+    if (t == 0) hdr[3] = ticket_v;
+  }
+  __device__ __forceinline__ void fetch_entry(const ItemQueue& q, const uint32_t (&hdr)[4]) {
+    idx = __builtin_amdgcn_readfirstlane(hdr[3]);
+    item = *(const_u32*)(q.queue + min(idx, q.max_items - 1));   // raw until fetch_count
+  }
+  __device__ __forceinline__ void fetch_count(const ItemQueue& q) {
+    item = min(item, q.max_items - 1);
+    cnt = *(const_i32*)(q.cnt + q.cnt_index(item));              // raw until publish
+  }
+  __device__ __forceinline__ void publish(const ItemQueue& q, uint32_t (&hdr)[4], unsigned t) const {
+    if (t == 0) {
+      hdr[0] = idx;
+      hdr[1] = item;
+      hdr[2] = (uint32_t)min(cnt, q.cap);
+    }
+  }
+  // all steps after take() at once, for an item without blocks of work
+  __device__ __forceinline__ void finish_now(const ItemQueue& q, uint32_t (&hdr)[4], unsigned t) {
+    stash(hdr, t);
+    __syncthreads();
+    fetch_entry(q, hdr);
+    fetch_count(q);
+    publish(q, hdr, t);
+  }
+};
+
 __device__ __forceinline__ const bf16x8& as_bf16x8(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }

@@ -34,7 +34,7 @@ struct alignas(16) FwdSmem {
   // partial tiles (key blocks t even / odd): bit i of hid[.][g][j] says
   // whether key j hides row 32 g + i of the query block
   uint32_t hid[2][BQ / 32][BK];
-  uint32_t item;
+  uint32_t hdr[2][4];   // headers of this and the next work item
 };
 
 // Place of key x (0 <= x < BK) inside a V^T row: bits 2 and 3 of the offset
@@ -148,19 +148,22 @@ void attn_fwd_kernel(const FwdArgs a) {
   const uint32_t n_items = min(a.counters[kCtrFwdItems], max_items);
   const int Sq = a.Sq, Sk = a.Sk;
 
-  for (;;) {
-    if (t == 0) sm.item = atomicAdd(&a.counters[kCtrFwdNext], 1u);
-    __syncthreads();
+  const ItemQueue iq{&a.counters[kCtrFwdNext], a.queue, a.cnt_q, n_items, max_items, a.nQ, a.H, a.Hm, a.nK};
+  if (t == 0) iq.first(sm.hdr[0]);
+  __syncthreads();
+  for (int n = 0;; ++n) {
     // the item is the same for the whole workgroup: keep it (and everything
     // derived from it) in scalar registers
-    const uint32_t idx = __builtin_amdgcn_readfirstlane(sm.item);
+    const uint32_t idx = __builtin_amdgcn_readfirstlane(sm.hdr[n & 1][0]);
     if (idx >= n_items) break;
-    const uint32_t it = min(a.queue[idx], max_items - 1);
+    const uint32_t it = __builtin_amdgcn_readfirstlane(sm.hdr[n & 1][1]);
+    const int cnt = __builtin_amdgcn_readfirstlane((int)sm.hdr[n & 1][2]);
+    ItemPrefetch pf;
+    pf.take(iq, t);
     const long bh = it / a.nQ;
     const int qb = (int)(it % a.nQ);
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
     const long bhm = (long)b * a.Hm + (a.Hm == 1 ? 0 : h);
-    const int cnt = min(a.cnt_q[bhm * a.nQ + qb], a.nK);
     const uint16_t* lst = a.list_q + (bhm * a.nQ + qb) * (long)a.nK;
     // buffer resources over this head's Q, K, V and bounds: loads past the
     // end of the rows return zeros
@@ -215,6 +218,7 @@ void attn_fwd_kernel(const FwdArgs a) {
           for (int g = 0; g < BQ / 32; ++g) sm.hid[0][g][t] = wd[g];
         }
       }
+      pf.stash(sm.hdr[(n + 1) & 1], t);   // the stores above waited for loads issued after the ticket
       if (cnt > 1) load_k<D>(st, kbase, block_start(e_next), t);
       __syncthreads();
 
@@ -342,6 +346,9 @@ void attn_fwd_kernel(const FwdArgs a) {
           for (int g = 0; g < BQ / 32; ++g) sm.hid[(tt + 1) & 1][g][t] = wd[g];
         }
 
+        // the next item's header, one scalar load in each of the first two blocks
+        if (tt == 0) pf.fetch_entry(iq, sm.hdr[(n + 1) & 1]);
+        if (tt == 1) pf.fetch_count(iq);
         __syncthreads();   // every wave is done with this block's V^T; K_{t+1} is in LDS
         if (has_next) {
           store_vt<D>(st, sm.vt, t);
@@ -354,6 +361,10 @@ void attn_fwd_kernel(const FwdArgs a) {
           e_next = e2;
         }
       }
+      if (cnt == 1) pf.fetch_count(iq);
+      pf.publish(iq, sm.hdr[(n + 1) & 1], t);
+    } else {
+      pf.finish_now(iq, sm.hdr[(n + 1) & 1], t);
     }
 
     // ---- finalise: O = acc / l, LSE = (m + log2 l) ln 2 ----
@@ -372,7 +383,7 @@ void attn_fwd_kernel(const FwdArgs a) {
         }
       if (hh == 0) a.lse[bh * Sq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : INFINITY;
     }
-    __syncthreads();   // every thread has read sm.item and finished with LDS
+    __syncthreads();   // every thread has finished with LDS; the next header is in LDS
   }
   // The last workgroup to leave resets the queue counters for the next call.
   if (t == 0) {
