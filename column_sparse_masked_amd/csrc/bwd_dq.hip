@@ -257,12 +257,14 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
             s[v] = 0.f;
             dp[v] = 0.f;
           }
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int kk = 0; kk < NS; ++kk) {
             const int off = (32 * jb + li) * KST + 16 * kk + 8 * hh;
             s = mfma32(as_bf16x8(&sm.u.kv.k[off]), qf[kk], s);
             dp = mfma32(as_bf16x8(&sm.u.kv.v[off]), of[kk], dp);
           }
+          __builtin_amdgcn_s_setprio(0);
           // ---- dS^T = P (dP scale - Delta scale), P = exp2(S scale log2 e - LSE log2 e) ----
           if (need_mask) {
 #pragma unroll

@@ -252,11 +252,13 @@ void attn_fwd_kernel(const FwdArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) s[j][v] = 0.f;
           // k-step major: the two accumulators advance together
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int kk = 0; kk < NS; ++kk)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
               s[j] = mfma32(as_bf16x8(&sm.k[(32 * (2 * hk + j) + li) * KST + 16 * kk + 8 * hh]), qf[kk], s[j]);
+          __builtin_amdgcn_s_setprio(0);
           if (need_mask) {
             // words of 4 consecutive keys for this wave's 32 rows; bit li is
             // this lane's row
