@@ -46,23 +46,32 @@ __device__ __forceinline__ int vt_pos(int x) { return (x & ~15) | perm16(x & 15)
 //   K: thread t holds column chunk t % CPR (8 head-dim values) of the NK
 //      consecutive rows NK*(t / CPR) ...  (loads and LDS stores then differ
 //      only by constant offsets);
-//   V: thread t holds 4*NV consecutive keys x column chunk (t/8) % CPR, with
-//      the key range chosen so that the transposed 8-byte LDS stores of 16
-//      neighbouring lanes fall on distinct banks.
+//   V: units of 4 consecutive keys x 8 head-dim columns, unit p = t + 256 j
+//      (j < NV) at key-unit 16 ((p / 64) / (CPR / 4)) + p % 16 and chunk
+//      stage_chunk(p % 64, (p / 64) % (CPR / 4)): the staging map that keeps
+//      the transposed 8-byte LDS stores free of bank conflicts (the 16 lanes
+//      served together write 16 distinct 8-byte places of rows that start on
+//      the same bank).
 template <int D>
 struct Stage {
   static constexpr int CPR = D / 8;               // 16-byte chunks per row
   static constexpr int NK = BK * CPR / 256;       // K rows per thread
-  static constexpr int NV = (BK / 4) * CPR / 256; // V key groups (of 4) per thread
+  static constexpr int NV = (BK / 4) * CPR / 256; // V units per thread
+  static_assert(CPR % 4 == 0 && ((BK / 4) * CPR) % 256 == 0, "whole V units per thread");
   bf16x8 k[NK];
   bf16x8 v[4 * NV];
 
   static __device__ __forceinline__ int k_row(unsigned t) { return NK * (int)(t / CPR); }
   static __device__ __forceinline__ int k_col(unsigned t) { return (int)(t % CPR); }
-  static __device__ __forceinline__ int v_key(unsigned t) {
-    return 4 * NV * (int)((t & 7u) + 8u * (t / (8u * CPR)));
+  // first key and column chunk of V unit j of thread t
+  static __device__ __forceinline__ int v_key(unsigned t, int j) {
+    const int p = (int)t + 256 * j;
+    return 4 * (16 * ((p >> 6) / (CPR / 4)) + stage_row_unit(p & 63));
   }
-  static __device__ __forceinline__ int v_col(unsigned t) { return (int)((t >> 3) % CPR); }
+  static __device__ __forceinline__ int v_col(unsigned t, int j) {
+    const int p = (int)t + 256 * j;
+    return stage_chunk(p & 63, (p >> 6) % (CPR / 4));
+  }
 };
 
 template <int D>
@@ -85,18 +94,23 @@ __device__ __forceinline__ void store_k(const Stage<D>& r, bf16* sk, unsigned t)
 template <int D>
 __device__ __forceinline__ void load_v(Stage<D>& r, BufRsrc vb, int k0, unsigned t) {
   using S = Stage<D>;
-  const uint32_t base = opaque(((uint32_t)S::v_key(t) * S::CPR + S::v_col(t)) * 16u) + (uint32_t)k0 * (D * 2);
 #pragma unroll
-  for (int q = 0; q < 4 * S::NV; ++q) r.v[q] = buf_load16(vb, base + (uint32_t)q * (D * 2));
+  for (int j = 0; j < S::NV; ++j) {
+    const uint32_t base =
+        opaque(((uint32_t)S::v_key(t, j) * S::CPR + S::v_col(t, j)) * 16u) + (uint32_t)k0 * (D * 2);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) r.v[4 * j + rr] = buf_load16(vb, base + (uint32_t)rr * (D * 2));
+  }
 }
 
 template <int D>
 __device__ __forceinline__ void store_vt(const Stage<D>& r, bf16* vt, unsigned t) {
   using S = Stage<D>;
   constexpr int VTS = FwdSmem<D>::VTS;
+  static_assert((8 * VTS * 2) % 128 == 0, "8 transposed rows start on the same bank");
 #pragma unroll
   for (int i = 0; i < S::NV; ++i) {
-    bf16* dst = vt + opaque((8 * S::v_col(t)) * VTS + vt_pos(S::v_key(t) + 4 * i));
+    bf16* dst = vt + opaque((8 * S::v_col(t, i)) * VTS + vt_pos(S::v_key(t, i)));
     // 4 keys x 8 columns -> 8 rows of 4 keys (constant shuffles only, so the
     // compiler keeps everything in registers)
     const bf16x16 p01 = __builtin_shufflevector(r.v[4 * i], r.v[4 * i + 1], 0, 8, 1, 9, 2, 10, 3,
