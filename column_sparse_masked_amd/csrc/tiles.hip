@@ -222,19 +222,25 @@ __global__ __launch_bounds__(kQueueThreads) void queue_kernel(
     const int* __restrict__ cnt_q, const int* __restrict__ cnt_k, uint32_t* __restrict__ fwd_q,
     uint32_t* __restrict__ bwd_q, uint32_t* __restrict__ counters, int B, int H, int Hm, int nQ,
     int nK) {
+  // workgroup 0 sorts the forward (and dQ) queue, workgroup 1 the backward one
   __shared__ int hist[kBuckets];
   __shared__ int scratch[kQueueThreads / 64 + 1];
-  if (nQ > 0) sort_items(cnt_q, fwd_q, B, H, Hm, nQ, hist, scratch);
-  if (nK > 0) sort_items(cnt_k, bwd_q, B, H, Hm, nK, hist, scratch);
-  if (threadIdx.x == 0) {
-    counters[kCtrFwdItems] = (uint32_t)((long)B * H * nQ);
-    counters[kCtrBwdItems] = (uint32_t)((long)B * H * nK);
-    counters[kCtrFwdNext] = 0;
-    counters[kCtrBwdNext] = 0;
-    counters[kCtrFwdExit] = 0;
-    counters[kCtrBwdExit] = 0;
-    counters[kCtrDqNext] = 0;
-    counters[kCtrDqExit] = 0;
+  if (blockIdx.x == 0) {
+    if (nQ > 0) sort_items(cnt_q, fwd_q, B, H, Hm, nQ, hist, scratch);
+    if (threadIdx.x == 0) {
+      counters[kCtrFwdItems] = (uint32_t)((long)B * H * nQ);
+      counters[kCtrFwdNext] = 0;
+      counters[kCtrFwdExit] = 0;
+      counters[kCtrDqNext] = 0;
+      counters[kCtrDqExit] = 0;
+    }
+  } else {
+    if (nK > 0) sort_items(cnt_k, bwd_q, B, H, Hm, nK, hist, scratch);
+    if (threadIdx.x == 0) {
+      counters[kCtrBwdItems] = (uint32_t)((long)B * H * nK);
+      counters[kCtrBwdNext] = 0;
+      counters[kCtrBwdExit] = 0;
+    }
   }
 }
 
@@ -250,7 +256,7 @@ hipError_t launch_tile_bounds(const TileArgs& a, hipStream_t stream) {
   // always, also for empty problems: it leaves (empty) queues and zeroed
   // counters behind, with a kernel rather than a memset, which stays correct
   // when a caller replays the calls as a captured graph
-  queue_kernel<<<1, kQueueThreads, 0, stream>>>(a.cnt_q, a.cnt_k, a.fwd_queue, a.bwd_queue,
+  queue_kernel<<<2, kQueueThreads, 0, stream>>>(a.cnt_q, a.cnt_k, a.fwd_queue, a.bwd_queue,
                                                 a.counters, a.B, a.H, a.Hm, a.nQ, a.nK);
   return hipGetLastError();
 }
