@@ -246,7 +246,7 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   if (!has_rows) {
     // no query rows: every key gets zero gradient
     const size_t bytes = (size_t)p->batch * p->heads * p->seqlen_k * p->head_dim * 2;
-    if (hipMemsetAsync(dk, 0, bytes, s) != hipSuccess || hipMemsetAsync(dv, 0, bytes, s) != hipSuccess)
+    if (fm::launch_zero16(dk, bytes, s) != hipSuccess || fm::launch_zero16(dv, bytes, s) != hipSuccess)
       return FM_ERR_HIP;
     return FM_OK;
   }

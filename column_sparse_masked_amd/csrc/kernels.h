@@ -73,6 +73,8 @@ hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t
 hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, int dq_grid,
                            hipStream_t stream, const KernelEvents& ev);
 hipError_t launch_attn_bwd_dq(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
+// Zero-fills `bytes` (a multiple of 16) at the 16-byte aligned `p`.
+hipError_t launch_zero16(void* p, size_t bytes, hipStream_t stream);
 
 // Workgroups per compute unit the persistent kernels are sized for.
 int fwd_blocks_per_cu(int head_dim);

@@ -244,6 +244,22 @@ __global__ __launch_bounds__(kQueueThreads) void queue_kernel(
   }
 }
 
+// Zero-fill of n16 16-byte words (a kernel rather than a memset, which stays
+// correct when a caller captures the call into a graph).  Used by the
+// backward when there are no query rows.
+__global__ __launch_bounds__(256) void zero16_kernel(uint4* __restrict__ p, long n16) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n16; i += (long)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_zero16(void* p, size_t bytes, hipStream_t stream) {
+  const long n16 = (long)(bytes / 16);
+  if (n16 <= 0) return hipSuccess;
+  const long blocks = (n16 + 255) / 256;
+  zero16_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(static_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
 hipError_t launch_tile_bounds(const TileArgs& a, hipStream_t stream) {
   const unsigned bhm = (unsigned)((long)a.B * a.Hm);
   if (bhm > 0 && a.nK > 0) {
