@@ -57,7 +57,8 @@ class TileinfoLayout(ctypes.Structure):
                 ("cls", ctypes.c_size_t), ("cnt_q", ctypes.c_size_t),
                 ("cnt_k", ctypes.c_size_t), ("list_q", ctypes.c_size_t),
                 ("list_k", ctypes.c_size_t), ("fwd_queue", ctypes.c_size_t),
-                ("bwd_queue", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+                ("bwd_queue", ctypes.c_size_t), ("fwd_partials", ctypes.c_size_t),
+                ("total", ctypes.c_size_t)]
 
 
 _P = ctypes.POINTER(Problem)

@@ -35,8 +35,22 @@ fm_status check_problem(const fm_problem* p) {
 
 struct Layout {
   int nQ, nK;
-  size_t counters, kbsum, cls, cnt_q, cnt_k, list_q, list_k, fwd_queue, bwd_queue, total;
+  int split_cap;   // forward items that may be split in two
+  size_t counters, kbsum, cls, cnt_q, cnt_k, list_q, list_k, fwd_queue, bwd_queue, fwd_partials, total;
 };
+
+// At most this many forward items are split (two partial-result slots each).
+constexpr long kMaxSplitItems = 512;
+
+// Forward items may be split only when there are fewer than four per
+// workgroup of the forward's persistent grid: with more, the longest-first
+// order already balances the grid, and the kernel without split handling
+// runs.  fm_tile_bounds and fm_attn_fwd take the same decision.
+int split_cap_for(const fm_problem* p, const Layout& L, int cus) {
+  const long items = (long)p->batch * p->heads * L.nQ;
+  const long slots = (long)cus * fm::fwd_blocks_per_cu(p->head_dim);
+  return items < 4 * slots ? L.split_cap : 0;
+}
 
 Layout make_layout(const fm_problem* p) {
   Layout L;
@@ -53,6 +67,10 @@ Layout make_layout(const fm_problem* p) {
   L.list_k = off;    off = align256(off + bhm * L.nK * L.nQ * sizeof(uint16_t));
   L.fwd_queue = off; off = align256(off + bh * L.nQ * sizeof(uint32_t));
   L.bwd_queue = off; off = align256(off + bh * L.nK * sizeof(uint32_t));
+  const long items_q = (long)bh * L.nQ;
+  L.split_cap = (int)(items_q < kMaxSplitItems ? items_q : kMaxSplitItems);
+  L.fwd_partials = off;
+  off = align256(off + (size_t)2 * L.split_cap * fm::BQ * ((size_t)p->head_dim * 2 + sizeof(float)));
   L.total = off;
   return L;
 }
@@ -128,6 +146,7 @@ fm_status fm_tileinfo_layout_query(const fm_problem* p, fm_tileinfo_layout* out)
   out->list_k = L.list_k;
   out->fwd_queue = L.fwd_queue;
   out->bwd_queue = L.bwd_queue;
+  out->fwd_partials = L.fwd_partials;
   out->total = L.total;
   return FM_OK;
 }
@@ -181,6 +200,10 @@ fm_status fm_tile_bounds(const fm_problem* p, const int32_t* bounds, void* tilei
   a.counters = at<uint32_t>(tileinfo, L.counters);
   a.B = p->batch; a.H = p->heads; a.Hm = p->mask_heads;
   a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
+  int cus = 0;
+  if ((st = cu_count(&cus)) != FM_OK) return st;
+  a.fwd_slots = cus * fm::fwd_blocks_per_cu(p->head_dim);
+  a.split_cap = split_cap_for(p, L, cus);
   return fm::launch_tile_bounds(a, (hipStream_t)stream) == hipSuccess ? FM_OK : FM_ERR_HIP;
 }
 
@@ -211,12 +234,16 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
   a.cnt_q = at<int>(tileinfo, L.cnt_q);
   a.queue = at<uint32_t>(tileinfo, L.fwd_queue);
   a.counters = at<uint32_t>(tileinfo, L.counters);
+  a.partials = at<float>(tileinfo, L.fwd_partials);
+  a.split_cap = split_cap_for(p, L, cus);
   a.B = p->batch; a.H = p->heads; a.Hm = p->mask_heads;
   a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
   a.scale_log2 = p->softmax_scale * fm::kLog2e;
+  // tickets: every item, plus a second one for each item that may be split
   const long items = (long)p->batch * p->heads * L.nQ;
+  const long tickets = items + (items < a.split_cap ? items : a.split_cap);
   const long slots = (long)cus * fm::fwd_blocks_per_cu(p->head_dim);
-  const int grid = (int)(items < slots ? items : slots);
+  const int grid = (int)(tickets < slots ? tickets : slots);
   return fm::launch_attn_fwd(a, p->head_dim, grid, (hipStream_t)stream, g_events) == hipSuccess
              ? FM_OK
              : FM_ERR_HIP;

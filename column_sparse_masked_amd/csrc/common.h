@@ -15,7 +15,8 @@ constexpr int kListIndex = 0x7fff;
 
 // counters[] slots inside the tileinfo buffer
 constexpr int kCtrFwdItems = 0, kCtrBwdItems = 1, kCtrFwdNext = 2, kCtrBwdNext = 3,
-              kCtrFwdExit = 4, kCtrBwdExit = 5, kCtrDqNext = 6, kCtrDqExit = 7;
+              kCtrFwdExit = 4, kCtrBwdExit = 5, kCtrDqNext = 6, kCtrDqExit = 7,
+              kCtrFwdSplit = 8;   // forward items split in two (the first of the queue)
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -161,6 +162,14 @@ struct ItemQueue {
   const int* cnt;         // non-skipped tiles per (b * Hm + hm, block)
   uint32_t n_items, max_items;
   int nBlk, H, Hm, cap;   // blocks per head; heads; mask heads; tile count cap
+  // The first nsplit queue entries are taken twice (two halves of their key
+  // blocks): ticket v < 2 nsplit is entry v / 2, ticket v >= 2 nsplit entry
+  // v - nsplit; n_items counts tickets.
+  uint32_t nsplit = 0;
+
+  __device__ __forceinline__ uint32_t position(uint32_t v) const {
+    return v < 2 * nsplit ? v >> 1 : v - nsplit;
+  }
 
   // index of item `it` (= (b * H + h) * nBlk + blk) in `cnt`
   __device__ __forceinline__ long cnt_index(uint32_t it) const {
@@ -174,7 +183,7 @@ struct ItemQueue {
     uint32_t it = 0;
     int c = 0;
     if (idx < n_items) {
-      it = min(queue[idx], max_items - 1);
+      it = min(queue[position(idx)], max_items - 1);
       c = min(cnt[cnt_index(it)], cap);
     }
     hdr[0] = idx;
@@ -213,7 +222,7 @@ struct ItemPrefetch {
   }
   __device__ __forceinline__ void fetch_entry(const ItemQueue& q, const uint32_t (&hdr)[4]) {
     idx = __builtin_amdgcn_readfirstlane(hdr[3]);
-    item = *(const_u32*)(q.queue + min(idx, q.max_items - 1));   // raw until fetch_count
+    item = *(const_u32*)(q.queue + min(q.position(idx), q.max_items - 1));   // raw until fetch_count
   }
   __device__ __forceinline__ void fetch_count(const ItemQueue& q) {
     item = min(item, q.max_items - 1);

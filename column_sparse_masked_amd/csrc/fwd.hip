@@ -145,7 +145,10 @@ __device__ __forceinline__ void hidden_rows(const int4 bd, int q0, uint32_t (&wd
   }
 }
 
-template <int D>
+// SPLIT: whether items may be split in two (the instance without is used
+// when the problem has enough items per workgroup for the longest-first
+// order to balance the grid; its code has none of the split handling).
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const FwdArgs a) {
   constexpr int NS = D / 16;   // k-steps over the head dimension
@@ -159,10 +162,15 @@ void attn_fwd_kernel(const FwdArgs a) {
   // item count and queue entries are range-checked so that a stale or foreign
   // tileinfo cannot make the kernel read outside its tensors
   const uint32_t max_items = (uint32_t)((long)a.B * a.H * a.nQ);
-  const uint32_t n_items = min(a.counters[kCtrFwdItems], max_items);
+  const uint32_t n_real = min(a.counters[kCtrFwdItems], max_items);
+  // the first nsplit items of the queue are taken as two halves each
+  const uint32_t nsplit =
+      SPLIT ? min(min(a.counters[kCtrFwdSplit], (uint32_t)max(a.split_cap, 0)), n_real) : 0u;
+  const uint32_t n_items = n_real + nsplit;
   const int Sq = a.Sq, Sk = a.Sk;
 
-  const ItemQueue iq{&a.counters[kCtrFwdNext], a.queue, a.cnt_q, n_items, max_items, a.nQ, a.H, a.Hm, a.nK};
+  const ItemQueue iq{&a.counters[kCtrFwdNext], a.queue, a.cnt_q, n_items, max_items, a.nQ, a.H, a.Hm, a.nK,
+                     nsplit};
   if (t == 0) iq.first(sm.hdr[0]);
   __syncthreads();
   for (int n = 0;; ++n) {
@@ -171,14 +179,19 @@ void attn_fwd_kernel(const FwdArgs a) {
     const uint32_t idx = __builtin_amdgcn_readfirstlane(sm.hdr[n & 1][0]);
     if (idx >= n_items) break;
     const uint32_t it = __builtin_amdgcn_readfirstlane(sm.hdr[n & 1][1]);
-    const int cnt = __builtin_amdgcn_readfirstlane((int)sm.hdr[n & 1][2]);
+    const int cnt_all = __builtin_amdgcn_readfirstlane((int)sm.hdr[n & 1][2]);
+    // a split item's ticket 2 j + p takes half p of its list of key blocks
+    const bool split = SPLIT && idx < 2 * nsplit;
+    const int half = (cnt_all + 1) >> 1;
+    const int first = split && (idx & 1u) ? half : 0;
+    const int cnt = split ? ((idx & 1u) ? cnt_all - half : half) : cnt_all;
     ItemPrefetch pf;
     pf.take(iq, t);
     const long bh = it / a.nQ;
     const int qb = (int)(it % a.nQ);
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
     const long bhm = (long)b * a.Hm + (a.Hm == 1 ? 0 : h);
-    const uint16_t* lst = a.list_q + (bhm * a.nQ + qb) * (long)a.nK;
+    const uint16_t* lst = a.list_q + (bhm * a.nQ + qb) * (long)a.nK + first;
     // buffer resources over this head's Q, K, V and bounds: loads past the
     // end of the rows return zeros
     const BufRsrc qbase = make_rsrc(a.q + bh * Sq * (long)D, (uint32_t)Sq * D * 2u);
@@ -383,9 +396,27 @@ void attn_fwd_kernel(const FwdArgs a) {
       pf.finish_now(iq, sm.hdr[(n + 1) & 1], t);
     }
 
-    // ---- finalise: O = acc / l, LSE = (m + log2 l) ln 2 ----
+    // ---- finalise: O = acc / l, LSE = (m + log2 l) ln 2.  A split item's
+    // half writes the same, its own O and LSE, into its slot for the merge ----
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (qrow < Sq) {
+    if (split) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const int r = qrow - qb * BQ;   // row within the block
+      bf16* orow = reinterpret_cast<bf16*>(a.partials) + ((size_t)idx * BQ + r) * D;
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          bf16x4 ov;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ov[q] = (bf16)(acc[d][4 * rr + q] * inv);
+          *reinterpret_cast<bf16x4*>(&orow[32 * d + 8 * rr + 4 * hh]) = ov;
+        }
+      if (hh == 0) {
+        float* plse = reinterpret_cast<float*>(reinterpret_cast<bf16*>(a.partials) + (size_t)2 * a.split_cap * (BQ * D));
+        plse[(size_t)idx * BQ + r] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : INFINITY;
+      }
+    } else if (qrow < Sq) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       bf16* orow = a.o + (bh * Sq + qrow) * D;
 #pragma unroll
@@ -414,16 +445,76 @@ void attn_fwd_kernel(const FwdArgs a) {
 
 int fwd_blocks_per_cu(int) { return 2; }
 
+// Merge of the two halves of each split item (FlashMask-3 paper summary,
+// abstract: softmax results over disjoint key ranges combine exactly through
+// their log-sum-exps).  Each half left its own O_p (bf16) and LSE_p (+inf
+// when the row sees no key of the half).  With M the larger finite LSE_p and
+// w_p = exp(LSE_p - M) (0 for an empty half):
+//   O = (w_0 O_0 + w_1 O_1) / (w_0 + w_1),  LSE = M + log(w_0 + w_1),
+// and O = 0, LSE = +inf when both halves are empty.  Workgroup j merges
+// split item j; thread t takes row t / 2 and half t % 2 of its columns.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(const FwdArgs a) {
+  const uint32_t max_items = (uint32_t)((long)a.B * a.H * a.nQ);
+  const uint32_t n_real = min(a.counters[kCtrFwdItems], max_items);
+  const uint32_t nsplit = min(min(a.counters[kCtrFwdSplit], (uint32_t)max(a.split_cap, 0)), n_real);
+  const bf16* po = reinterpret_cast<const bf16*>(a.partials);
+  const float* pl = reinterpret_cast<const float*>(po + (size_t)2 * a.split_cap * (BQ * D));
+  const int t = threadIdx.x, r = t >> 1, c0 = (t & 1) * (D / 2);
+  for (uint32_t j = blockIdx.x; j < nsplit; j += gridDim.x) {
+    const uint32_t it = min(a.queue[j], max_items - 1);
+    const long bh = it / a.nQ;
+    const int row = (int)(it % a.nQ) * BQ + r;
+    if (row >= a.Sq) continue;
+    const float L0 = pl[(size_t)(2 * j) * BQ + r], L1 = pl[(size_t)(2 * j + 1) * BQ + r];
+    const bool e0 = !(L0 < INFINITY), e1 = !(L1 < INFINITY);
+    const float M = e0 ? L1 : e1 ? L0 : fmaxf(L0, L1);
+    const float w0 = e0 ? 0.f : __expf(L0 - M), w1 = e1 ? 0.f : __expf(L1 - M);
+    const float wsum = w0 + w1;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const bf16* o0 = po + ((size_t)(2 * j) * BQ + r) * D;
+    const bf16* o1 = po + ((size_t)(2 * j + 1) * BQ + r) * D;
+    bf16* orow = a.o + (bh * a.Sq + row) * D;
+#pragma unroll
+    for (int c = c0; c < c0 + D / 2; c += 8) {
+      const bf16x8 x = as_bf16x8(o0 + c), y = as_bf16x8(o1 + c);
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (bf16)(((float)x[e] * w0 + (float)y[e] * w1) * inv);
+      *reinterpret_cast<bf16x8*>(&orow[c]) = o;
+    }
+    if ((t & 1) == 0) a.lse[bh * a.Sq + row] = wsum > 0.f ? M + __logf(wsum) : INFINITY;
+  }
+}
+
 hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream,
                            const KernelEvents& ev) {
   hipError_t err;
   if (ev.begin && (err = hipEventRecord(ev.begin, stream)) != hipSuccess) return err;
-  if (head_dim == 128)
-    attn_fwd_kernel<128><<<grid, 256, 0, stream>>>(a);
-  else
-    attn_fwd_kernel<64><<<grid, 256, 0, stream>>>(a);
+  const bool split = a.split_cap > 0;
+  if (head_dim == 128) {
+    if (split)
+      attn_fwd_kernel<128, true><<<grid, 256, 0, stream>>>(a);
+    else
+      attn_fwd_kernel<128, false><<<grid, 256, 0, stream>>>(a);
+  } else {
+    if (split)
+      attn_fwd_kernel<64, true><<<grid, 256, 0, stream>>>(a);
+    else
+      attn_fwd_kernel<64, false><<<grid, 256, 0, stream>>>(a);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ev.end && (err = hipEventRecord(ev.end, stream)) != hipSuccess) return err;
+  if (a.split_cap > 0 && grid > 0) {
+    // the number of split items is on the device: one workgroup per
+    // possible split item, up to the grid size, each looping
+    const int mgrid = a.split_cap < grid ? a.split_cap : grid;
+    if (head_dim == 128)
+      fwd_merge_kernel<128><<<mgrid, 256, 0, stream>>>(a);
+    else
+      fwd_merge_kernel<64><<<mgrid, 256, 0, stream>>>(a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   return hipSuccess;
 }
 

@@ -18,6 +18,8 @@ struct TileArgs {
   uint32_t* bwd_queue;
   uint32_t* counters;
   int B, H, Hm, Sq, Sk, nQ, nK;
+  int fwd_slots;   // workgroups of the forward's persistent grid
+  int split_cap;   // forward items that may be split (partial-result slots / 2)
 };
 
 struct FwdArgs {
@@ -31,6 +33,8 @@ struct FwdArgs {
   const int* cnt_q;
   const uint32_t* queue;
   uint32_t* counters;
+  float* partials;    // bf16 O [2 split_cap][BQ][D], then fp32 LSE [2 split_cap][BQ]: halves of split items
+  int split_cap;
   int B, H, Hm, Sq, Sk, nQ, nK;
   float scale_log2;   // softmax_scale * log2(e)
 };

@@ -176,8 +176,35 @@ __device__ int block_exclusive_scan(int x, int* scratch, int* total) {
 
 // Counting sort of n items by tile count, descending.  Item it = bh*nBlk+blk
 // has count cnt[(b*Hm + hm)*nBlk + blk].  Order inside a count is arbitrary.
+// Sum over the workgroup of one 64-bit value per thread (every thread gets it).
+__device__ long block_sum(long x, long* scratch) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  if (lane == 0) scratch[wave] = x;
+  __syncthreads();
+  long total = 0;
+  for (int w = 0; w < kQueueThreads / 64; ++w) total += scratch[w];
+  __syncthreads();
+  return total;
+}
+
+// Which forward items to split (split != nullptr: the forward queue).  The
+// forward is a persistent grid of fwd_slots workgroups taking items longest
+// first; when few items share a workgroup, the longest ones set the end of
+// the kernel.  Items with more than max(16, ceil(total / (2 fwd_slots)))
+// tiles (half the mean load of a workgroup) are split in two halves of their
+// key blocks, at most split_cap of them; they are the first entries of the
+// sorted queue.  Counted from the histogram of tile counts, which is exact
+// below the top bucket; with any item in the top bucket nothing is split.
+struct SplitRule {
+  int fwd_slots, split_cap;
+  uint32_t* out;
+  long* scratch;   // kQueueThreads / 64 longs
+};
+
 __device__ void sort_items(const int* __restrict__ cnt, uint32_t* __restrict__ queue, int B,
-                           int H, int Hm, int nBlk, int* hist, int* scratch) {
+                           int H, int Hm, int nBlk, int* hist, int* scratch, const SplitRule* split) {
   const int t = threadIdx.x;
   const long n = (long)B * H * nBlk;
   for (int i = t; i < kBuckets; i += kQueueThreads) hist[i] = 0;
@@ -190,6 +217,20 @@ __device__ void sort_items(const int* __restrict__ cnt, uint32_t* __restrict__ q
     atomicAdd(&hist[min(c, kBuckets - 1)], 1);
   }
   __syncthreads();
+  if (split) {
+    long tiles = 0;
+    for (int i = t; i < kBuckets - 1; i += kQueueThreads) tiles += (long)i * hist[i];
+    const long total = block_sum(tiles, split->scratch);
+    const long slots = max(split->fwd_slots, 1);
+    const long thr = max(16L, (total + 2 * slots - 1) / (2 * slots));
+    long above = 0;
+    for (int i = t; i < kBuckets - 1; i += kQueueThreads) above += i > thr ? hist[i] : 0;
+    above = block_sum(above, split->scratch);
+    if (t == 0)
+      *split->out = (hist[kBuckets - 1] > 0 || thr >= kBuckets - 1)
+                        ? 0u
+                        : (uint32_t)min(above, (long)max(split->split_cap, 0));
+  }
   // thread t owns buckets kBuckets-1-4t ... kBuckets-4-4t (descending order)
   constexpr int per = kBuckets / kQueueThreads;
   int local[per];
@@ -221,21 +262,27 @@ __device__ void sort_items(const int* __restrict__ cnt, uint32_t* __restrict__ q
 __global__ __launch_bounds__(kQueueThreads) void queue_kernel(
     const int* __restrict__ cnt_q, const int* __restrict__ cnt_k, uint32_t* __restrict__ fwd_q,
     uint32_t* __restrict__ bwd_q, uint32_t* __restrict__ counters, int B, int H, int Hm, int nQ,
-    int nK) {
+    int nK, int fwd_slots, int split_cap) {
   // workgroup 0 sorts the forward (and dQ) queue, workgroup 1 the backward one
   __shared__ int hist[kBuckets];
   __shared__ int scratch[kQueueThreads / 64 + 1];
+  __shared__ long lscratch[kQueueThreads / 64];
   if (blockIdx.x == 0) {
-    if (nQ > 0) sort_items(cnt_q, fwd_q, B, H, Hm, nQ, hist, scratch);
+    __shared__ uint32_t nsplit;
+    if (threadIdx.x == 0) nsplit = 0;
+    const SplitRule rule{fwd_slots, split_cap, &nsplit, lscratch};
+    if (nQ > 0) sort_items(cnt_q, fwd_q, B, H, Hm, nQ, hist, scratch, split_cap > 0 ? &rule : nullptr);
+    __syncthreads();
     if (threadIdx.x == 0) {
       counters[kCtrFwdItems] = (uint32_t)((long)B * H * nQ);
+      counters[kCtrFwdSplit] = nsplit;
       counters[kCtrFwdNext] = 0;
       counters[kCtrFwdExit] = 0;
       counters[kCtrDqNext] = 0;
       counters[kCtrDqExit] = 0;
     }
   } else {
-    if (nK > 0) sort_items(cnt_k, bwd_q, B, H, Hm, nK, hist, scratch);
+    if (nK > 0) sort_items(cnt_k, bwd_q, B, H, Hm, nK, hist, scratch, nullptr);
     if (threadIdx.x == 0) {
       counters[kCtrBwdItems] = (uint32_t)((long)B * H * nK);
       counters[kCtrBwdNext] = 0;
@@ -273,7 +320,8 @@ hipError_t launch_tile_bounds(const TileArgs& a, hipStream_t stream) {
   // counters behind, with a kernel rather than a memset, which stays correct
   // when a caller replays the calls as a captured graph
   queue_kernel<<<2, kQueueThreads, 0, stream>>>(a.cnt_q, a.cnt_k, a.fwd_queue, a.bwd_queue,
-                                                a.counters, a.B, a.H, a.Hm, a.nQ, a.nK);
+                                                a.counters, a.B, a.H, a.Hm, a.nQ, a.nK, a.fwd_slots,
+                                                a.split_cap);
   return hipGetLastError();
 }
 

@@ -70,7 +70,9 @@ typedef struct {
 /* Byte offsets of the parts of a tileinfo buffer (each 256-byte aligned), as
  * written by fm_tile_bounds.  nQ = ceil(Sq/block_q), nK = ceil(Sk/block_k).
  *   counters  uint32[16]: [0] forward items, [1] backward items,
- *             [2],[3] forward / backward next-item counters, [4],[5] exit counters
+ *             [2],[3] forward / backward next-item counters, [4],[5] exit counters,
+ *             [6],[7] the dQ kernel's next-item and exit counters,
+ *             [8] forward items split in two (the first entries of fwd_queue)
  *   kbsum     int32 [B][Hm][nK][8]  per key block, over its columns j < Sk, the
  *             min and max of each bound clamped to [0, Sq]:
  *             LTS min, LTS max, LTE min, LTE max, UTS min, UTS max, UTE min, UTE max
@@ -81,10 +83,13 @@ typedef struct {
  *             increasing order (first cnt_q entries), bit 15 set if partial
  *   list_k    uint16[B][Hm][nK][nQ] per key block, its non-skipped query blocks
  *   fwd_queue uint32[B*H*nQ]         forward items (b*H+h)*nQ+qb, most tiles first
- *   bwd_queue uint32[B*H*nK]         backward items (b*H+h)*nK+kb, most tiles first */
+ *   bwd_queue uint32[B*H*nK]         backward items (b*H+h)*nK+kb, most tiles first
+ *   fwd_partials bf16[2*C][block_q][D] then float[2*C][block_q], C = min(B*H*nQ, 512):
+ *             for each split forward item, the output and LSE of each half of
+ *             its key blocks (scratch of fm_attn_fwd; no meaning between calls) */
 typedef struct {
   int32_t block_q, block_k, n_qblocks, n_kblocks;
-  size_t counters, kbsum, cls, cnt_q, cnt_k, list_q, list_k, fwd_queue, bwd_queue;
+  size_t counters, kbsum, cls, cnt_q, cnt_k, list_q, list_k, fwd_queue, bwd_queue, fwd_partials;
   size_t total;           /* bytes the caller must allocate                     */
 } fm_tileinfo_layout;
 
@@ -133,7 +138,10 @@ fm_status fm_tile_bounds(const fm_problem* p, const int32_t* bounds, void* tilei
  * LSE_i = log sum_j exp(scale * q_i.k_j) over visible j (+inf if none).
  * Skipped tiles are never touched; the elementwise mask is evaluated only on
  * partial tiles.  bf16 MFMA with fp32 accumulation; O rounded to nearest even.
- * Needs a tileinfo from fm_tile_bounds for the same problem and bounds.
+ * Needs a tileinfo from fm_tile_bounds for the same problem and bounds.  The
+ * query blocks that fm_tile_bounds marked for splitting are computed as two
+ * halves of their key blocks, whose partial results (in tileinfo) a second
+ * kernel merges; the call writes O and LSE of every row either way.
  */
 fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const void* v,
                       const int32_t* bounds, void* tileinfo, void* o, float* lse, void* stream);

@@ -110,3 +110,24 @@ def check_tileinfo(w, ti):
         assert np.all(np.diff(np.minimum(cost, 4095)) <= 0), f"{name} not sorted by tile count"
     c = ti["counters"]
     assert c[0] == B * H * nQ and c[1] == B * H * nK and c[2] == 0 and c[3] == 0
+    assert c[8] == expected_split_count(cq, H, Hm), "number of split forward items differs"
+
+
+def expected_split_count(cq, H, Hm):
+    """Forward items the tile pass splits in two: none when there are at
+    least 4 W items; else those with more than
+    max(16, ceil(total / (2 W))) non-skipped tiles, W the forward's persistent
+    grid (two workgroups per compute unit), at most min(items, 512) of them,
+    none when the threshold or any item reaches the top bucket of the sort
+    (4095 tiles)."""
+    from column_sparse_masked_amd import _lib
+    B, Hm_, nQ = cq.shape
+    per_item = np.repeat(cq, H // Hm, axis=1) if Hm == 1 else cq      # [B][H][nQ]
+    total = int(per_item.sum())
+    W = 2 * _lib.device_cu_count()
+    if B * per_item.shape[1] * nQ >= 4 * W:      # enough items per workgroup: never split
+        return 0
+    thr = max(16, -(-total // (2 * W)))
+    if thr >= 4095 or (per_item >= 4095).any():
+        return 0
+    return min(int((per_item > thr).sum()), min(B * H * nQ, 512))

@@ -30,7 +30,7 @@ def test_every_declared_function_is_exported():
 
 def test_struct_sizes_match_header():
     assert ctypes.sizeof(L.Problem) == 28
-    assert ctypes.sizeof(L.TileinfoLayout) == 16 + 10 * 8
+    assert ctypes.sizeof(L.TileinfoLayout) == 16 + 11 * 8
 
 
 def _p(**kw):
@@ -133,7 +133,10 @@ def test_tileinfo_layout(B, H, Hm, Sq, Sk):
     parts = [("counters", 64), ("kbsum", B * Hm * nK * 32), ("cls", B * Hm * nQ * nK),
              ("cnt_q", B * Hm * nQ * 4), ("cnt_k", B * Hm * nK * 4),
              ("list_q", B * Hm * nQ * nK * 2), ("list_k", B * Hm * nK * nQ * 2),
-             ("fwd_queue", B * H * nQ * 4), ("bwd_queue", B * H * nK * 4)]
+             ("fwd_queue", B * H * nQ * 4), ("bwd_queue", B * H * nK * 4),
+             # two partial-result slots (bf16 O, fp32 LSE of 128 rows) per forward
+             # item that may be split, at most 512 of them
+             ("fwd_partials", 2 * min(B * H * nQ, 512) * 128 * (128 * 2 + 4))]
     end = 0
     for name, size in parts:
         off = getattr(lay, name)

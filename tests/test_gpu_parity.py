@@ -72,6 +72,16 @@ def _cases():
         "single_row_S1_D128": lambda: M.custom(M.causal_document_bounds([1]), B=1, H=1, Sq=1, D=128, seed=30),
         "tiny_S17_D64": lambda: M.custom(M.causal_document_bounds([5, 12]), B=2, H=2, Sq=17, D=64, seed=31),
         "extreme_int32_bounds": lambda: M.custom(_extreme_bounds(300), B=1, H=2, Sq=300, D=128, seed=32),
+        # long lists: query blocks with more than 16 key blocks are computed as
+        # two halves and merged (ragged last block; rows that see keys in one
+        # half only; rows that see none)
+        "split_unmasked_S4000_D128": lambda: M.custom(M.empty_bounds(4000, 4000), B=1, H=2, Sq=4000,
+                                                      D=128, seed=36),
+        "split_causal_docs_S4200_D64": lambda: M.custom(M.causal_document_bounds([2500, 1700]), B=1, H=2,
+                                                        Sq=4200, D=64, seed=37),
+        "split_masked_rows_S3000": lambda: M.custom(
+            np.stack([np.full(3000, 1000), np.full(3000, 1100), np.zeros(3000), np.zeros(3000)], 1).astype(np.int32),
+            B=1, H=2, Sq=3000, D=128, seed=38),
     }
     return cases
 
@@ -108,7 +118,7 @@ def test_empty_problem_zeroes_counters():
     att.buf.tileinfo.fill_(0xFF)
     att.tile_bounds(to_device_bounds(w.bounds))
     torch.cuda.synchronize()
-    assert att.read_tileinfo()["counters"].tolist() == [0] * 8 + [0xFFFFFFFF] * 8
+    assert att.read_tileinfo()["counters"].tolist() == [0] * 9 + [0xFFFFFFFF] * 7
 
 
 def test_empty_query_set():
