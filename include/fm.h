@@ -25,9 +25,9 @@
  * allocates nothing and keeps no per-call state; it caches only the device's
  * compute-unit count.  `tileinfo` (size from fm_tileinfo_layout) is written by
  * fm_tile_bounds and then read by fm_attn_fwd / fm_attn_bwd, which also use
- * two work counters inside it; the counters are left at zero when a call's
- * kernels finish.  So at most one forward and one backward may be in flight
- * per tileinfo buffer; calls that share a tileinfo must be ordered (one stream).
+ * work counters and scratch slots inside it; the counters are left at zero
+ * when a call's kernels finish.  Calls that share a tileinfo must therefore be
+ * ordered (one stream): no two of them may be in flight at once.
  *
  * Streams: `stream` is a hipStream_t (NULL = default stream).  Every entry
  * point validates its arguments on the host, enqueues its kernels on `stream`
