@@ -187,23 +187,12 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
       for (int v = 0; v < 16; ++v) acc[d][v] = 0.f;
 
     if (cnt > 0) {
-      // Q and dO rows of this lane's query (B operands), LSE and Delta
-      bf16x8 qf[NS], of[NS];
-      {
-        const uint32_t off = ((uint32_t)qrow * D + 8u * hh) * 2u;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          qf[s] = buf_load16(qbase, off + 32u * s);
-          of[s] = buf_load16(obase, off + 32u * s);
-        }
-      }
-      const bool live = qrow < Sq;
-      const float lse2 = live ? a.lse[bh * Sq + qrow] * kLog2e : INFINITY;
-      const float dls = live ? a.delta[bh * Sq + qrow] * a.scale : 0.f;
 
       // hidden-row words of a partial key block (threads < BK, one key each)
-      auto hidden_words = [&](int k0, uint32_t (&wd)[BQ / 32]) __attribute__((always_inline)) {
-        const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(bbase, (k0 + (int)t) * 16, 0, 0);
+      auto key_bounds = [&](int k0) __attribute__((always_inline)) {
+        return __builtin_amdgcn_raw_buffer_load_b128(bbase, (k0 + (int)t) * 16, 0, 0);
+      };
+      auto words_of = [&](const i32x4 x, int k0, uint32_t (&wd)[BQ / 32]) __attribute__((always_inline)) {
         const bool in = k0 + (int)t < Sk;   // keys past the end hide every row
         const int lts = in ? x[0] : INT_MIN, lte = in ? x[1] : INT_MAX;
         const int uts = in ? x[2] : 0, ute = in ? x[3] : 0;
@@ -214,24 +203,59 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
           wd[g] = row_bits(clip(lts), clip(lte)) | row_bits(clip(uts), clip(ute));
         }
       };
+      auto hidden_words = [&](int k0, uint32_t (&wd)[BQ / 32]) __attribute__((always_inline)) {
+        words_of(key_bounds(k0), k0, wd);
+      };
 
       DqStage<D> st;
       int e_cur = list_entry(lst, 0);
+      // The first key block's loads go first: its LDS staging then waits for
+      // them only, with the Q and dO rows (needed after the barrier) in flight.
+      const int k00 = block_start(e_cur);
+      const bool m00 = block_masked(e_cur, k00) && t < BK;
+      i32x4 bd00 = {0, 0, 0, 0};
+      if (m00) bd00 = key_bounds(k00);
+      dq_load<D>(st, kbase, vbase, k00, t);
+      // Q and dO rows of this lane's query (B operands), LSE and Delta.  The
+      // lane's offsets are rebuilt per item from its lane index rather than
+      // kept, spilled, through the kernel: reloading a spill waits for every
+      // load issued before it.  LSE and Delta are used only after the
+      // barrier below.
+      const int ln = lane_in(n);
+      const int qrow0 = q0 + 32 * __builtin_amdgcn_readfirstlane(qw);
+      bf16x8 qf[NS], of[NS];
       {
-        const int k0 = block_start(e_cur);
-        dq_load<D>(st, kbase, vbase, k0, t);
-        uint32_t wd[BQ / 32];
-        const bool m = block_masked(e_cur, k0) && t < BK;
-        if (m) hidden_words(k0, wd);
-        dq_store_rows<D>(st, sm, t);
-        dq_store_kt<D>(st, sm, t);
-        if (m)
+        const uint32_t off = (uint32_t)((ln & 31) * D + 8 * (ln >> 5)) * 2u + (uint32_t)qrow0 * (D * 2);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          qf[s] = buf_load16(qbase, off + 32u * s);
+          of[s] = buf_load16(obase, off + 32u * s);
+        }
+      }
+      const uint32_t roff = (uint32_t)(ln & 31) * 4u + (uint32_t)qrow0 * 4u;
+      const float lse_raw = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.lse + bh * Sq, (uint32_t)Sq * 4u), (int)roff, 0, 0));
+      const float dl_raw = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.delta + bh * Sq, (uint32_t)Sq * 4u), (int)roff, 0, 0));
+      {
+        if (m00) {
+          uint32_t wd[BQ / 32];
+          words_of(bd00, k00, wd);
 #pragma unroll
           for (int g = 0; g < BQ / 32; ++g) sm.hid[g][t] = wd[g];
+        }
+        dq_store_rows<D>(st, sm, t);
+        dq_store_kt<D>(st, sm, t);
       }
       pf.stash(sm.hdr[(n + 1) & 1], t);   // the stores above waited for loads issued after the ticket
-      if (cnt > 1) dq_load<D>(st, kbase, vbase, block_start(list_entry(lst, 1)), t);
+      // Unconditional (a one-block item loads its block again, unused), so
+      // that the waits for LSE and Delta count these loads as issued after
+      // them on every path instead of waiting for them too.
+      dq_load<D>(st, kbase, vbase, block_start(list_entry(lst, cnt > 1 ? 1 : 0)), t);
       __syncthreads();
+      const bool live = qrow < Sq;
+      const float lse2 = live ? lse_raw * kLog2e : INFINITY;
+      const float dls = live ? dl_raw * a.scale : 0.f;
 
       // Per key block t (K, V, hid of t and K^T of t in LDS; t+1 in registers):
       //   S^T, dP^T, dS^T of both 32-key sub-blocks | barrier | K, V, hid of

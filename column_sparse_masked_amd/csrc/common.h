@@ -120,6 +120,15 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x, int salt) {
   return x;
 }
 
+// This lane's index in its wave (0..63), computed afresh where it is called
+// inside a loop (tied to `salt`, as above): a value rebuilt from it in two
+// instructions then takes no register, nor a spill slot, across the loop.
+__device__ __forceinline__ int lane_in(int salt) {
+  int r;
+  asm("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r) : "s"(salt));
+  return r;
+}
+
 // Entry i of a uint16 tile list, read through the scalar cache: the list of
 // a work item is the same for the whole workgroup, so the aligned 32-bit word
 // holding the entry is fetched with a scalar load (constant address space).
