@@ -74,6 +74,34 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+E4M3_MAX = 448.0
+
+
+def e4m3_codes(x: np.ndarray):
+    """Per-tensor E4M3 encoding of fp32 values for the fp8 forward's inputs:
+    descale = max|x| / 448 (1 for an all-zero tensor) and codes = x / descale
+    rounded to E4M3 (nearest, ties to even; torch's float8_e4m3fn cast).
+    Returns (uint8 codes of x's shape, float32 descale)."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    descale = np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+    t = torch.from_numpy(x) / float(descale)
+    codes = t.clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, descale
+
+
+def fp8_inputs(tensors):
+    """E4M3 Q, K, V (uint8 codes) and their descale factors (float32[3]) from
+    the bf16 draws (q, k, v, ...) of a workload."""
+    out, ds = [], []
+    for x in tensors[:3]:
+        c, d = e4m3_codes(bf16_to_f32(x))
+        out.append(c)
+        ds.append(d)
+    return out[0], out[1], out[2], np.array(ds, dtype=np.float32)
+
+
 # --------------------------------------------------------------------------- #
 # seeded structure draws                                                       #
 # --------------------------------------------------------------------------- #

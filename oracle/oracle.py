@@ -111,6 +111,40 @@ def forward(q, k, v, bounds, scale):
 
 
 # --------------------------------------------------------------------------- #
+# the fp8 forward                                                             #
+# --------------------------------------------------------------------------- #
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """OCP 8-bit floating point, E4M3 format (OCP OFP8 specification, the
+    E4M3 encoding table) -> float64, exactly.  Bit 7 is the sign, bits 6..3 the
+    exponent (bias 7), bits 2..0 the mantissa.  Exponent field 0 encodes
+    subnormals m/8 * 2^-6; the code with every exponent and mantissa bit set
+    is NaN; there are no infinities, so the largest finite value is
+    1.75 * 2^8 = 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, mag)
+    return sign * mag
+
+
+def forward_fp8(q8, k8, v8, descale, bounds, scale):
+    """O [B][H][Sq][D], LSE [B][H][Sq] (float64) of the fp8 forward.
+
+    The pages name FP8 mixed precision as part of FlashMask V3 (PaddlePaddle
+    3.2.0 release note, FlashMask V3 highlights) and give nothing more.  The
+    reading taken: Q, K and V arrive as E4M3 codes with one fp32 descale
+    factor per tensor (value = decode(code) * descale), and the result is the
+    same masked attention of those values.  This is that definition: decode,
+    scale, and the float64 forward above.  Rounding the kernel does on the
+    way (P to E4M3 before the P V product) is not modelled here; its effect is
+    bounded in the tests."""
+    dq, dk, dv = (float(x) for x in descale)
+    return forward(decode_e4m3(q8) * dq, decode_e4m3(k8) * dk, decode_e4m3(v8) * dv, bounds, scale)
+
+
+# --------------------------------------------------------------------------- #
 # backward                                                                    #
 # --------------------------------------------------------------------------- #
 def head_backward(qh, kh, vh, doh, bounds_h, scale, rows=None, lse=None):

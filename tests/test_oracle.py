@@ -322,3 +322,68 @@ def test_batched_entry_points_match_heads():
     for h in range(H):
         r = O.head_forward(q[1, h], k[1, h], v[1, h], bounds[1, 0], 0.35)[0]
         np.testing.assert_array_equal(o1[1, h], r)
+
+
+# --------------------------------------------------------------------------- #
+# fp8 forward                                                                  #
+# --------------------------------------------------------------------------- #
+def test_e4m3_decode_table():
+    """Code points of the OCP OFP8 E4M3 encoding (the specification's table of
+    special values: zero, smallest subnormal and normal, one, the largest
+    finite value, NaN)."""
+    want = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0,
+            0x3F: 1.875, 0x40: 2.0, 0x7E: 448.0, 0x77: 240.0, 0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0}
+    got = O.decode_e4m3(np.array(list(want), dtype=np.uint8))
+    assert np.array_equal(got, np.array(list(want.values())))
+    assert np.signbit(O.decode_e4m3(np.array([0x80], np.uint8)))[0]
+    assert np.isnan(O.decode_e4m3(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.decode_e4m3(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # positive finite codes are strictly increasing
+    assert np.all(np.diff(got[:0x7F]) > 0)
+
+
+def test_e4m3_inputs_round_trip():
+    """Encoding in the input module: every value within half an E4M3 step of
+    x / descale (relative 2^-4 for normals, 2^-10 absolute for subnormals)."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(4096).astype(np.float32) * 3
+    codes, ds = M.e4m3_codes(x)
+    assert ds == np.float32(np.abs(x).max() / 448)
+    y = x / np.float64(ds)
+    err = np.abs(O.decode_e4m3(codes) - y)
+    assert np.all(err <= np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) + 1e-12)
+
+
+@pytest.mark.parametrize("family", ["causal", "sliding"])
+def test_fp8_forward_equals_sdpa_on_decoded_inputs(family):
+    """The fp8 forward is masked attention of decode(codes) * descale: checked
+    against torch's float64 SDPA with the dense mask."""
+    rng = np.random.default_rng(11)
+    Sq = Sk = 200
+    D = 32
+    q, k, v = (rng.standard_normal((1, 1, Sq, D)).astype(np.float32) for _ in range(3))
+    (q8, dq), (k8, dk), (v8, dv) = (M.e4m3_codes(x) for x in (q, k, v))
+    bounds = (M.causal_document_bounds([120, 80]) if family == "causal"
+              else M.sliding_window_bounds(Sq, 37))[None, None].astype(np.int32)
+    scale = 0.3
+    o, lse = O.forward_fp8(q8, k8, v8, (dq, dk, dv), bounds, scale)
+    vis = ~O.dense_mask(bounds[0, 0], np.arange(Sq))
+    qd, kd, vd = (O.decode_e4m3(c)[0, 0] * float(d) for c, d in ((q8, dq), (k8, dk), (v8, dv)))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(qd)[None], torch.tensor(kd)[None], torch.tensor(vd)[None],
+        attn_mask=torch.tensor(vis)[None], scale=scale)[0].numpy()
+    live = vis.any(axis=1)
+    assert np.allclose(o[0, 0][live], ref[live], atol=1e-12, rtol=1e-10)
+    s = (qd @ kd.T) * scale
+    s[~vis] = -np.inf
+    m = s.max(axis=1)
+    lse_ref = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    assert np.allclose(lse[0, 0][live], lse_ref[live], atol=1e-12)
