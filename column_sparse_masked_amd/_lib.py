@@ -71,6 +71,7 @@ lib.fm_bwd_workspace_bytes.argtypes = [_P, ctypes.POINTER(ctypes.c_size_t)]
 lib.fm_device_cu_count.argtypes = [ctypes.POINTER(ctypes.c_int32)]
 lib.fm_tile_bounds.argtypes = [_P, _vp, _vp, _vp]
 lib.fm_attn_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+lib.fm_attn_fwd_fp8.argtypes = [_P, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_float), _vp, _vp, _vp, _vp, _vp]
 lib.fm_attn_bwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 for _f in ("fm_tile_shape", "fm_tileinfo_layout_query", "fm_bwd_workspace_bytes",
            "fm_device_cu_count", "fm_tile_bounds", "fm_attn_fwd", "fm_attn_bwd"):
@@ -141,6 +142,14 @@ def fm_tile_bounds(p: Problem, bounds, tileinfo, stream=None):
 def fm_attn_fwd(p: Problem, q, k, v, bounds, tileinfo, o, lse, stream=None):
     _check(lib.fm_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(bounds), _ptr(tileinfo),
                            _ptr(o), _ptr(lse), _stream(stream)), "fm_attn_fwd")
+
+
+def fm_attn_fwd_fp8(p: Problem, q8, k8, v8, descale, bounds, tileinfo, o, lse, stream=None):
+    """q8, k8, v8: uint8 device tensors of E4M3 codes; descale: three host
+    floats (q, k, v)."""
+    ds = (ctypes.c_float * 3)(*[float(x) for x in descale])
+    _check(lib.fm_attn_fwd_fp8(ctypes.byref(p), _ptr(q8), _ptr(k8), _ptr(v8), ds, _ptr(bounds),
+                               _ptr(tileinfo), _ptr(o), _ptr(lse), _stream(stream)), "fm_attn_fwd_fp8")
 
 
 def fm_attn_bwd(p: Problem, q, k, v, o, dout, lse, bounds, tileinfo, dq, dk, dv, workspace,

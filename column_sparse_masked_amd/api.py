@@ -16,6 +16,11 @@ def to_device_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
 
 
+def to_device_u8(codes: np.ndarray, device="cuda") -> torch.Tensor:
+    """uint8 codes (E4M3) -> uint8 tensor on ``device``."""
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).to(device)
+
+
 def to_device_bounds(bounds: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bounds, dtype=np.int32)).to(device)
 
@@ -48,6 +53,18 @@ class MaskedAttention:
         if lse is None:
             lse = torch.empty((p.batch, p.heads, p.seqlen_q), dtype=torch.float32, device=self.device)
         _lib.fm_attn_fwd(p, q, k, v, bounds, self.buf.tileinfo, o, lse, stream)
+        return o, lse
+
+    def forward_fp8(self, q8, k8, v8, descale, bounds, o=None, lse=None, stream=None):
+        """The forward with E4M3 inputs: q8, k8, v8 uint8 code tensors in the
+        bf16 tensors' layouts, descale three floats (q, k, v)."""
+        p = self.p
+        if o is None:
+            o = torch.empty((p.batch, p.heads, p.seqlen_q, p.head_dim), dtype=torch.bfloat16,
+                            device=self.device)
+        if lse is None:
+            lse = torch.empty((p.batch, p.heads, p.seqlen_q), dtype=torch.float32, device=self.device)
+        _lib.fm_attn_fwd_fp8(p, q8, k8, v8, descale, bounds, self.buf.tileinfo, o, lse, stream)
         return o, lse
 
     def backward(self, q, k, v, o, dout, lse, bounds, dq=None, dk=None, dv=None, stream=None):

@@ -249,6 +249,50 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
              : FM_ERR_HIP;
 }
 
+fm_status fm_attn_fwd_fp8(const fm_problem* p, const void* q, const void* k, const void* v,
+                          const float* descale, const int32_t* bounds, void* tileinfo, void* o, float* lse,
+                          void* stream) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  if (p->head_dim != 128) return FM_ERR_UNSUPPORTED;
+  if (!descale) return FM_ERR_NULL;
+  for (int i = 0; i < 3; ++i)
+    if (!(descale[i] > 0.f) || !std::isfinite(descale[i])) return FM_ERR_UNSUPPORTED;
+  const float qk = p->softmax_scale * descale[0] * descale[1];
+  if (!(qk > 0.f) || !std::isfinite(qk)) return FM_ERR_UNSUPPORTED;
+  const bool has_rows = p->batch > 0 && p->seqlen_q > 0;
+  const bool has_cols = p->batch > 0 && p->seqlen_k > 0;
+  if (!tileinfo) return FM_ERR_NULL;
+  if (has_rows && (!tensor_ok(q) || !tensor_ok(o) || !lse)) return FM_ERR_NULL;
+  if (has_cols && (!tensor_ok(k) || !tensor_ok(v) || !bounds)) return FM_ERR_NULL;
+  if (!aligned(tileinfo, 256) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(o, 16) || !aligned(bounds, 16) || !aligned(lse, 4))
+    return FM_ERR_ALIGN;
+  if (!has_rows) return FM_OK;
+  Layout L = make_layout(p);
+  int cus = 0;
+  if ((st = cu_count(&cus)) != FM_OK) return st;
+  fm::Fp8FwdArgs a;
+  a.q = static_cast<const uint8_t*>(q);
+  a.k = static_cast<const uint8_t*>(k);
+  a.v = static_cast<const uint8_t*>(v);
+  a.o = static_cast<__bf16*>(o);
+  a.lse = lse;
+  a.bounds = reinterpret_cast<const int4*>(bounds);
+  a.list_q = at<uint16_t>(tileinfo, L.list_q);
+  a.cnt_q = at<int>(tileinfo, L.cnt_q);
+  a.queue = at<uint32_t>(tileinfo, L.fwd_queue);
+  a.counters = at<uint32_t>(tileinfo, L.counters);
+  a.B = p->batch; a.H = p->heads; a.Hm = p->mask_heads;
+  a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
+  a.scale_log2 = qk * fm::kLog2e;
+  a.o_scale = descale[2];
+  const long items = (long)p->batch * p->heads * L.nQ;
+  const long slots = (long)cus * fm::fwd_blocks_per_cu(p->head_dim);
+  const int grid = (int)(items < slots ? items : slots);
+  return fm::launch_attn_fwd_fp8(a, grid, (hipStream_t)stream, g_events) == hipSuccess ? FM_OK : FM_ERR_HIP;
+}
+
 fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
                       const void* o, const void* dout, const float* lse,
                       const int32_t* bounds, void* tileinfo,

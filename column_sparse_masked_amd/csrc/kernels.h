@@ -39,6 +39,23 @@ struct FwdArgs {
   float scale_log2;   // softmax_scale * log2(e)
 };
 
+// The fp8 forward (head_dim 128): E4M3 q, k, v with per-tensor descales.
+struct Fp8FwdArgs {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  __bf16* o;
+  float* lse;
+  const int4* bounds;
+  const uint16_t* list_q;
+  const int* cnt_q;
+  const uint32_t* queue;
+  uint32_t* counters;
+  int B, H, Hm, Sq, Sk, nQ, nK;
+  float scale_log2;   // softmax_scale * descale_q * descale_k * log2(e)
+  float o_scale;      // descale_v
+};
+
 struct BwdArgs {
   const __bf16* q;
   const __bf16* k;
@@ -74,6 +91,7 @@ struct KernelEvents {
 
 hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream,
                            const KernelEvents& ev);
+hipError_t launch_attn_fwd_fp8(const Fp8FwdArgs& a, int grid, hipStream_t stream, const KernelEvents& ev);
 hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, int dq_grid,
                            hipStream_t stream, const KernelEvents& ev);
 hipError_t launch_attn_bwd_dq(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);

@@ -147,6 +147,27 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
                       const int32_t* bounds, void* tileinfo, void* o, float* lse, void* stream);
 
 /*
+ * fm_attn_fwd_fp8 - the same forward with E4M3 inputs (head_dim 128 only).
+ * PaddlePaddle 3.2.0 release note, FlashMask V3 highlights: FlashMask V3
+ * comes with FP8 mixed precision; nothing more is specified there.
+ * q, k, v are OCP E4M3 codes (1 byte per value, same [B][H][S][128] layouts
+ * as the bf16 tensors, 16-byte aligned); `descale` is a HOST array of three
+ * fp32 factors (q, k, v), finite and > 0: the value of a code c of tensor x
+ * is decode(c) * descale[x].  O (bf16) and LSE (fp32) are those of the exact
+ * attention of these values, up to rounding: both products run on the fp8
+ * matrix cores with fp32 accumulation, and the softmax probabilities are
+ * rounded to E4M3 (relative error <= 2^-4) before the P.V product; the row
+ * sums, and so LSE, use the unrounded fp32 probabilities.  Needs a tileinfo
+ * from fm_tile_bounds for the same problem and bounds; no item is split.
+ * Shares the forward's queue counters in tileinfo: calls on one tileinfo,
+ * fp8 or not, must be ordered.  Errors: FM_ERR_UNSUPPORTED for head_dim 64
+ * or a bad descale; otherwise as fm_attn_fwd.
+ */
+fm_status fm_attn_fwd_fp8(const fm_problem* p, const void* q, const void* k, const void* v,
+                          const float* descale, const int32_t* bounds, void* tileinfo,
+                          void* o, float* lse, void* stream);
+
+/*
  * fm_attn_bwd - gradients of fm_attn_fwd given dL/dO.
  * With P = exp(scale * q.k - LSE) (0 where masked), dP = dO v^T,
  * Delta_i = sum_d dO_id O_id, dS = P (dP - Delta):

@@ -131,3 +131,92 @@ def expected_split_count(cq, H, Hm):
     if thr >= 4095 or (per_item >= 4095).any():
         return 0
     return min(int((per_item > thr).sum()), min(B * H * nQ, 512))
+
+
+# --------------------------------------------------------------------------- #
+# fp8 forward                                                                  #
+# --------------------------------------------------------------------------- #
+# Tolerance contract of the fp8 forward, derived from what its kernel rounds.
+# Its scores are exact products of E4M3 values accumulated in fp32, so LSE
+# keeps the bf16 forward's bound.  Its probabilities p (relative to a running
+# reference m' with m' <= the row maximum m) are rounded to E4M3 before the
+# P.V product: |round(p) - p| <= 2^-4 p for normal values and <= 2^-10 for
+# subnormal ones.  With l' = sum_j p_j >= l = sum_j exp(s_j - m), the error of
+# O_id = sum_j p_j v_jd / l' is at most
+#     2^-4 sum_j P_ij |v_jd|  +  2^-10 sum_{j visible} |v_jd| / l_i
+# (P the exact softmax), plus bf16 rounding of O (2^-8 |O| covers it) and a
+# small fp32 allowance.  Over a tensor, the errors are a weighted mean of
+# independent relative roundings, so ||O - O_ref|| / ||O_ref|| <= 2^-4.
+FP8_O_REL_L2 = 2.0 ** -4
+
+
+def fp8_decoded(codes, descale):
+    q8, k8, v8 = codes
+    return tuple(oracle.decode_e4m3(c) * float(d) for c, d in zip((q8, k8, v8), descale))
+
+
+def fp8_head_check(qd, kd, vd, bounds_h, scale, rows, go, gl):
+    """Compare GPU O (rows x D, float64) and LSE (rows) of one head with the
+    exact attention of the decoded inputs, within the per-element bound
+    above.  Returns (sum of squared errors, sum of squared references, max
+    LSE error, max error / bound)."""
+    num = den = lse_err = worst = 0.0
+    for s0 in range(0, rows.size, 256):
+        r = rows[s0:s0 + 256]
+        vis = ~oracle.dense_mask(bounds_h, r)
+        s = scale * (qd[r] @ kd.T)
+        s[~vis] = -np.inf
+        m = s.max(axis=1) if s.shape[1] else np.full(r.size, -np.inf)
+        live = np.isfinite(m)
+        e = np.zeros_like(s)
+        e[live] = np.exp(s[live] - m[live, None])
+        l = e.sum(axis=1)
+        P = np.zeros_like(s)
+        P[live] = e[live] / l[live, None]
+        ref = P @ vd
+        absv = np.abs(vd)
+        bound = np.zeros_like(ref)
+        bound[live] = (2.0 ** -4 * (P[live] @ absv) + 2.0 ** -10 * (vis[live] @ absv) / l[live, None]
+                       + 2.0 ** -8 * np.abs(ref[live]) + 1e-5 * (absv.max() if absv.size else 0.0))
+        o = go[s0:s0 + 256]
+        lse = gl[s0:s0 + 256]
+        assert (o[~live] == 0).all(), "a row with no visible key has O != 0"
+        assert np.isposinf(lse[~live]).all() and np.isfinite(lse[live]).all(), "LSE +inf positions differ"
+        err = np.abs(o - ref)
+        if live.any():
+            worst = max(worst, float((err[live] / bound[live]).max()))
+            lse_err = max(lse_err, float(np.abs(lse[live] - (m[live] + np.log(l[live]))).max()))
+        num += float(np.sum(err ** 2))
+        den += float(np.sum(ref ** 2))
+    return num, den, lse_err, worst
+
+
+def run_gpu_fp8(w, codes, descale, device="cuda"):
+    import torch
+    from column_sparse_masked_amd.api import MaskedAttention, to_device_bounds, to_device_u8
+    tq, tk, tv = (to_device_u8(c, device) for c in codes)
+    tb = to_device_bounds(w.bounds, device)
+    att = MaskedAttention.for_workload(w, device)
+    att.tile_bounds(tb)
+    o, lse = att.forward_fp8(tq, tk, tv, descale, tb)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), att
+
+
+def check_fp8(w, go, gl, codes, descale, heads=None, rows_of=None, label=""):
+    qd, kd, vd = fp8_decoded(codes, descale)
+    heads = heads or [(b, h) for b in range(w.B) for h in range(w.H)]
+    num = den = lse_err = worst = 0.0
+    for (b, h) in heads:
+        bh = w.bounds[b, oracle.mask_head(w.bounds, h)]
+        rows = np.arange(w.Sq) if rows_of is None else rows_of(b, h)
+        n_, d_, le, wo = fp8_head_check(qd[b, h], kd[b, h], vd[b, h], bh, w.scale, rows,
+                                        go[b, h][rows], gl[b, h][rows])
+        num, den = num + n_, den + d_
+        lse_err, worst = max(lse_err, le), max(worst, wo)
+    rel = float(np.sqrt(num / den)) if den > 0 else float(np.sqrt(num))
+    say(f"{label}: fp8 O rel-L2 {rel:.3e}, max error/bound {worst:.3f}, LSE max-abs {lse_err:.2e}")
+    assert worst <= 1.0, f"{label} O error above its bound ({worst})"
+    assert rel <= FP8_O_REL_L2, f"{label} O rel-L2 {rel}"
+    assert lse_err <= LSE_TOL, f"{label} LSE max-abs {lse_err}"
+    return rel, worst, lse_err

@@ -145,3 +145,38 @@ def test_tileinfo_layout(B, H, Hm, Sq, Sk):
     assert lay.total >= end
     ws = L.bwd_workspace_bytes(p)
     assert ws >= B * H * Sq * 4   # Delta of every row
+
+
+def test_fp8_forward_validation():
+    """fm_attn_fwd_fp8 rejects head_dim 64, a missing or bad descale, null and
+    misaligned tensors before any launch."""
+    fake = ctypes.c_void_p(1 << 20)
+    ds = (ctypes.c_float * 3)(0.01, 0.02, 0.03)
+    p64 = _p(head_dim=64)
+    assert L.lib.fm_attn_fwd_fp8(ctypes.byref(p64), fake, fake, fake, ds, fake, fake, fake, fake, None) \
+        == L.FM_ERR_UNSUPPORTED
+    p = _p()
+    assert L.lib.fm_attn_fwd_fp8(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, None) \
+        == L.FM_ERR_NULL
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        for i in range(3):
+            d = (ctypes.c_float * 3)(0.01, 0.02, 0.03)
+            d[i] = bad
+            assert L.lib.fm_attn_fwd_fp8(ctypes.byref(p), fake, fake, fake, d, fake, fake, fake, fake,
+                                         None) == L.FM_ERR_UNSUPPORTED, (bad, i)
+    tensors = [fake] * 3 + [None] + [fake] * 4   # q k v | descale slot | bounds tileinfo o lse
+    for i in (0, 1, 2, 4, 5, 6, 7):
+        a = list(tensors)
+        a[i] = None
+        a[3] = ds
+        assert L.lib.fm_attn_fwd_fp8(ctypes.byref(p), *a, None) == L.FM_ERR_NULL, i
+    bad = ctypes.c_void_p((1 << 20) + 8)
+    for i in (0, 1, 2, 4, 5, 6):
+        a = list(tensors)
+        a[i] = bad
+        a[3] = ds
+        assert L.lib.fm_attn_fwd_fp8(ctypes.byref(p), *a, None) == L.FM_ERR_ALIGN, i
+    for kw in (dict(batch=-1), dict(heads=0), dict(softmax_scale=0.0)):
+        q = _p(**kw)
+        assert L.lib.fm_attn_fwd_fp8(ctypes.byref(q), fake, fake, fake, ds, fake, fake, fake, fake, None) \
+            != L.FM_OK
