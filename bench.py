@@ -16,6 +16,10 @@ per (batch, head), nnz being the number of unmasked (query, key) pairs, so
 masked work the kernels skip is not credited and masked elements they compute
 inside partial tiles are not credited either.
 
+With head_dim 128 the fp8 forward (fm_attn_fwd_fp8, E4M3 inputs) is then
+timed on the same workload and reported beside the step ("fp8_forward"; not
+part of the step or its throughput).
+
 Printed: one JSON line with the whole-step throughput, the roofline of the
 dominant kernel (timed live with HIP events recorded by the library right
 around that kernel, on the stream it runs on) and the fp64 CPU oracle timed on
@@ -41,6 +45,7 @@ if ROOT not in sys.path:
 METRIC = "mask-effective attention fwd+bwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 # Dense bf16 MFMA peak of MI355X: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
 PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP8_TFLOPS = 5033.2
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -53,6 +58,7 @@ def parse_args(argv=None):
     ap.add_argument("--seed", type=int, default=None, help="default: the config's index")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle sample (at least one head is always run)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward's line (head_dim 128 only)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="leave out the oracle timing (profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -140,6 +146,41 @@ def cpu_baseline(w, tensors, budget_s):
         "sample": f"{len(done)} of {w.B * w.H} (batch, head) pairs of the same workload, whole "
                   f"forward+backward in float64 numpy, {dt:.1f} s",
     }
+
+
+def fp8_forward(w, tensors, att, tb, args, k_fwd_bf16, f_fwd):
+    """The fp8 forward (fm_attn_fwd_fp8) on the same workload, inputs encoded
+    to E4M3 with per-tensor descales: W untimed calls, then K calls with the
+    library's kernel events around the forward kernel.  Mask-effective
+    4*D*nnz flops per call, against the fp8 dense matrix-core peak."""
+    import numpy as np
+    import torch
+    from column_sparse_masked_amd import _lib, masks
+    from column_sparse_masked_amd.api import to_device_u8
+    q8, k8, v8, ds = masks.fp8_inputs(tensors)
+    t8 = [to_device_u8(c, tb.device) for c in (q8, k8, v8)]
+    o8 = torch.empty((w.B, w.H, w.Sq, w.D), dtype=torch.bfloat16, device=tb.device)
+    l8 = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=tb.device)
+    for _ in range(args.warmup):
+        att.forward_fp8(*t8, ds, tb, o=o8, lse=l8)
+    evs = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        _lib.set_kernel_events(e0, e1)
+        att.forward_fp8(*t8, ds, tb, o=o8, lse=l8)
+    _lib.set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    achieved = f_fwd / (kms * 1e-3) / 1e12
+    return {"kernel": "attn_fwd_fp8_kernel", "dtype": "e4m3", "avg_kernel_ms": round(kms, 4),
+            "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+            "speedup_vs_bf16_forward_kernel": round(k_fwd_bf16 / kms, 3)}
 
 
 def main(argv=None):
@@ -299,6 +340,8 @@ def main(argv=None):
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if w.D == 128 and not args.no_fp8:
+        out["fp8_forward"] = fp8_forward(w, tensors, att, tb, args, k_fwd, f_fwd)
     if not args.no_cpu_baseline:
         print(f"# oracle sample on the host ({args.cpu_seconds:.0f} s budget)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, tensors, args.cpu_seconds)
