@@ -148,7 +148,7 @@ def cpu_baseline(w, tensors, budget_s):
     }
 
 
-def fp8_forward(w, tensors, att, tb, args, k_fwd_bf16, f_fwd):
+def fp8_forward(w, tensors, att, tb, args, k_fwd_bf16, f_fwd, tag):
     """The fp8 forward (fm_attn_fwd_fp8) on the same workload, inputs encoded
     to E4M3 with per-tensor descales: W untimed calls, then K calls with the
     library's kernel events around the forward kernel.  Mask-effective
@@ -180,6 +180,7 @@ def fp8_forward(w, tensors, att, tb, args, k_fwd_bf16, f_fwd):
     return {"kernel": "attn_fwd_fp8_kernel", "dtype": "e4m3", "avg_kernel_ms": round(kms, 4),
             "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+            "traffic": read_traffic("attn_fwd_fp8_kernel", tag, kernel_source_digest(["fwd_fp8.hip", "common.h"])),
             "speedup_vs_bf16_forward_kernel": round(k_fwd_bf16 / kms, 3)}
 
 
@@ -341,7 +342,7 @@ def main(argv=None):
         "cpu_baseline": None,
     }
     if w.D == 128 and not args.no_fp8:
-        out["fp8_forward"] = fp8_forward(w, tensors, att, tb, args, k_fwd, f_fwd)
+        out["fp8_forward"] = fp8_forward(w, tensors, att, tb, args, k_fwd, f_fwd, tag)
     if not args.no_cpu_baseline:
         print(f"# oracle sample on the host ({args.cpu_seconds:.0f} s budget)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, tensors, args.cpu_seconds)
