@@ -94,15 +94,21 @@ def test_fp8_repeated_and_interleaved_calls():
     assert att.read_tileinfo()["counters"][2:6].tolist() == [0, 0, 0, 0]
 
 
-def test_fp8_full_size_sliding_window():
-    """The 8K sliding-window workload (B=2, H=16, D=128, window 1024), in the
-    benchmark's launch configuration; sampled rows of two heads."""
-    w = M.config(2)
-    say(f"[fp8] full size config 2: drawing inputs")
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_fp8_full_size(cfg):
+    """The head-dim-128 evaluation workloads at full size (8K sliding window,
+    32K share-question, 128K documents, the context-parallel share), in the
+    benchmark's launch configuration; sampled rows (random, block edges and
+    the mask's boundary rows) of two heads."""
+    w = M.config(cfg)
+    say(f"[fp8] full size config {cfg} ({M.CONFIG_NAMES[cfg]}): drawing inputs")
     q8, k8, v8, ds = M.fp8_inputs(w.draw())
     go, gl, att = run_gpu_fp8(w, (q8, k8, v8), ds)
     check_tileinfo(w, att.read_tileinfo())
-    rng = np.random.default_rng(202)
-    rows = np.unique(np.concatenate([rng.integers(0, w.Sq, 40), [0, 1, 127, 128, 1023, 1024, w.Sq - 1]]))
+    rng = np.random.default_rng(200 + cfg)
+    lts = np.unique(np.clip(w.bounds[0, 0, :, 0].astype(np.int64), 1, w.Sq - 1))
+    edges = lts[np.linspace(0, lts.size - 1, min(8, lts.size)).astype(int)]
+    rows = np.unique(np.concatenate([rng.integers(0, w.Sq, 40), [0, 1, 127, 128, w.Sq - 1], edges - 1, edges]))
+    rows = rows[(rows >= 0) & (rows < w.Sq)]
     check_fp8(w, go, gl, (q8, k8, v8), ds, heads=[(0, 0), (w.B - 1, w.H - 1)], rows_of=lambda b, h: rows,
-              label="config 2 (sampled rows)")
+              label=f"config {cfg} (sampled rows)")
