@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <climits>
 #include <stdint.h>
 
 namespace fm {
@@ -97,6 +98,25 @@ typedef __amdgpu_buffer_rsrc_t BufRsrc;
 // zero-fills ragged tiles without branches.  bytes < 2^31.
 __device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Bounds of key k0 + t (forward kernels) for an elementwise-masked tile;
+// keys past the end get an interval that covers every row.
+__device__ __forceinline__ int4 load_bnd(BufRsrc bb, int k0, int Sk, int t) {
+  const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(bb, (k0 + t) * 16, 0, 0);
+  return (k0 + t < Sk) ? make_int4(x[0], x[1], x[2], x[3]) : make_int4(INT_MIN, INT_MAX, 0, 0);
+}
+
+// Hidden-row words of one key: word g has bit i set when the key's bounds
+// hide row q0 + 32 g + i (the union of its two intervals, clipped).
+__device__ __forceinline__ void hidden_rows(const int4 bd, int q0, uint32_t (&wd)[BQ / 32]) {
+#pragma unroll
+  for (int g = 0; g < BQ / 32; ++g) {
+    const int base = q0 + 32 * g;
+    auto clip = [&](int y) { return min(max(y, base), base + 32) - base; };
+    auto rows = [](int lo, int hi) { return hi > lo ? (~0u >> (32 - hi)) & (~0u << lo) : 0u; };
+    wd[g] = rows(clip(bd.x), clip(bd.y)) | rows(clip(bd.z), clip(bd.w));
+  }
 }
 
 __device__ __forceinline__ bf16x8 buf_load16(BufRsrc r, uint32_t byte_offset) {

@@ -123,21 +123,6 @@ __device__ __forceinline__ void store_vt8(const Stage8& r, uint8_t* vt, unsigned
   }
 }
 
-__device__ __forceinline__ int4 load_bnd8(BufRsrc bb, int k0, int Sk, int t) {
-  const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(bb, (k0 + t) * 16, 0, 0);
-  return (k0 + t < Sk) ? make_int4(x[0], x[1], x[2], x[3]) : make_int4(INT_MIN, INT_MAX, 0, 0);
-}
-
-__device__ __forceinline__ void hidden_rows8(const int4 bd, int q0, uint32_t (&wd)[BQ / 32]) {
-#pragma unroll
-  for (int g = 0; g < BQ / 32; ++g) {
-    const int base = q0 + 32 * g;
-    auto clip = [&](int y) { return min(max(y, base), base + 32) - base; };
-    auto rows = [](int lo, int hi) { return hi > lo ? (~0u >> (32 - hi)) & (~0u << lo) : 0u; };
-    wd[g] = rows(clip(bd.x), clip(bd.y)) | rows(clip(bd.z), clip(bd.w));
-  }
-}
-
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8_kernel(const Fp8FwdArgs a) {
   constexpr int ND = D8 / 32;   // 32-wide blocks of the head dimension
@@ -204,12 +189,12 @@ void attn_fwd_fp8_kernel(const Fp8FwdArgs a) {
         load_k8(st, kbase, k0, t);
         load_v8(st, vbase, k0, t);
         int4 breg = make_int4(0, 0, 0, 0);
-        if (block_masked(e_cur, k0) && t < BK) breg = load_bnd8(bbase, k0, Sk, t);
+        if (block_masked(e_cur, k0) && t < BK) breg = load_bnd(bbase, k0, Sk, t);
         store_k8(st, sm.k, t);
         store_vt8(st, sm.vt, t);
         if (block_masked(e_cur, k0) && t < BK) {
           uint32_t wd[BQ / 32];
-          hidden_rows8(breg, qb * BQ, wd);
+          hidden_rows(breg, qb * BQ, wd);
 #pragma unroll
           for (int g = 0; g < BQ / 32; ++g) sm.hid[0][g][t] = wd[g];
         }
@@ -310,7 +295,7 @@ void attn_fwd_fp8_kernel(const Fp8FwdArgs a) {
         int4 breg = make_int4(0, 0, 0, 0);
         if (has_next) {
           store_k8(st, sm.k, t);
-          if (nm_next && t < BK) breg = load_bnd8(bbase, k0n, Sk, t);
+          if (nm_next && t < BK) breg = load_bnd(bbase, k0n, Sk, t);
           load_v8(st, vbase, k0n, t);
         }
         half_pv(1, s1);
@@ -318,7 +303,7 @@ void attn_fwd_fp8_kernel(const Fp8FwdArgs a) {
         l_run += rs;
         if (nm_next && t < BK) {
           uint32_t wd[BQ / 32];
-          hidden_rows8(breg, qb * BQ, wd);
+          hidden_rows(breg, qb * BQ, wd);
 #pragma unroll
           for (int g = 0; g < BQ / 32; ++g) sm.hid[(tt + 1) & 1][g][t] = wd[g];
         }
