@@ -156,9 +156,11 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
  * is decode(c) * descale[x].  O (bf16) and LSE (fp32) are those of the exact
  * attention of these values, up to rounding: both products run on the fp8
  * matrix cores with fp32 accumulation, and the softmax probabilities are
- * rounded to E4M3 (relative error <= 2^-4) before the P.V product; the row
- * sums, and so LSE, use the unrounded fp32 probabilities.  Needs a tileinfo
- * from fm_tile_bounds for the same problem and bounds; no item is split.
+ * rounded to E4M3 (error at most 2^-4 relative, or 2^-10 absolute below
+ * 2^-6) before the P.V product; the row sums, and so LSE, use the unrounded
+ * fp32 probabilities.  NaN codes (0x7F, 0xFF) are not checked: they make the
+ * rows that see them NaN.  Needs a tileinfo from fm_tile_bounds for the same
+ * problem and bounds; no item is split.
  * Shares the forward's queue counters in tileinfo: calls on one tileinfo,
  * fp8 or not, must be ordered.  Errors: FM_ERR_UNSUPPORTED for head_dim 64
  * or a bad descale; otherwise as fm_attn_fwd.
