@@ -59,6 +59,11 @@ class MaskedAttention:
         """The forward with E4M3 inputs: q8, k8, v8 uint8 code tensors in the
         bf16 tensors' layouts, descale three floats (q, k, v)."""
         p = self.p
+        for name, t, rows in (("q8", q8, p.seqlen_q), ("k8", k8, p.seqlen_k), ("v8", v8, p.seqlen_k)):
+            if t.dtype != torch.uint8 or not t.is_contiguous() or \
+                    tuple(t.shape) != (p.batch, p.heads, rows, p.head_dim):
+                raise ValueError(f"{name}: expected contiguous uint8 E4M3 codes of shape "
+                                 f"{(p.batch, p.heads, rows, p.head_dim)}, got {t.dtype} {tuple(t.shape)}")
         if o is None:
             o = torch.empty((p.batch, p.heads, p.seqlen_q, p.head_dim), dtype=torch.bfloat16,
                             device=self.device)

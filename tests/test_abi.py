@@ -180,3 +180,19 @@ def test_fp8_forward_validation():
         q = _p(**kw)
         assert L.lib.fm_attn_fwd_fp8(ctypes.byref(q), fake, fake, fake, ds, fake, fake, fake, fake, None) \
             != L.FM_OK
+
+
+def test_fp8_binding_rejects_wrong_tensors():
+    """The Python wrapper checks dtype and shape of the code tensors before
+    calling the library (CPU tensors: nothing reaches a kernel)."""
+    import torch
+    from column_sparse_masked_amd.api import MaskedAttention
+    att = MaskedAttention.__new__(MaskedAttention)
+    att.p = _p(seqlen_q=5, seqlen_k=7)
+    att.device = torch.device("cpu")
+    ok_q = torch.zeros((1, 2, 5, 128), dtype=torch.uint8)
+    ok_k = torch.zeros((1, 2, 7, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        att.forward_fp8(ok_q.to(torch.bfloat16), ok_k, ok_k, (1.0, 1.0, 1.0), None)
+    with pytest.raises(ValueError):
+        att.forward_fp8(ok_q, ok_k[:, :, :6], ok_k, (1.0, 1.0, 1.0), None)
