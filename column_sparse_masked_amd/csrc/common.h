@@ -100,6 +100,16 @@ __device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// -inf where bit `bit` of `word` is set, else x: the bit, sign-extended to a
+// whole word, selects between the two bit patterns (two instructions, no
+// condition register).
+__device__ __forceinline__ float hide_if(uint32_t word, int bit, float x) {
+  const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)word, bit, 1);
+  float r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "s"(0xff800000u), "v"(x));
+  return r;
+}
+
 // Bounds of key k0 + t (forward kernels) for an elementwise-masked tile;
 // keys past the end get an interval that covers every row.
 __device__ __forceinline__ int4 load_bnd(BufRsrc bb, int k0, int Sk, int t) {

@@ -280,7 +280,7 @@ void attn_fwd_kernel(const FwdArgs a) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                   const int v = 4 * r + q;
-                  s[j][v] = (hq[q] >> li) & 1u ? -INFINITY : s[j][v];
+                  s[j][v] = hide_if(hq[q], li, s[j][v]);
                 }
               }
           }
