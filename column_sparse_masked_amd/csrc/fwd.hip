@@ -193,30 +193,29 @@ void attn_fwd_kernel(const FwdArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
 
     if (cnt > 0) {
-      // Q rows of this wave (B operand of S^T = K Q^T); issued first so that
-      // the key-block loads issued after it can stay in flight
-      bf16x8 qf[NS];
-      {
-        const uint32_t qoff = ((uint32_t)qrow * D + 8u * hh) * 2u;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) qf[s] = buf_load16(qbase, qoff + 32u * s);
-      }
       // ---- first key block: global -> registers -> LDS; second K block in flight ----
-      // List entries are read one block ahead through a buffer resource (a
-      // vector load whose value is the same in every lane).
+      // In the loop, list entries are read one block ahead through a buffer
+      // resource (a vector load whose value is the same in every lane).  The
+      // first two are scalar loads: waiting for a vector load would also wait
+      // for every vector load issued before it.
       const BufRsrc lbase = make_rsrc(lst, (uint32_t)cnt * 2u);
       auto list_at = [&](int i) -> uint32_t {
         return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(lbase, i * 2, 0, 0);
       };
       Stage<D> st;
-      int e_cur = __builtin_amdgcn_readfirstlane(list_at(0));
-      int e_next = cnt > 1 ? __builtin_amdgcn_readfirstlane(list_at(1)) : 0;
+      int e_cur = list_entry(lst, 0);
+      int e_next = cnt > 1 ? list_entry(lst, 1) : 0;
+      bf16x8 qf[NS];   // Q rows of this wave (B operand of S^T = K Q^T)
       {
         const int k0 = block_start(e_cur);
         load_k<D>(st, kbase, k0, t);
         load_v<D>(st, vbase, k0, t);
         int4 breg = make_int4(0, 0, 0, 0);
         if (block_masked(e_cur, k0) && t < BK) breg = load_bnd(bbase, k0, Sk, t);
+        // issued after the block's loads: the staging below waits for those only
+        const uint32_t qoff = ((uint32_t)qrow * D + 8u * hh) * 2u;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) qf[s] = buf_load16(qbase, qoff + 32u * s);
         store_k<D>(st, sm.k, t);
         store_vt<D>(st, sm.vt, t);
         if (block_masked(e_cur, k0) && t < BK) {
