@@ -166,9 +166,23 @@ void attn_fwd_fp8_kernel(const Fp8FwdArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
 
     if (cnt > 0) {
-      // Q row of this lane (B operand of S^T = K Q^T): head-dims 64 kk + 32 hh ..
-      i32x8 qf[2];
+      const BufRsrc lbase = make_rsrc(lst, (uint32_t)cnt * 2u);
+      auto list_at = [&](int i) -> uint32_t {
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(lbase, i * 2, 0, 0);
+      };
+      Stage8 st;
+      // the first two list entries by scalar loads (waiting for a vector load
+      // would also wait for every vector load issued before it)
+      int e_cur = list_entry(lst, 0);
+      int e_next = cnt > 1 ? list_entry(lst, 1) : 0;
+      i32x8 qf[2];   // Q row of this lane (B operand of S^T = K Q^T): head-dims 64 kk + 32 hh ..
       {
+        const int k0 = block_start(e_cur);
+        load_k8(st, kbase, k0, t);
+        load_v8(st, vbase, k0, t);
+        int4 breg = make_int4(0, 0, 0, 0);
+        if (block_masked(e_cur, k0) && t < BK) breg = load_bnd(bbase, k0, Sk, t);
+        // issued after the block's loads: the staging below waits for those only
         const uint32_t qoff = (uint32_t)qrow * D8 + 32u * hh;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -176,20 +190,6 @@ void attn_fwd_fp8_kernel(const Fp8FwdArgs a) {
           const i32x4 hi = load16(qbase, qoff + 64u * kk + 16u);
           qf[kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-      }
-      const BufRsrc lbase = make_rsrc(lst, (uint32_t)cnt * 2u);
-      auto list_at = [&](int i) -> uint32_t {
-        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(lbase, i * 2, 0, 0);
-      };
-      Stage8 st;
-      int e_cur = __builtin_amdgcn_readfirstlane(list_at(0));
-      int e_next = cnt > 1 ? __builtin_amdgcn_readfirstlane(list_at(1)) : 0;
-      {
-        const int k0 = block_start(e_cur);
-        load_k8(st, kbase, k0, t);
-        load_v8(st, vbase, k0, t);
-        int4 breg = make_int4(0, 0, 0, 0);
-        if (block_masked(e_cur, k0) && t < BK) breg = load_bnd(bbase, k0, Sk, t);
         store_k8(st, sm.k, t);
         store_vt8(st, sm.vt, t);
         if (block_masked(e_cur, k0) && t < BK) {
