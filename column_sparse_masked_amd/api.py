@@ -26,7 +26,12 @@ def to_device_bounds(bounds: np.ndarray, device="cuda") -> torch.Tensor:
 
 
 class MaskedAttention:
-    """One problem shape: owns the tileinfo and backward workspace buffers."""
+    """One problem shape: owns the tileinfo and backward workspace buffers.
+
+    Every tensor handed to an entry point is checked before the library is
+    called: dtype, shape of this problem, contiguity and device.  A tensor
+    that is too small, of the wrong type or strided would make the kernels
+    read or write outside it, so a mismatch raises ValueError instead."""
 
     def __init__(self, batch, heads, mask_heads, seqlen_q, seqlen_k, head_dim,
                  softmax_scale=None, device="cuda"):
@@ -41,17 +46,46 @@ class MaskedAttention:
     def for_workload(cls, w, device="cuda"):
         return cls(w.B, w.H, w.Hm, w.Sq, w.Sk, w.D, w.scale, device)
 
+    # ---- argument checks ----
+    def _shape(self, kind):
+        p = self.p
+        return {"q": (p.batch, p.heads, p.seqlen_q, p.head_dim),
+                "k": (p.batch, p.heads, p.seqlen_k, p.head_dim),
+                "rows": (p.batch, p.heads, p.seqlen_q),
+                "bounds": (p.batch, p.mask_heads, p.seqlen_k, 4)}[kind]
+
+    def _check(self, name, t, dtype, kind):
+        shape = self._shape(kind)
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+        if t.dtype != dtype or tuple(t.shape) != shape:
+            raise ValueError(f"{name}: expected {dtype} of shape {shape}, got {t.dtype} {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous tensor (the kernels ignore strides)")
+        same_device = t.device.type == self.device.type and (
+            self.device.index is None or t.device.index == self.device.index)
+        if not same_device:
+            raise ValueError(f"{name}: on {t.device}, expected {self.device}")
+
+    def _check_all(self, specs):
+        for name, t, dtype, kind in specs:
+            self._check(name, t, dtype, kind)
+
     # ---- the three entry points ----
     def tile_bounds(self, bounds, stream=None):
+        self._check("bounds", bounds, torch.int32, "bounds")
         _lib.fm_tile_bounds(self.p, bounds, self.buf.tileinfo, stream)
 
     def forward(self, q, k, v, bounds, o=None, lse=None, stream=None):
         p = self.p
         if o is None:
-            o = torch.empty((p.batch, p.heads, p.seqlen_q, p.head_dim), dtype=torch.bfloat16,
-                            device=self.device)
+            o = torch.empty(self._shape("q"), dtype=torch.bfloat16, device=self.device)
         if lse is None:
-            lse = torch.empty((p.batch, p.heads, p.seqlen_q), dtype=torch.float32, device=self.device)
+            lse = torch.empty(self._shape("rows"), dtype=torch.float32, device=self.device)
+        bf = torch.bfloat16
+        self._check_all([("q", q, bf, "q"), ("k", k, bf, "k"), ("v", v, bf, "k"),
+                         ("bounds", bounds, torch.int32, "bounds"), ("o", o, bf, "q"),
+                         ("lse", lse, torch.float32, "rows")])
         _lib.fm_attn_fwd(p, q, k, v, bounds, self.buf.tileinfo, o, lse, stream)
         return o, lse
 
@@ -59,23 +93,26 @@ class MaskedAttention:
         """The forward with E4M3 inputs: q8, k8, v8 uint8 code tensors in the
         bf16 tensors' layouts, descale three floats (q, k, v)."""
         p = self.p
-        for name, t, rows in (("q8", q8, p.seqlen_q), ("k8", k8, p.seqlen_k), ("v8", v8, p.seqlen_k)):
-            if t.dtype != torch.uint8 or not t.is_contiguous() or \
-                    tuple(t.shape) != (p.batch, p.heads, rows, p.head_dim):
-                raise ValueError(f"{name}: expected contiguous uint8 E4M3 codes of shape "
-                                 f"{(p.batch, p.heads, rows, p.head_dim)}, got {t.dtype} {tuple(t.shape)}")
+        self._check_all([("q8", q8, torch.uint8, "q"), ("k8", k8, torch.uint8, "k"),
+                         ("v8", v8, torch.uint8, "k")])
         if o is None:
-            o = torch.empty((p.batch, p.heads, p.seqlen_q, p.head_dim), dtype=torch.bfloat16,
-                            device=self.device)
+            o = torch.empty(self._shape("q"), dtype=torch.bfloat16, device=self.device)
         if lse is None:
-            lse = torch.empty((p.batch, p.heads, p.seqlen_q), dtype=torch.float32, device=self.device)
+            lse = torch.empty(self._shape("rows"), dtype=torch.float32, device=self.device)
+        self._check_all([("bounds", bounds, torch.int32, "bounds"), ("o", o, torch.bfloat16, "q"),
+                         ("lse", lse, torch.float32, "rows")])
         _lib.fm_attn_fwd_fp8(p, q8, k8, v8, descale, bounds, self.buf.tileinfo, o, lse, stream)
         return o, lse
 
     def backward(self, q, k, v, o, dout, lse, bounds, dq=None, dk=None, dv=None, stream=None):
+        bf = torch.bfloat16
+        self._check_all([("q", q, bf, "q"), ("k", k, bf, "k"), ("v", v, bf, "k"), ("o", o, bf, "q"),
+                         ("dout", dout, bf, "q"), ("lse", lse, torch.float32, "rows"),
+                         ("bounds", bounds, torch.int32, "bounds")])
         dq = torch.empty_like(q) if dq is None else dq
         dk = torch.empty_like(k) if dk is None else dk
         dv = torch.empty_like(v) if dv is None else dv
+        self._check_all([("dq", dq, bf, "q"), ("dk", dk, bf, "k"), ("dv", dv, bf, "k")])
         _lib.fm_attn_bwd(self.p, q, k, v, o, dout, lse, bounds, self.buf.tileinfo, dq, dk, dv,
                          self.buf.workspace, stream)
         return dq, dk, dv

@@ -23,7 +23,7 @@
  *
  * Memory: every pointer is a device pointer owned by the caller.  The library
  * allocates nothing and keeps no per-call state; it caches only the device's
- * compute-unit count.  `tileinfo` (size from fm_tileinfo_layout) is written by
+ * compute-unit count.  `tileinfo` (size from fm_tileinfo_layout_query) is written by
  * fm_tile_bounds and then read by fm_attn_fwd / fm_attn_bwd, which also use
  * work counters and scratch slots inside it; the counters are left at zero
  * when a call's kernels finish.  Calls that share a tileinfo must therefore be
@@ -134,14 +134,28 @@ fm_status fm_tile_bounds(const fm_problem* p, const int32_t* bounds, void* tilei
 
 /*
  * fm_attn_fwd - masked scaled-dot-product attention forward.
- * For every query row i: O_i = sum_j softmax_j(scale * q_i.k_j, masked -> -inf) v_j,
+ * "FlashMask-3 targets masked distributed attention on Hopper GPUs",
+ * In-depth insight (the abstract): the method is attention under a structured
+ * mask held as four query-axis boundary vectors per key position, computed by
+ * a mask-aware kernel that works only where the mask leaves keys visible.
+ * This is that forward:
+ * for every query row i: O_i = sum_j softmax_j(scale * q_i.k_j, masked -> -inf) v_j,
  * LSE_i = log sum_j exp(scale * q_i.k_j) over visible j (+inf if none).
+ * Arguments: q bf16 [B][H][Sq][D], k and v bf16 [B][H][Sk][D], bounds int32
+ * [B][Hm][Sk][4] (device, read only); tileinfo from fm_tile_bounds for the
+ * same problem and bounds (device, read, and its forward counters and
+ * partial-result slots written); o bf16 [B][H][Sq][D] and lse fp32 [B][H][Sq]
+ * (device, written).  All are caller-owned.
  * Skipped tiles are never touched; the elementwise mask is evaluated only on
  * partial tiles.  bf16 MFMA with fp32 accumulation; O rounded to nearest even.
- * Needs a tileinfo from fm_tile_bounds for the same problem and bounds.  The
- * query blocks that fm_tile_bounds marked for splitting are computed as two
- * halves of their key blocks, whose partial results (in tileinfo) a second
- * kernel merges; the call writes O and LSE of every row either way.
+ * The query blocks that fm_tile_bounds marked for splitting are computed as
+ * two halves of their key blocks, whose partial results (in tileinfo) a
+ * second kernel merges; the call writes O and LSE of every row either way.
+ * Errors: FM_ERR_NULL for a missing tensor that the problem needs (q, o, lse
+ * when there are query rows; k, v, bounds when there are keys; tileinfo
+ * always), FM_ERR_ALIGN for a tensor not 16-byte aligned (lse: 4 bytes,
+ * tileinfo: 256 bytes), the problem's own checks, FM_ERR_HIP for a launch
+ * the runtime rejects.  Sq = 0 or B = 0 enqueues nothing.
  */
 fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const void* v,
                       const int32_t* bounds, void* tileinfo, void* o, float* lse, void* stream);
@@ -171,14 +185,28 @@ fm_status fm_attn_fwd_fp8(const fm_problem* p, const void* q, const void* k, con
 
 /*
  * fm_attn_bwd - gradients of fm_attn_fwd given dL/dO.
- * With P = exp(scale * q.k - LSE) (0 where masked), dP = dO v^T,
+ * "FlashMask-3 targets masked distributed attention on Hopper GPUs",
+ * In-depth insight (the abstract): the mask-aware kernel serves long-context
+ * training, so it provides the backward of the masked attention as well,
+ * again visiting only the tiles the boundary vectors leave visible.  The
+ * gradients are the exact ones of the forward above:
+ * with P = exp(scale * q.k - LSE) (0 where masked), dP = dO v^T,
  * Delta_i = sum_d dO_id O_id, dS = P (dP - Delta):
  *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
- * `o` and `lse` are the forward's outputs.  `workspace` must hold
+ * Arguments: q, o, dout bf16 [B][H][Sq][D], k, v bf16 [B][H][Sk][D], lse
+ * fp32 [B][H][Sq] (`o` and `lse` the forward's outputs), bounds int32
+ * [B][Hm][Sk][4], tileinfo from fm_tile_bounds (all device, read; the
+ * tileinfo's backward counters are written); dq bf16 [B][H][Sq][D], dk, dv
+ * bf16 [B][H][Sk][D] (device, written).  `workspace` must hold
  * fm_bwd_workspace_bytes bytes, 16-byte aligned; its contents on entry do not
- * matter.  Three kernels: Delta; dK and dV key-stationary over the tiles of
- * each key block; dQ query-stationary over the tiles of each query block
- * (S and dP recomputed, no atomics).  The results are deterministic.
+ * matter.  All are caller-owned.  Three kernels: Delta; dK and dV
+ * key-stationary over the tiles of each key block; dQ query-stationary over
+ * the tiles of each query block (S and dP recomputed, no atomics).  The
+ * results are deterministic.
+ * Errors: FM_ERR_NULL for a missing tensor that the problem needs,
+ * FM_ERR_ALIGN as fm_attn_fwd (workspace: 16 bytes), the problem's own
+ * checks, FM_ERR_HIP for a launch the runtime rejects.  With Sq = 0, dK and
+ * dV are zero-filled; with Sk = 0, dQ is written as zero.
  */
 fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
                       const void* o, const void* dout, const float* lse,

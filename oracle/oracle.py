@@ -179,6 +179,40 @@ def head_backward(qh, kh, vh, doh, bounds_h, scale, rows=None, lse=None):
     return dQ, dK, dV
 
 
+def column_gradients(qh, kh, vh, doh, bounds_h, scale, cols, rows, o_rows, lse_rows):
+    """dK[cols] and dV[cols] for one (batch, head), complete when ``rows``
+    holds every query row that sees one of ``cols``; ``o_rows`` and
+    ``lse_rows`` are the forward's O and LSE of those rows.
+
+    The same gradients as head_backward, restricted to a few key columns so
+    that heavily seen columns of long sequences stay affordable: for
+    j in cols, P_ij = exp(scale q_i.k_j - LSE_i) (0 where masked),
+    dP_ij = dO_i.v_j, Delta_i = dO_i.O_i (equal to sum_j P_ij dP_ij, because
+    O_i = sum_j P_ij v_j), dS_ij = P_ij (dP_ij - Delta_i),
+    dK_j = scale sum_i dS_ij q_i, dV_j = sum_i P_ij dO_i."""
+    cols = np.asarray(cols)
+    rows = np.asarray(rows)
+    dK = np.zeros((cols.size, kh.shape[1]))
+    dV = np.zeros((cols.size, vh.shape[1]))
+    for s0 in range(0, rows.size, STRIP):
+        r = rows[s0:s0 + STRIP]
+        lse = lse_rows[s0:s0 + r.size]
+        live = np.isfinite(lse)
+        if not live.any():
+            continue
+        r, lse, o = r[live], lse[live], o_rows[s0:s0 + STRIP][live]
+        M = dense_mask(bounds_h[cols], r)
+        S = scale * (qh[r] @ kh[cols].T)
+        P = np.exp(S - lse[:, None])
+        P[M] = 0.0
+        dP = doh[r] @ vh[cols].T
+        delta = (doh[r] * o).sum(axis=1)
+        dS = P * (dP - delta[:, None])
+        dK += scale * (dS.T @ qh[r])
+        dV += P.T @ doh[r]
+    return dK, dV
+
+
 def backward(q, k, v, do, bounds, scale, lse=None):
     """dQ, dK, dV (float64) for float64 inputs."""
     B, H, Sq, D = q.shape

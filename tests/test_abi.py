@@ -196,3 +196,65 @@ def test_fp8_binding_rejects_wrong_tensors():
         att.forward_fp8(ok_q.to(torch.bfloat16), ok_k, ok_k, (1.0, 1.0, 1.0), None)
     with pytest.raises(ValueError):
         att.forward_fp8(ok_q, ok_k[:, :, :6], ok_k, (1.0, 1.0, 1.0), None)
+
+
+def _cpu_wrapper(**kw):
+    """A MaskedAttention whose buffers are never allocated (CPU tensors:
+    whatever the checks let through would fail in the library, not a kernel)."""
+    import torch
+    from column_sparse_masked_amd.api import MaskedAttention
+    att = MaskedAttention.__new__(MaskedAttention)
+    att.p = _p(**kw)
+    att.device = torch.device("cpu")
+    return att
+
+
+def test_binding_rejects_wrong_bf16_tensors():
+    """forward / backward / tile_bounds check dtype, shape, contiguity and
+    device of every tensor before the library sees a pointer."""
+    import torch
+    att = _cpu_wrapper(batch=1, heads=2, mask_heads=1, seqlen_q=5, seqlen_k=7, head_dim=64)
+    bf = torch.bfloat16
+    q = torch.zeros((1, 2, 5, 64), dtype=bf)
+    k = torch.zeros((1, 2, 7, 64), dtype=bf)
+    o = torch.zeros_like(q)
+    lse = torch.zeros((1, 2, 5), dtype=torch.float32)
+    bounds = torch.zeros((1, 1, 7, 4), dtype=torch.int32)
+    fwd_ok = dict(q=q, k=k, v=k, bounds=bounds, o=o, lse=lse)
+    bad = {
+        "q": [q.float(), q[:, :, :4], torch.zeros((1, 2, 64, 5), dtype=bf).transpose(2, 3)],
+        "k": [k.to(torch.float16), k[:, :1]],
+        "v": [k[:, :, :6], torch.zeros((1, 2, 7, 128), dtype=bf)],
+        "bounds": [bounds.to(torch.int64), bounds[:, :, :6], torch.zeros((1, 1, 4, 7), dtype=torch.int32).transpose(2, 3)],
+        "o": [o.float(), o[..., :32]],
+        "lse": [lse.double(), lse[:, :, :4]],
+    }
+    for name, variants in bad.items():
+        for t in variants:
+            args = dict(fwd_ok)
+            args[name] = t
+            with pytest.raises(ValueError, match=name):
+                att.forward(**args)
+    bwd_ok = dict(q=q, k=k, v=k, o=o, dout=q, lse=lse, bounds=bounds, dq=torch.zeros_like(q),
+                  dk=torch.zeros_like(k), dv=torch.zeros_like(k))
+    bad_bwd = {"dout": q[:, :, :3], "dq": q.float(), "dk": k[..., :32], "dv": torch.zeros((1, 2, 8, 64), dtype=bf),
+               "lse": lse.half(), "o": o[:, :1]}
+    for name, t in bad_bwd.items():
+        args = dict(bwd_ok)
+        args[name] = t
+        with pytest.raises(ValueError, match=name):
+            att.backward(**args)
+    with pytest.raises(ValueError, match="bounds"):
+        att.tile_bounds(bounds[:, :, :5])
+    with pytest.raises(ValueError, match="bounds"):
+        att.tile_bounds(bounds.numpy())
+
+
+def test_binding_rejects_tensors_on_another_device():
+    import torch
+    att = _cpu_wrapper(seqlen_q=5, seqlen_k=7, head_dim=64)
+    att.device = torch.device("cuda", 0)   # tensors below live on the CPU
+    bounds = torch.zeros((1, 1, 7, 4), dtype=torch.int32)
+    with pytest.raises(ValueError, match="expected cuda"):
+        att.tile_bounds(bounds)
+

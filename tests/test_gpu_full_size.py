@@ -126,7 +126,7 @@ def test_full_size_parity(cfg):
     rng = np.random.default_rng(100 + cfg)
     q, k, v, do = tensors
     up = oracle.upcast_bf16
-    heads = sorted({(0, 0), (w.B - 1, w.H - 1)})
+    heads = sorted({(0, 0), (0, w.H // 2), (w.B - 1, w.H - 1)})
     errs = {"o": 0.0, "lse": 0.0}
     num = {n: 0.0 for n in ("dq", "dk", "dv")}
     den = {n: 0.0 for n in ("dq", "dk", "dv")}
@@ -164,6 +164,53 @@ def test_full_size_parity(cfg):
         assert e <= GRAD_TOL, f"{n} rel-L2 {e} on the sample"
     say(f"[full] config {cfg}: O max-abs {errs['o']:.2e}, LSE {errs['lse']:.2e}, "
         + ", ".join(f"{n} rel-L2 {e:.2e}" for n, e in rel.items()))
+
+
+def _heaviest_key_block(bounds_h, Sq, BK=128):
+    """The key block whose columns are seen by the most query rows (the
+    longest key-stationary item of the backward): per column, Sq minus the
+    rows its two intervals hide, then the block maximum."""
+    b = np.clip(bounds_h.astype(np.int64), 0, Sq)
+    l1 = np.maximum(b[:, 1] - b[:, 0], 0)
+    l2 = np.maximum(b[:, 3] - b[:, 2], 0)
+    ov = np.maximum(np.minimum(b[:, 1], b[:, 3]) - np.maximum(b[:, 0], b[:, 2]), 0)
+    seen = Sq - (l1 + l2 - np.where((l1 > 0) & (l2 > 0), ov, 0))
+    return int(np.argmax(seen)) // BK
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_heavy_key_columns(cfg):
+    """dK and dV of the whole key block that the most query rows see, compared
+    element by element with the oracle over every row that sees it (the
+    backward's longest key-stationary item: the shared question's first
+    block, seen by all 32768 rows, at the share-question workload; the first
+    block of the longest document, seen by its 43257 rows, at the 128K
+    documents workload; the densest block of the context-parallel share).
+    The oracle runs the forward over those rows for their LSE and O, then
+    the gradients of the block's columns alone."""
+    import torch
+    w = M.config(cfg)
+    b, h = 0, 0
+    bh = w.bounds[b, oracle.mask_head(w.bounds, h)]
+    kb = _heaviest_key_block(bh, w.Sq)
+    cols = np.arange(kb * 128, min(w.Sk, kb * 128 + 128))
+    rows = oracle.rows_seeing(bh, w.Sq, cols)
+    say(f"[heavy] config {cfg}: key block {kb} seen by {rows.size} rows; drawing inputs")
+    tensors = w.draw()
+    _, g = _run(w, tensors)
+    ci = torch.as_tensor(cols, device=g["dk"].device)
+    got = {n: g[n][b, h, ci].float().cpu().numpy() for n in ("dk", "dv")}
+    del g
+    say(f"[heavy] config {cfg}: GPU done; oracle over {rows.size} rows")
+    q, k, v, do = tensors
+    up = oracle.upcast_bf16
+    qh, kh, vh, doh = up(q[b, h]), up(k[b, h]), up(v[b, h]), up(do[b, h])
+    o_r, lse_r = oracle.head_forward(qh, kh, vh, bh, w.scale, rows)
+    rdk, rdv = oracle.column_gradients(qh, kh, vh, doh, bh, w.scale, cols, rows, o_r, lse_r)
+    for n, ref in (("dk", rdk), ("dv", rdv)):
+        e = rel_l2(got[n], ref)
+        say(f"[heavy] config {cfg}: {n} of key block {kb} rel-L2 {e:.2e}")
+        assert e <= GRAD_TOL, f"{n} rel-L2 {e} on key block {kb}"
 
 
 def test_context_parallel_shares_add_up():

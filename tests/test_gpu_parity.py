@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from column_sparse_masked_amd import masks as M
-from _parity import check_full, check_tileinfo, run_gpu, say
+from _parity import GRAD_TOL, check_full, check_lse, check_tileinfo, rel_l2, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -98,6 +98,95 @@ def test_small_problem_parity(name):
     check_full(w, got, tensors, name)
 
 
+def _scaled_bf16(bits, mult):
+    """bf16 bits times a power of two (exact: only the exponent changes)."""
+    return M.bf16_bits(M.bf16_to_f32(bits) * np.float32(mult))
+
+
+LARGE_LOGIT_CASES = {
+    # (workload, Q multiplier, K multiplier on the spike columns)
+    # split items (24 key blocks per query block, 48 items): both halves and
+    # the merge see logits in the hundreds
+    "large_logits_split_unmasked_S3000_D128": (
+        lambda: M.custom(M.empty_bounds(3000, 3000), B=1, H=2, Sq=3000, D=128, seed=44), 8.0, 4.0),
+    "large_logits_causal_docs_S1500_D64": (
+        lambda: M.custom(M.causal_document_bounds([900, 600]), B=1, H=2, Sq=1500, D=64, seed=45), 16.0, 4.0),
+    "large_logits_sliding_S1300_D128": (
+        lambda: M.custom(M.sliding_window_bounds(1300, 700), B=1, H=2, Sq=1300, D=128, seed=46), 16.0, 2.0),
+}
+
+
+def _o_bound_large_logits(w, q, k, v, lse_ref):
+    """The P-dependent part of the per-element bound of the forward's O
+    error, from what the kernel rounds: P (relative to a running reference
+    up to 2^8 below the row maximum) is rounded to bf16 (unit roundoff 2^-8)
+    for the P V product while the row sum keeps the unrounded P, so the
+    numerator's weights carry a relative error of at most 2^-8 each:
+    |dO_id| <= 2^-8 sum_j P_ij |v_jd|.  An item split in two rounds each
+    half's O to bf16 before the exact log-sum-exp merge, which adds at most
+    2^-8 sum_p w_p |O_p,id| <= 2^-8 sum_j P_ij |v_jd| more: 2^-7 in all.
+    The caller adds the final bf16 rounding of O (2^-8 |O_id|) and 1e-4
+    max|v| for the fp32 scores and sums.  Where O is an average of many
+    keys (N(0, 1) inputs) this is far below the 2e-2 max-abs contract; where
+    one key dominates a row, |O| approaches max|v| ~ 4.5 and bf16 alone
+    cannot hold O to 2e-2 (its half-ulp at 4 is 2^-6), so the stress cases
+    are held to this bound."""
+    import oracle
+    up = oracle.upcast_bf16
+    out = np.zeros((w.B, w.H, w.Sq, w.D))
+    for b in range(w.B):
+        for h in range(w.H):
+            bh = w.bounds[b, oracle.mask_head(w.bounds, h)]
+            qh, kh, vh = up(q[b, h]), up(k[b, h]), up(v[b, h])
+            S = w.scale * (qh @ kh.T)
+            L = lse_ref[b, h]
+            live = np.isfinite(L)
+            P = np.zeros_like(S)
+            P[live] = np.exp(S[live] - L[live, None])
+            P[oracle.dense_mask(bh, np.arange(w.Sq))] = 0.0
+            out[b, h] = 2.0 ** -7 * (P @ np.abs(vh))
+    return out
+
+
+@pytest.mark.parametrize("name", list(LARGE_LOGIT_CASES))
+def test_large_logit_parity(name):
+    """Scores far from N(0, 1): Q multiplied by 8 or 16, and the K rows of
+    spike columns (every 97th key of the second half of the keys) by a
+    further 2 or 4, so that LSE / scale runs into the hundreds or thousands
+    and a row's running maximum jumps by far more than the forward's lazy
+    rescale threshold partway along the row.  This exercises the forward's
+    rescale of O and l, the split items' merge, and the backward's row term
+    -LSE / scale carried as a (hi, lo) bf16 pair.  LSE and the gradients are
+    held to the usual contract; O to the per-element bound derived from its
+    bf16 roundings (_o_bound_large_logits), since one key dominates many
+    rows here and |O| approaches max|v|."""
+    import oracle
+    make, qm, km = LARGE_LOGIT_CASES[name]
+    w = make()
+    q, k, v, do = w.draw()
+    q = _scaled_bf16(q, qm)
+    spikes = np.arange(w.Sk // 2, w.Sk)
+    spikes = spikes[spikes % 97 == 0]
+    k = k.copy()
+    k[:, :, spikes] = _scaled_bf16(k[:, :, spikes], km)
+    say(f"[parity] {name}: Q x{qm}, K x{km} on {spikes.size} spike columns")
+    up = oracle.upcast_bf16
+    ro, rl, rdq, rdk, rdv = oracle.attention(up(q), up(k), up(v), up(do), w.bounds, w.scale)
+    fin = np.isfinite(rl)
+    assert np.abs(rl[fin]).max() / w.scale > 200, "the case does not reach large logits"
+    got, _ = run_gpu(w, (q, k, v, do))
+    bound = _o_bound_large_logits(w, q, k, v, rl) + 2.0 ** -8 * np.abs(ro) + 1e-4 * np.abs(up(v)).max()
+    err = np.abs(got["o"] - ro)
+    ratio = float((err / bound).max())
+    check_lse(got["lse"], rl)
+    errs = {n: rel_l2(got[n], r) for n, r in (("dq", rdq), ("dk", rdk), ("dv", rdv))}
+    say(f"{name}: O max-abs {err.max():.3e}, max error/bound {ratio:.3f}, "
+        + " ".join(f"{n} {e:.3e}" for n, e in errs.items()))
+    assert ratio <= 1.0, f"O error above its bound ({ratio})"
+    for n, e in errs.items():
+        assert e <= GRAD_TOL, f"{name} {n} rel-L2 {e}"
+
+
 def test_empty_key_set():
     """Sk = 0: every row is fully masked: O = 0, LSE = +inf, dQ = 0."""
     w = M.custom(np.zeros((0, 4), np.int32), B=1, H=2, Sq=200, D=128, seed=40)
@@ -142,8 +231,9 @@ def test_empty_query_set():
 
 def test_repeated_calls_reuse_tileinfo():
     """The work counters inside tileinfo are reset by the kernels themselves:
-    calling forward and backward again gives the same results (forward and
-    dK/dV bit-identical; dQ within tolerance, its atomics are unordered)."""
+    calling forward and backward again gives bit-identical results (every
+    output element is computed by one workgroup in a fixed order, with no
+    atomic accumulation), and every queue and exit counter is back at zero."""
     import torch
     from column_sparse_masked_amd.api import MaskedAttention, to_device_bf16, to_device_bounds
     w = M.custom(M.sliding_window_bounds(1024, 300), B=1, H=4, Sq=1024, D=128, seed=42)
@@ -160,11 +250,7 @@ def test_repeated_calls_reuse_tileinfo():
         outs.append([x.clone() for x in (o, lse, dq, dk, dv)])
     torch.cuda.synchronize()
     for later in outs[1:]:
-        for a, b in zip(outs[0][:2], later[:2]):
-            assert torch.equal(a, b)
-        for a, b in zip(outs[0][3:], later[3:]):
-            assert torch.equal(a, b)
-        d = (outs[0][2].float() - later[2].float()).norm() / outs[0][2].float().norm()
-        assert d.item() < 1e-3
+        for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), outs[0], later):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{name} differs between calls"
     ti = att.read_tileinfo()
-    assert ti["counters"][2:6].tolist() == [0, 0, 0, 0]
+    assert ti["counters"][2:8].tolist() == [0] * 6

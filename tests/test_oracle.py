@@ -205,6 +205,36 @@ def test_row_subset_gradients_complete_for_their_columns():
     np.testing.assert_allclose(o, full[0][rows[::7]], atol=1e-14)
 
 
+@pytest.mark.parametrize("family", ["documents", "share_question", "fully_masked_band"])
+def test_column_gradients_match_sdpa(family):
+    """column_gradients (dK, dV of a few key columns from the rows that see
+    them, with Delta from dO.O) against torch's float64 SDPA autograd on the
+    dense mask, and against head_backward's columns."""
+    rng = np.random.default_rng(21)
+    S, D, scale = 300, 16, 0.27
+    if family == "documents":
+        b = M.causal_document_bounds(M.composition(rng, S, 5))
+    elif family == "share_question":
+        b = M.share_question_bounds(60, M.composition(rng, S - 60, 4))
+    else:   # rows 40..70 see nothing
+        b = np.stack([np.full(S, 40), np.full(S, 70), np.zeros(S), np.arange(S)], 1)
+    q, k, v, do = (_rand(rng, S, D) for _ in range(4))
+    vis = ~O.dense_mask(b, np.arange(S))
+    live = vis.any(axis=1)
+    # torch's SDPA gives NaN rows where nothing is visible: zero those rows' dO
+    do_t = do * live[:, None]
+    _, _, rdk, rdv = _torch_sdpa(q, k, v, do_t, vis | ~live[:, None], scale)
+    cols = np.array([0, 3, 59, 60, 61, 150, 299])
+    rows = O.rows_seeing(b, S, cols)
+    o, lse = O.head_forward(q, k, v, b, scale, rows)
+    dk, dv = O.column_gradients(q, k, v, do, b, scale, cols, rows, o, lse)
+    np.testing.assert_allclose(dk, rdk[cols], atol=1e-11)
+    np.testing.assert_allclose(dv, rdv[cols], atol=1e-11)
+    full = _oracle_head(q, k, v, do, b, scale)
+    np.testing.assert_allclose(dk, full[3][cols], atol=1e-12)
+    np.testing.assert_allclose(dv, full[4][cols], atol=1e-12)
+
+
 # --------------------------------------------------------------------------- #
 # tile classification                                                         #
 # --------------------------------------------------------------------------- #
@@ -322,6 +352,29 @@ def test_batched_entry_points_match_heads():
     for h in range(H):
         r = O.head_forward(q[1, h], k[1, h], v[1, h], bounds[1, 0], 0.35)[0]
         np.testing.assert_array_equal(o1[1, h], r)
+
+
+# --------------------------------------------------------------------------- #
+# inputs                                                                       #
+# --------------------------------------------------------------------------- #
+def test_upcast_bf16_matches_torch_on_every_pattern():
+    """Every oracle operand goes through upcast_bf16: checked against torch's
+    own bfloat16 -> float64 conversion on all 65536 bit patterns (signed
+    zeros, subnormals, infinities and NaN positions included)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = O.upcast_bf16(bits)
+    assert got.dtype == np.float64 and got.shape == bits.shape
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2 * 127
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # a few values by hand: 1.0, -2.0, the smallest subnormal, +inf
+    hand = O.upcast_bf16(np.array([0x3F80, 0xC000, 0x0001, 0x7F80], np.uint16))
+    assert hand.tolist() == [1.0, -2.0, 2.0 ** -133, np.inf]
+    # shape and order are kept (a transposed or reshaped view maps element-wise)
+    grid = bits[:12].reshape(3, 4).T
+    assert np.array_equal(O.upcast_bf16(grid), ref[:12].reshape(3, 4).T)
 
 
 # --------------------------------------------------------------------------- #
