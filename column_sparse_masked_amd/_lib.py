@@ -14,7 +14,7 @@ from dataclasses import dataclass
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfm.so")
 
-FM_OK, FM_ERR_NULL, FM_ERR_SHAPE, FM_ERR_UNSUPPORTED, FM_ERR_ALIGN, FM_ERR_HIP = range(6)
+FM_OK, FM_ERR_NULL, FM_ERR_SHAPE, FM_ERR_UNSUPPORTED, FM_ERR_ALIGN, FM_ERR_HIP, FM_ERR_SCRATCH = range(7)
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m column_sparse_masked_amd.build`")
@@ -73,8 +73,10 @@ lib.fm_tile_bounds.argtypes = [_P, _vp, _vp, _vp]
 lib.fm_attn_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.fm_attn_fwd_fp8.argtypes = [_P, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_float), _vp, _vp, _vp, _vp, _vp]
 lib.fm_attn_bwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+lib.fm_attn_bwd_noalloc.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 for _f in ("fm_tile_shape", "fm_tileinfo_layout_query", "fm_bwd_workspace_bytes",
-           "fm_device_cu_count", "fm_tile_bounds", "fm_attn_fwd", "fm_attn_bwd"):
+           "fm_device_cu_count", "fm_tile_bounds", "fm_attn_fwd", "fm_attn_fwd_fp8", "fm_attn_bwd",
+           "fm_attn_bwd_noalloc"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -157,6 +159,14 @@ def fm_attn_bwd(p: Problem, q, k, v, o, dout, lse, bounds, tileinfo, dq, dk, dv,
     _check(lib.fm_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                            _ptr(bounds), _ptr(tileinfo), _ptr(dq), _ptr(dk), _ptr(dv),
                            _ptr(workspace), _stream(stream)), "fm_attn_bwd")
+
+
+def fm_attn_bwd_noalloc(p: Problem, q, k, v, o, dout, lse, bounds, tileinfo, dq, dk, dv, stream=None):
+    """fm_attn_bwd with the library's static scratch array in place of a
+    workspace (for callers that cannot allocate)."""
+    _check(lib.fm_attn_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                   _ptr(lse), _ptr(bounds), _ptr(tileinfo), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   _stream(stream)), "fm_attn_bwd_noalloc")
 
 
 @dataclass

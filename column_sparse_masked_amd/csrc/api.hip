@@ -100,6 +100,31 @@ fm_status cu_count(int* out) {
 
 bool tensor_ok(const void* p) { return p != nullptr; }
 
+// Device memory of fm_attn_bwd_noalloc, for callers that cannot allocate:
+// Delta of up to kScratchRows query rows (16 MiB), one copy per GPU, held
+// until the process ends.  Host code never uses the array's name as an
+// address: each device's copy is found with hipGetSymbolAddress once, with
+// that device current, and that address is what the kernels are given.
+constexpr long kScratchRows = 4L << 20;
+static __device__ __align__(256) float scratch[kScratchRows];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[64] = {nullptr};
+
+fm_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FM_ERR_HIP;
+  if (dev < 0 || dev >= 64) return FM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FM_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FM_OK;
+}
+
 thread_local fm::KernelEvents g_events;
 
 }  // namespace
@@ -115,6 +140,8 @@ const char* fm_status_str(fm_status s) {
       return "FM_ERR_UNSUPPORTED: head_dim must be 64 or 128, mask_heads 1 or heads, scale > 0";
     case FM_ERR_ALIGN: return "FM_ERR_ALIGN: a tensor pointer is not suitably aligned";
     case FM_ERR_HIP: return "FM_ERR_HIP: the HIP runtime rejected a call or launch";
+    case FM_ERR_SCRATCH:
+      return "FM_ERR_SCRATCH: batch * heads * seqlen_q exceeds the 4194304 rows of the static scratch array";
   }
   return "unknown fm_status";
 }
@@ -293,17 +320,23 @@ fm_status fm_attn_fwd_fp8(const fm_problem* p, const void* q, const void* k, con
   return fm::launch_attn_fwd_fp8(a, grid, (hipStream_t)stream, g_events) == hipSuccess ? FM_OK : FM_ERR_HIP;
 }
 
-fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
-                      const void* o, const void* dout, const float* lse,
-                      const int32_t* bounds, void* tileinfo,
-                      void* dq, void* dk, void* dv, void* workspace, void* stream) {
+// The backward of fm_attn_bwd and fm_attn_bwd_noalloc.  Delta (fp32, one
+// value per query row) goes to the caller's `workspace`, or with
+// use_scratch to the library's static scratch array (looked up after every
+// argument check has passed).
+static fm_status attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
+                          const void* o, const void* dout, const float* lse,
+                          const int32_t* bounds, void* tileinfo,
+                          void* dq, void* dk, void* dv, void* workspace, bool use_scratch,
+                          void* stream) {
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
+  if (use_scratch && (long)p->batch * p->heads * p->seqlen_q > kScratchRows) return FM_ERR_SCRATCH;
   const bool has_rows = p->batch > 0 && p->seqlen_q > 0;
   const bool has_cols = p->batch > 0 && p->seqlen_k > 0;
   if (!tileinfo) return FM_ERR_NULL;
   if (has_rows && (!tensor_ok(q) || !tensor_ok(o) || !tensor_ok(dout) || !lse || !tensor_ok(dq) ||
-                   !workspace))
+                   (!use_scratch && !workspace)))
     return FM_ERR_NULL;
   if (has_cols && (!tensor_ok(k) || !tensor_ok(v) || !bounds || !tensor_ok(dk) || !tensor_ok(dv)))
     return FM_ERR_NULL;
@@ -323,6 +356,7 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   }
   int cus = 0;
   if ((st = cu_count(&cus)) != FM_OK) return st;
+  if (use_scratch && (st = scratch_address(&workspace)) != FM_OK) return st;
   fm::BwdArgs a;
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
@@ -353,6 +387,20 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   const int dq_grid = (int)(dq_items < cus ? dq_items : cus);
   return fm::launch_attn_bwd(a, p->head_dim, grid, dq_grid, s, g_events) == hipSuccess ? FM_OK
                                                                                         : FM_ERR_HIP;
+}
+
+fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
+                      const void* o, const void* dout, const float* lse,
+                      const int32_t* bounds, void* tileinfo,
+                      void* dq, void* dk, void* dv, void* workspace, void* stream) {
+  return attn_bwd(p, q, k, v, o, dout, lse, bounds, tileinfo, dq, dk, dv, workspace, false, stream);
+}
+
+fm_status fm_attn_bwd_noalloc(const fm_problem* p, const void* q, const void* k, const void* v,
+                              const void* o, const void* dout, const float* lse,
+                              const int32_t* bounds, void* tileinfo,
+                              void* dq, void* dk, void* dv, void* stream) {
+  return attn_bwd(p, q, k, v, o, dout, lse, bounds, tileinfo, dq, dk, dv, nullptr, true, stream);
 }
 
 }  // extern "C"

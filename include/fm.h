@@ -54,7 +54,8 @@ typedef enum {
   FM_ERR_SHAPE = 2,       /* a size is negative or beyond the supported range   */
   FM_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, or mask_heads not 1 or heads  */
   FM_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned            */
-  FM_ERR_HIP = 5          /* the HIP runtime rejected a call or launch          */
+  FM_ERR_HIP = 5,         /* the HIP runtime rejected a call or launch          */
+  FM_ERR_SCRATCH = 6      /* the problem exceeds the library's static scratch   */
 } fm_status;
 
 typedef struct {
@@ -212,6 +213,27 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
                       const void* o, const void* dout, const float* lse,
                       const int32_t* bounds, void* tileinfo,
                       void* dq, void* dk, void* dv, void* workspace, void* stream);
+
+/*
+ * fm_attn_bwd_noalloc - fm_attn_bwd without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The Delta row terms that
+ * fm_attn_bwd keeps in `workspace` live instead in a static device array of
+ * the library, 16 MiB on each GPU the library runs on (held until the process
+ * ends), which limits the problem to batch * heads * seqlen_q <= 4194304 rows:
+ * larger problems return FM_ERR_SCRATCH and enqueue nothing.  The call
+ * allocates nothing; the array's address is looked up once per device, on the
+ * first call made with that device current.  Arguments, results (the same
+ * kernels run: bit-identical to fm_attn_bwd) and other errors are those of
+ * fm_attn_bwd.  Every call on one GPU uses that GPU's array: calls that
+ * overlap on one GPU (different streams, different host threads) race and
+ * give wrong gradients, so such calls must be ordered.  The array's contents
+ * between calls have no meaning (each call writes every value it reads).
+ */
+fm_status fm_attn_bwd_noalloc(const fm_problem* p, const void* q, const void* k, const void* v,
+                              const void* o, const void* dout, const float* lse,
+                              const int32_t* bounds, void* tileinfo,
+                              void* dq, void* dk, void* dv, void* stream);
 
 #ifdef __cplusplus
 }

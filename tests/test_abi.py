@@ -116,7 +116,7 @@ def test_misaligned_tensors_rejected_before_launch():
 
 
 def test_status_strings():
-    for c in range(6):
+    for c in range(7):
         s = L.status_str(c)
         assert s.startswith("FM_")
     assert L.status_str(99) == "unknown fm_status"
@@ -258,3 +258,28 @@ def test_binding_rejects_tensors_on_another_device():
     with pytest.raises(ValueError, match="expected cuda"):
         att.tile_bounds(bounds)
 
+
+def test_noalloc_backward_validation():
+    """fm_attn_bwd_noalloc: problems beyond its static scratch array (more
+    than 4194304 query rows over batch and heads) are rejected with
+    FM_ERR_SCRATCH, bad problems, null and misaligned tensors as in
+    fm_attn_bwd, all before any HIP call."""
+    fake = ctypes.c_void_p(1 << 20)
+    big = _p(batch=2, heads=16, seqlen_q=131073, seqlen_k=128)
+    assert L.lib.fm_attn_bwd_noalloc(ctypes.byref(big), *([fake] * 11), None) == L.FM_ERR_SCRATCH
+    assert "static scratch" in L.status_str(L.FM_ERR_SCRATCH)
+    for kw, code in ((dict(batch=-1), L.FM_ERR_SHAPE), (dict(head_dim=96), L.FM_ERR_UNSUPPORTED)):
+        q = _p(**kw)
+        assert L.lib.fm_attn_bwd_noalloc(ctypes.byref(q), *([fake] * 11), None) == code
+    p = _p()
+    for i in range(11):
+        a = [fake] * 11
+        a[i] = None
+        assert L.lib.fm_attn_bwd_noalloc(ctypes.byref(p), *a, None) == L.FM_ERR_NULL, i
+    bad = ctypes.c_void_p((1 << 20) + 8)
+    for i in range(11):
+        if i == 5:   # lse only needs 4-byte alignment
+            continue
+        a = [fake] * 11
+        a[i] = bad
+        assert L.lib.fm_attn_bwd_noalloc(ctypes.byref(p), *a, None) == L.FM_ERR_ALIGN, i
