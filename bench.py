@@ -22,12 +22,15 @@ part of the step or its throughput).
 
 Printed: one JSON line with the whole-step throughput, the roofline of the
 dominant kernel (timed live with HIP events recorded by the library right
-around that kernel, on the stream it runs on) and the fp64 CPU oracle timed on
-a bounded sample of the same workload on the host cores (a reported baseline,
-not a target).  The default workload is the causal sliding window (w = 1024)
-at B=2, H=16, S=8192, D=128, seed 2; --config picks another of the five
-evaluation workloads (1 causal documents S=1K D=64, 3 share-question S=32K,
-4 documents with prefix-LM S=128K, 5 one context-parallel rank's share).
+around that kernel, on the stream it runs on; medians of the K eager steps)
+and the fp64 CPU oracle timed on a bounded sample of the same workload on the
+host cores (a reported baseline, not a target).  The headline workload is the
+largest one, documents with a 10% bidirectional prefix at B=1, H=8, S=131072,
+D=128, seed 4; --config picks another of the five evaluation workloads
+(1 causal documents S=1K D=64, 2 sliding window S=8K, 3 share-question S=32K,
+5 one context-parallel rank's share).  Unless --only is given, the other
+workloads of 8K-128K are timed the same way after it and reported under
+"other_workloads" (same fields, no CPU baseline or fp8 line).
 """
 from __future__ import annotations
 
@@ -54,7 +57,11 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5],
+                    help="the headline workload (default 4, the largest: documents with prefix-LM, S=128K)")
+    ap.add_argument("--only", action="store_true",
+                    help="time only the headline workload (default: also the other workloads of 8K-128K, "
+                         "reported under other_workloads)")
     ap.add_argument("--seed", type=int, default=None, help="default: the config's index")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle sample (at least one head is always run)")
@@ -108,9 +115,25 @@ def read_traffic(kernel: str, workload_tag: str, digest: str):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, tensors, budget_s):
-    """The fp64 oracle (forward + backward) on whole heads, in (b, h) order,
-    until the time budget is spent; mask-effective TFLOP/s of what ran."""
+    """The fp64 oracle (forward + backward) on a bounded sample of the same
+    workload: strips of 256 consecutive query rows of head (0, 0), at seeded
+    random places, until the time budget is spent (at least one strip).  Each
+    strip is the oracle's own unit of work (its rows against every key they
+    see).  Mask-effective flops of the sampled rows (14 D times their unmasked
+    (i, j) pairs) over the time taken; heads and strips are independent, so
+    this is the rate at which the oracle would run the whole workload."""
     import numpy as np
     import oracle
     try:
@@ -119,32 +142,34 @@ def cpu_baseline(w, tensors, budget_s):
     except Exception:  # threadpoolctl missing: numpy's BLAS default is one thread per core
         cores = os.cpu_count() or 1
     q, k, v, do = tensors
-    nnz = w.nnz_per_head()
     up = oracle.upcast_bf16
-    done, flops = [], 0.0
-    t0 = time.perf_counter()
-    for b in range(w.B):
-        for h in range(w.H):
-            hm = 0 if w.Hm == 1 else h
-            bh = w.bounds[b, hm]
-            qh, kh, vh, doh = up(q[b, h]), up(k[b, h]), up(v[b, h]), up(do[b, h])
-            oh, lse = oracle.head_forward(qh, kh, vh, bh, w.scale)
-            oracle.head_backward(qh, kh, vh, doh, bh, w.scale, lse=lse)
-            done.append((b, h))
-            flops += 14.0 * w.D * float(nnz[b, hm])
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        else:
-            continue
-        break
-    dt = time.perf_counter() - t0
+    b, h = 0, 0
+    bh = w.bounds[b, oracle.mask_head(w.bounds, h)]
+    qh, kh, vh, doh = up(q[b, h]), up(k[b, h]), up(v[b, h]), up(do[b, h])
+    strip = 256
+    n_strips = -(-w.Sq // strip)
+    order = np.random.default_rng(1000 + w.seed).permutation(n_strips)
+    flops, rows_done, strips, dt = 0.0, 0, 0, 0.0
+    for s_ in order:
+        rows = np.arange(s_ * strip, min(w.Sq, (s_ + 1) * strip))
+        t0 = time.perf_counter()
+        oh, lse = oracle.head_forward(qh, kh, vh, bh, w.scale, rows)
+        oracle.head_backward(qh, kh, vh, doh, bh, w.scale, rows, lse)
+        dt += time.perf_counter() - t0
+        flops += 14.0 * w.D * float((~oracle.dense_mask(bh, rows)).sum())
+        rows_done += rows.size
+        strips += 1
+        if dt >= budget_s:
+            break
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(cores),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
-        "sample": f"{len(done)} of {w.B * w.H} (batch, head) pairs of the same workload, whole "
-                  f"forward+backward in float64 numpy, {dt:.1f} s",
+        "sample": f"{strips} of {n_strips} strips of 256 query rows ({rows_done} rows) of head (0, 0) of the "
+                  f"same workload, forward + backward in float64 numpy, {dt:.1f} s; the rate extrapolates to "
+                  f"all {w.B * w.H} (batch, head) pairs, which are independent",
     }
 
 
@@ -175,7 +200,7 @@ def fp8_forward(w, tensors, att, tb, args, k_fwd_bf16, f_fwd, tag):
         att.forward_fp8(*t8, ds, tb, o=o8, lse=l8)
     _lib.set_kernel_events(None, None)
     torch.cuda.synchronize()
-    kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kms = median([a.elapsed_time(b) for a, b in evs])
     achieved = f_fwd / (kms * 1e-3) / 1e12
     return {"kernel": "attn_fwd_fp8_kernel", "dtype": "e4m3", "avg_kernel_ms": round(kms, 4),
             "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
@@ -184,27 +209,32 @@ def fp8_forward(w, tensors, att, tb, args, k_fwd_bf16, f_fwd, tag):
             "speedup_vs_bf16_forward_kernel": round(k_fwd_bf16 / kms, 3)}
 
 
-def main(argv=None):
-    args = parse_args(argv)
-    if args.copy_calibration:
-        return copy_calibration(args.copy_calibration)
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(no sharding, no collectives).", file=sys.stderr)
-        return 2
+def tile_pass_bytes(w, nQ, nK):
+    """Algorithmic HBM bytes of the tile pass: the bounds read once (16 B per
+    key column and mask head), the key-block summaries written and read back
+    once, the tile classes, the per-block counts (written, then read by the
+    queue kernel), both tile lists and both queues written."""
+    bhm = w.B * w.Hm
+    return (16 * w.Sk * bhm + 2 * 32 * nK * bhm + nQ * nK * bhm + 2 * 4 * (nQ + nK) * bhm
+            + 2 * 2 * nQ * nK * bhm + 4 * w.B * w.H * (nQ + nK))
 
+
+def median(xs):
+    import numpy as np
+    return float(np.median(np.asarray(xs, dtype=np.float64)))
+
+
+def run_workload(cfg, seed, args, dev, with_fp8):
+    """Time the whole step (tile pass, forward, backward) on one of the
+    evaluation workloads; returns the record and what the CPU baseline needs."""
     import numpy as np
     import torch
 
     from column_sparse_masked_amd import _lib, masks
     from column_sparse_masked_amd.api import MaskedAttention, to_device_bf16, to_device_bounds
 
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        return 1
-    dev = torch.device("cuda:0")
-    w = masks.config(args.config, args.seed)
-    print(f"# workload {masks.CONFIG_NAMES[args.config]} seed {w.seed}", file=sys.stderr, flush=True)
+    w = masks.config(cfg, seed)
+    print(f"# workload {masks.CONFIG_NAMES[cfg]} seed {w.seed}: drawing inputs", file=sys.stderr, flush=True)
     tensors = w.draw()
     tq, tk, tv, tdo = (to_device_bf16(x, dev) for x in tensors)
     tb = to_device_bounds(w.bounds, dev)
@@ -254,7 +284,7 @@ def main(argv=None):
     ref = [x.clone() for x in (o, lse, dq, dk, dv)]
 
     # The timed steps: one step captured as a HIP graph and replayed, which
-    # removes the launch gaps between the step's seven kernels.  A replay must
+    # removes the launch gaps between the step's kernels.  A replay must
     # reproduce the eager outputs bit for bit, else the eager time is used.
     launch = "hip_graph"
     try:
@@ -276,76 +306,118 @@ def main(argv=None):
             g.replay()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        del g
     except Exception as exc:   # graph capture unavailable: time the eager steps instead
         print(f"# graph replay not used ({exc}); timing the eager steps", file=sys.stderr, flush=True)
         launch, wall = "eager", wall_eager
     print(f"# timed {args.steps} steps ({launch}) in {wall:.3f} s; eager {wall_eager:.3f} s",
           file=sys.stderr, flush=True)
 
-    def avg_ms(a, b):
-        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+    def med_ms(a, b):
+        return median([e[a].elapsed_time(e[b]) for e in evs])
 
-    t_tile, t_fwd, t_bwd = avg_ms("s0", "s1"), avg_ms("s1", "s2"), avg_ms("s2", "s3")
-    k_fwd, k_bwd, k_dq = avg_ms("fk0", "fk1"), avg_ms("bk0", "bk1"), avg_ms("bq0", "bq1")
+    t_tile, t_fwd, t_bwd = med_ms("s0", "s1"), med_ms("s1", "s2"), med_ms("s2", "s3")
+    k_fwd, k_bwd, k_dq = med_ms("fk0", "fk1"), med_ms("bk0", "bk1"), med_ms("bq0", "bq1")
     ms_per_step = wall / args.steps * 1e3
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
 
-    # Dominant kernel: the longest of the three attention kernels, credited
-    # with the products it computes itself: forward S, PV (4 D nnz); dK/dV
-    # kernel S, dP, dV, dK (8 D nnz); dQ kernel S, dP, dQ (6 D nnz).
-    f_dkdv, f_dq = 8.0 * w.D * nnz, 6.0 * w.D * nnz
-    kernels = [("attn_fwd_kernel", f_fwd, k_fwd, ["fwd.hip", "common.h"]),
-               ("attn_bwd_kernel", f_dkdv, k_bwd, ["bwd.hip", "common.h"]),
-               ("attn_bwd_dq_kernel", f_dq, k_dq, ["bwd_dq.hip", "common.h"])]
-    kname, kflops, kms, srcs = max(kernels, key=lambda x: x[2])
-    achieved = kflops / (kms * 1e-3) / 1e12
-    tag = f"cfg{args.config}_seed{w.seed}"
-    roofline = {
-        "bound": "mfma",
-        "kernel": kname,
-        "achieved": round(achieved, 2),
-        "peak": PEAK_BF16_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": read_traffic(kname, tag, kernel_source_digest(srcs)),
-        "avg_kernel_ms": round(kms, 4),
-        "algorithmic_flops_per_launch": kflops,
+    # Per-kernel rooflines: each attention kernel is credited with the
+    # mask-effective products that belong to it in the 4 + 10 D nnz
+    # accounting: the forward (with its merge of split items) S and PV,
+    # 4 D nnz; the dK/dV kernel S, dP, dV, dK, 8 D nnz; the dQ kernel its dQ
+    # product, 2 D nnz (the S and dP it recomputes are not credited; its
+    # hardware flops are 6 D nnz).  The dominant kernel is the longest.
+    tag = f"cfg{cfg}_seed{w.seed}"
+    kernels = {
+        "attn_fwd_kernel": (4.0 * w.D * nnz, k_fwd, ["fwd.hip", "common.h"]),
+        "attn_bwd_kernel": (8.0 * w.D * nnz, k_bwd, ["bwd.hip", "common.h"]),
+        "attn_bwd_dq_kernel": (2.0 * w.D * nnz, k_dq, ["bwd_dq.hip", "common.h"]),
     }
+
+    def roofline(name):
+        flops, kms, srcs = kernels[name]
+        achieved = flops / (kms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": name, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": read_traffic(name, tag, kernel_source_digest(srcs)),
+                "avg_kernel_ms": round(kms, 4), "timing": f"median of {args.steps} eager launches, HIP events",
+                "algorithmic_flops_per_launch": flops}
+
+    dom = max(kernels, key=lambda n: kernels[n][1])
+    layout = att.buf.layout
+    tb_bytes = tile_pass_bytes(w, layout.n_qblocks, layout.n_kblocks)
+    rec = {
+        "workload": masks.CONFIG_NAMES[cfg],
+        "seed": w.seed, "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "D": w.D,
+        "nnz_per_head_mean": nnz / (w.B * w.H),
+        "mask_flops_fwd_bwd": f_fwd + f_bwd,
+        "step_launch": launch,
+        "value": round(value, 2),
+        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_eager": round(wall_eager / args.steps * 1e3, 4),
+        "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "stages_ms": {"tile_bounds": round(t_tile, 4), "fwd": round(t_fwd, 4), "bwd": round(t_bwd, 4)},
+        "kernel_ms": {"fwd": round(k_fwd, 4), "bwd_dkdv": round(k_bwd, 4), "bwd_dq": round(k_dq, 4)},
+        "tflops_fwd_kernel": round(f_fwd / (k_fwd * 1e-3) / 1e12, 2),
+        "tflops_bwd_kernels_mask_effective": round(f_bwd / ((k_bwd + k_dq) * 1e-3) / 1e12, 2),
+        "tflops_without_tile_pass": round((f_fwd + f_bwd) / ((t_fwd + t_bwd) * 1e-3) / 1e12, 2),
+        "tile_pass": {"ms": round(t_tile, 4), "algorithmic_bytes": tb_bytes,
+                      "GB_per_s": round(tb_bytes / (t_tile * 1e-3) / 1e9, 2), "launches": 3},
+        "roofline": roofline(dom),
+        "kernel_rooflines": {n: {k: v for k, v in roofline(n).items() if k in ("achieved", "frac", "avg_kernel_ms")}
+                             for n in kernels},
+    }
+    if with_fp8 and w.D == 128:
+        rec["fp8_forward"] = fp8_forward(w, tensors, att, tb, args, k_fwd, f_fwd, tag)
+    del tq, tk, tv, tdo, tb, att, o, lse, dq, dk, dv, ref
+    torch.cuda.empty_cache()
+    return rec, w, tensors
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(no sharding, no collectives).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    head, w, tensors = run_workload(args.config, args.seed, args, dev, not args.no_fp8)
+    others = {}
+    if not args.only:
+        for c in (2, 3, 4, 5):
+            if c != args.config:
+                others[f"config{c}"], _, _ = run_workload(c, None, args, dev, False)
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {
-            "workload": masks.CONFIG_NAMES[args.config],
-            "seed": w.seed, "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "D": w.D,
-            "nnz_per_head_mean": nnz / (w.B * w.H),
-            "mask_flops_fwd_bwd": f_fwd + f_bwd,
-            "step_launch": launch,
-        },
-        "ms_per_step_eager": round(wall_eager / args.steps * 1e3, 4),
-        "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "stages_ms": {"tile_bounds": round(t_tile, 4), "fwd": round(t_fwd, 4), "bwd": round(t_bwd, 4)},
-        "tflops_fwd_kernel": round(f_fwd / (k_fwd * 1e-3) / 1e12, 2),
-        "kernel_ms": {"fwd": round(k_fwd, 4), "bwd_dkdv": round(k_bwd, 4), "bwd_dq": round(k_dq, 4)},
-        "tflops_bwd_kernels_mask_effective": round(f_bwd / ((k_bwd + k_dq) * 1e-3) / 1e12, 2),
-        "tflops_without_tile_pass": round((f_fwd + f_bwd) / ((t_fwd + t_bwd) * 1e-3) / 1e12, 2),
-        "roofline": roofline,
-        "cpu_baseline": None,
+        "config": {k: head[k] for k in ("workload", "seed", "B", "H", "Sq", "Sk", "D", "nnz_per_head_mean",
+                                         "mask_flops_fwd_bwd", "step_launch")},
     }
-    if w.D == 128 and not args.no_fp8:
-        out["fp8_forward"] = fp8_forward(w, tensors, att, tb, args, k_fwd, f_fwd, tag)
+    out.update({k: v for k, v in head.items() if k not in out["config"] and k not in ("value", "ms_per_step")})
+    out["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         print(f"# oracle sample on the host ({args.cpu_seconds:.0f} s budget)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, tensors, args.cpu_seconds)
+    if others:
+        out["other_workloads"] = others
     print(json.dumps(out), flush=True)
     return 0
 
