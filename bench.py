@@ -49,6 +49,7 @@ METRIC = "mask-effective attention fwd+bwd TFLOP/s on 1 MI355X; % of bf16 MFMA p
 # Dense bf16 MFMA peak of MI355X: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP8_TFLOPS = 5033.2
+PEAK_HBM_GBS = 8000.0   # HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -66,6 +67,8 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle sample (at least one head is always run)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward's line (head_dim 128 only)")
+    ap.add_argument("--no-tile-cache", action="store_true",
+                    help="run the backward without the tile cache (dQ recomputes S and dP)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="leave out the oracle timing (profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -267,10 +270,17 @@ def run_workload(cfg, seed, args, dev, with_fp8):
             _lib.set_kernel_events(None, None)
             ev["s3"].record()
 
+    # The backward's workspace holds the tile cache for every non-skipped
+    # tile (dQ from the cached scale * dS); it is sized from one tile pass,
+    # before any timed work.
+    att.tile_bounds(tb)
+    cache_bytes = att.reserve_tile_cache() if not args.no_tile_cache else 0
+    n_tiles = att.tile_count()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"# warmup {args.warmup} steps done", file=sys.stderr, flush=True)
+    print(f"# warmup {args.warmup} steps done ({n_tiles} tiles, workspace {cache_bytes / 2**30:.2f} GiB)",
+          file=sys.stderr, flush=True)
 
     # Eager steps with the library's event hook: per-stage and per-kernel times.
     evs = [{n: new_event() for n in ("s0", "s1", "s2", "s3", "fk0", "fk1", "bk0", "bk1", "bq0", "bq1")}
@@ -324,26 +334,38 @@ def run_workload(cfg, seed, args, dev, with_fp8):
     # Per-kernel rooflines: each attention kernel is credited with the
     # mask-effective products that belong to it in the 4 + 10 D nnz
     # accounting: the forward (with its merge of split items) S and PV,
-    # 4 D nnz; the dK/dV kernel S, dP, dV, dK, 8 D nnz; the dQ kernel its dQ
-    # product, 2 D nnz (the S and dP it recomputes are not credited; its
-    # hardware flops are 6 D nnz).  The dominant kernel is the longest.
+    # 4 D nnz; the dK/dV kernel S, dP, dV, dK, 8 D nnz.  dQ: from the tile
+    # cache it is bound by reading the cached tiles, so its roofline is HBM
+    # bytes (every cached tile of scale * dS, K once, dQ written); without the
+    # cache it recomputes S and dP and is credited with its dQ product only,
+    # 2 D nnz (its hardware flops are 6 D nnz).  The dominant kernel is the
+    # longest.
     tag = f"cfg{cfg}_seed{w.seed}"
+    dq_cached = cache_bytes > 0
+    dq_bytes = float(n_tiles) * 128 * 128 * 2 + 2.0 * w.B * w.H * (w.Sk + w.Sq) * w.D
     kernels = {
-        "attn_fwd_kernel": (4.0 * w.D * nnz, k_fwd, ["fwd.hip", "common.h"]),
-        "attn_bwd_kernel": (8.0 * w.D * nnz, k_bwd, ["bwd.hip", "common.h"]),
-        "attn_bwd_dq_kernel": (2.0 * w.D * nnz, k_dq, ["bwd_dq.hip", "common.h"]),
+        "attn_fwd_kernel": ("mfma", 4.0 * w.D * nnz, k_fwd, ["fwd.hip", "common.h"]),
+        "attn_bwd_kernel": ("mfma", 8.0 * w.D * nnz, k_bwd, ["bwd.hip", "common.h"]),
+        ("attn_bwd_dq_cached_kernel" if dq_cached else "attn_bwd_dq_kernel"):
+            ("hbm", dq_bytes, k_dq, ["bwd_dq_cached.hip", "common.h"]) if dq_cached
+            else ("mfma", 2.0 * w.D * nnz, k_dq, ["bwd_dq.hip", "common.h"]),
     }
 
     def roofline(name):
-        flops, kms, srcs = kernels[name]
-        achieved = flops / (kms * 1e-3) / 1e12
-        return {"bound": "mfma", "kernel": name, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        bound, work, kms, srcs = kernels[name]
+        if bound == "mfma":
+            achieved, peak, unit, key = work / (kms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", \
+                "algorithmic_flops_per_launch"
+        else:
+            achieved, peak, unit, key = work / (kms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", \
+                "algorithmic_bytes_per_launch"
+        return {"bound": bound, "kernel": name, "achieved": round(achieved, 2), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4),
                 "traffic": read_traffic(name, tag, kernel_source_digest(srcs)),
                 "avg_kernel_ms": round(kms, 4), "timing": f"median of {args.steps} eager launches, HIP events",
-                "algorithmic_flops_per_launch": flops}
+                key: work}
 
-    dom = max(kernels, key=lambda n: kernels[n][1])
+    dom = max(kernels, key=lambda n: kernels[n][2])
     layout = att.buf.layout
     tb_bytes = tile_pass_bytes(w, layout.n_qblocks, layout.n_kblocks)
     rec = {
@@ -362,9 +384,11 @@ def run_workload(cfg, seed, args, dev, with_fp8):
         "tflops_bwd_kernels_mask_effective": round(f_bwd / ((k_bwd + k_dq) * 1e-3) / 1e12, 2),
         "tflops_without_tile_pass": round((f_fwd + f_bwd) / ((t_fwd + t_bwd) * 1e-3) / 1e12, 2),
         "tile_pass": {"ms": round(t_tile, 4), "algorithmic_bytes": tb_bytes,
-                      "GB_per_s": round(tb_bytes / (t_tile * 1e-3) / 1e9, 2), "launches": 3},
+                      "GB_per_s": round(tb_bytes / (t_tile * 1e-3) / 1e9, 2), "launches": 2},
+        "tile_cache": {"tiles": n_tiles, "workspace_bytes": cache_bytes, "dq_from_cache": dq_cached},
         "roofline": roofline(dom),
-        "kernel_rooflines": {n: {k: v for k, v in roofline(n).items() if k in ("achieved", "frac", "avg_kernel_ms")}
+        "kernel_rooflines": {n: {k: v for k, v in roofline(n).items()
+                                 if k in ("bound", "achieved", "unit", "frac", "avg_kernel_ms")}
                              for n in kernels},
     }
     if with_fp8 and w.D == 128:

@@ -58,6 +58,7 @@ class TileinfoLayout(ctypes.Structure):
                 ("cnt_k", ctypes.c_size_t), ("list_q", ctypes.c_size_t),
                 ("list_k", ctypes.c_size_t), ("fwd_queue", ctypes.c_size_t),
                 ("bwd_queue", ctypes.c_size_t), ("fwd_partials", ctypes.c_size_t),
+                ("cpos", ctypes.c_size_t), ("colbase", ctypes.c_size_t),
                 ("total", ctypes.c_size_t)]
 
 
@@ -72,11 +73,15 @@ lib.fm_device_cu_count.argtypes = [ctypes.POINTER(ctypes.c_int32)]
 lib.fm_tile_bounds.argtypes = [_P, _vp, _vp, _vp]
 lib.fm_attn_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.fm_attn_fwd_fp8.argtypes = [_P, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_float), _vp, _vp, _vp, _vp, _vp]
-lib.fm_attn_bwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+lib.fm_attn_bwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+lib.fm_bwd_cache_bytes.argtypes = [_P, ctypes.c_uint64, ctypes.POINTER(ctypes.c_size_t)]
+_i32p = ctypes.POINTER(ctypes.c_int32)
+lib.fm_localize_bounds.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32,
+                                   _i32p, _i32p, _vp, _vp]
 lib.fm_attn_bwd_noalloc.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
-for _f in ("fm_tile_shape", "fm_tileinfo_layout_query", "fm_bwd_workspace_bytes",
+for _f in ("fm_tile_shape", "fm_tileinfo_layout_query", "fm_bwd_workspace_bytes", "fm_bwd_cache_bytes",
            "fm_device_cu_count", "fm_tile_bounds", "fm_attn_fwd", "fm_attn_fwd_fp8", "fm_attn_bwd",
-           "fm_attn_bwd_noalloc"):
+           "fm_attn_bwd_noalloc", "fm_localize_bounds"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -114,6 +119,13 @@ def tileinfo_layout(p: Problem) -> TileinfoLayout:
 def bwd_workspace_bytes(p: Problem) -> int:
     n = ctypes.c_size_t()
     _check(lib.fm_bwd_workspace_bytes(ctypes.byref(p), ctypes.byref(n)), "fm_bwd_workspace_bytes")
+    return n.value
+
+
+def bwd_cache_bytes(p: Problem, n_tiles: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.fm_bwd_cache_bytes(ctypes.byref(p), ctypes.c_uint64(n_tiles), ctypes.byref(n)),
+           "fm_bwd_cache_bytes")
     return n.value
 
 
@@ -156,9 +168,12 @@ def fm_attn_fwd_fp8(p: Problem, q8, k8, v8, descale, bounds, tileinfo, o, lse, s
 
 def fm_attn_bwd(p: Problem, q, k, v, o, dout, lse, bounds, tileinfo, dq, dk, dv, workspace,
                 stream=None):
+    """workspace: a uint8 device tensor of at least bwd_workspace_bytes(p)
+    bytes; its whole size is passed (room beyond Delta is the tile cache)."""
     _check(lib.fm_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                            _ptr(bounds), _ptr(tileinfo), _ptr(dq), _ptr(dk), _ptr(dv),
-                           _ptr(workspace), _stream(stream)), "fm_attn_bwd")
+                           _ptr(workspace), ctypes.c_size_t(0 if workspace is None else workspace.numel()),
+                           _stream(stream)), "fm_attn_bwd")
 
 
 def fm_attn_bwd_noalloc(p: Problem, q, k, v, o, dout, lse, bounds, tileinfo, dq, dk, dv, stream=None):
@@ -167,6 +182,17 @@ def fm_attn_bwd_noalloc(p: Problem, q, k, v, o, dout, lse, bounds, tileinfo, dq,
     _check(lib.fm_attn_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                                    _ptr(lse), _ptr(bounds), _ptr(tileinfo), _ptr(dq), _ptr(dk), _ptr(dv),
                                    _stream(stream)), "fm_attn_bwd_noalloc")
+
+
+def fm_localize_bounds(global_bounds, chunk_start, chunk_len, local_bounds, stream=None):
+    """global_bounds, local_bounds: int32 [B][Hm][Sk][4] device tensors;
+    chunk_start, chunk_len: the rank's query chunks (host sequences)."""
+    B, Hm, Sk, _ = global_bounds.shape
+    n = len(chunk_start)
+    starts = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in chunk_start])
+    lens = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in chunk_len])
+    _check(lib.fm_localize_bounds(B, Hm, Sk, _ptr(global_bounds), n, starts, lens, _ptr(local_bounds),
+                                  _stream(stream)), "fm_localize_bounds")
 
 
 @dataclass

@@ -25,6 +25,20 @@ def to_device_bounds(bounds: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bounds, dtype=np.int32)).to(device)
 
 
+def localize_bounds(global_bounds: torch.Tensor, chunk_start, chunk_len, stream=None) -> torch.Tensor:
+    """One context-parallel rank's bounds, computed on the device from the
+    global ones (fm_localize_bounds): the rank's query chunks are
+    [chunk_start[c], chunk_start[c] + chunk_len[c]), in increasing order."""
+    if global_bounds.dtype != torch.int32 or global_bounds.dim() != 4 or global_bounds.shape[-1] != 4 \
+            or not global_bounds.is_contiguous():
+        raise ValueError("global_bounds: expected a contiguous int32 tensor [B][Hm][Sk][4]")
+    if len(chunk_start) != len(chunk_len):
+        raise ValueError("chunk_start and chunk_len differ in length")
+    out = torch.empty_like(global_bounds)
+    _lib.fm_localize_bounds(global_bounds, chunk_start, chunk_len, out, stream)
+    return out
+
+
 class MaskedAttention:
     """One problem shape: owns the tileinfo and backward workspace buffers.
 
@@ -117,6 +131,27 @@ class MaskedAttention:
                          self.buf.workspace, stream)
         return dq, dk, dv
 
+    def tile_count(self) -> int:
+        """Non-skipped tiles over every (batch, head) pair, as counted by the
+        last tile pass on this object's tileinfo (synchronises the device)."""
+        return int(self.buf.tileinfo[:64].cpu().numpy().view(np.uint32)[9])
+
+    def reserve_tile_cache(self, n_tiles=None):
+        """Grow the backward workspace to hold the tile cache for n_tiles
+        tiles (default: the last tile pass's count), so that the backward
+        computes dQ from cached scale * dS instead of recomputing S and dP.
+        Returns the workspace size in bytes."""
+        n = self.tile_count() if n_tiles is None else int(n_tiles)
+        need = _lib.bwd_cache_bytes(self.p, n)
+        if self.buf.workspace.numel() < need:
+            self.buf.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self.buf.workspace.numel()
+
+    def drop_tile_cache(self):
+        """Back to the smallest workspace (Delta only): dQ is recomputed."""
+        self.buf.workspace = torch.empty(max(_lib.bwd_workspace_bytes(self.p), 256), dtype=torch.uint8,
+                                         device=self.device)
+
     # ---- inspection of the tile pass (tests) ----
     def read_tileinfo(self) -> dict:
         p, L = self.p, self.buf.layout
@@ -138,5 +173,7 @@ class MaskedAttention:
             "list_k": view(L.list_k, np.uint16, (bhm, nK, nQ)).reshape(p.batch, p.mask_heads, nK, nQ),
             "fwd_queue": view(L.fwd_queue, np.uint32, (bh * nQ,)),
             "bwd_queue": view(L.bwd_queue, np.uint32, (bh * nK,)),
+            "cpos": view(L.cpos, np.uint16, (bhm, nK, nQ)).reshape(p.batch, p.mask_heads, nK, nQ),
+            "colbase": view(L.colbase, np.uint32, (bh * nK,)),
             "nQ": nQ, "nK": nK,
         }

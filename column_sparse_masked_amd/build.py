@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["tiles.hip", "fwd.hip", "fwd_fp8.hip", "bwd.hip", "bwd_dq.hip", "api.hip"]
+SOURCES = ["tiles.hip", "fwd.hip", "fwd_fp8.hip", "bwd.hip", "bwd_dq.hip", "bwd_dq_cached.hip", "localize.hip",
+           "api.hip"]
 ARCH = os.environ.get("FM_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are turned off for all device code.  The

@@ -36,7 +36,8 @@ fm_status check_problem(const fm_problem* p) {
 struct Layout {
   int nQ, nK;
   int split_cap;   // forward items that may be split in two
-  size_t counters, kbsum, cls, cnt_q, cnt_k, list_q, list_k, fwd_queue, bwd_queue, fwd_partials, total;
+  size_t counters, kbsum, cls, cnt_q, cnt_k, list_q, list_k, fwd_queue, bwd_queue, fwd_partials, cpos, colbase,
+      total;
 };
 
 // At most this many forward items are split (two partial-result slots each).
@@ -71,6 +72,8 @@ Layout make_layout(const fm_problem* p) {
   L.split_cap = (int)(items_q < kMaxSplitItems ? items_q : kMaxSplitItems);
   L.fwd_partials = off;
   off = align256(off + (size_t)2 * L.split_cap * fm::BQ * ((size_t)p->head_dim * 2 + sizeof(float)));
+  L.cpos = off;      off = align256(off + bhm * L.nK * L.nQ * sizeof(uint16_t));
+  L.colbase = off;   off = align256(off + bh * L.nK * sizeof(uint32_t));
   L.total = off;
   return L;
 }
@@ -174,6 +177,8 @@ fm_status fm_tileinfo_layout_query(const fm_problem* p, fm_tileinfo_layout* out)
   out->fwd_queue = L.fwd_queue;
   out->bwd_queue = L.bwd_queue;
   out->fwd_partials = L.fwd_partials;
+  out->cpos = L.cpos;
+  out->colbase = L.colbase;
   out->total = L.total;
   return FM_OK;
 }
@@ -185,6 +190,45 @@ fm_status fm_bwd_workspace_bytes(const fm_problem* p, size_t* bytes) {
   const size_t rows = (size_t)p->batch * p->heads * p->seqlen_q;
   *bytes = align256(rows * sizeof(float));
   return FM_OK;
+}
+
+fm_status fm_bwd_cache_bytes(const fm_problem* p, uint64_t n_tiles, size_t* bytes) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  if (!bytes) return FM_ERR_NULL;
+  if (n_tiles > 0xFFFFFFFEull) return FM_ERR_SHAPE;
+  const size_t rows = (size_t)p->batch * p->heads * p->seqlen_q;
+  *bytes = align256(rows * sizeof(float)) + (size_t)n_tiles * fm::kTileBytes;
+  return FM_OK;
+}
+
+fm_status fm_localize_bounds(int32_t batch, int32_t mask_heads, int32_t seqlen_k, const int32_t* global_bounds,
+                             int32_t n_chunks, const int32_t* chunk_start, const int32_t* chunk_len,
+                             int32_t* local_bounds, void* stream) {
+  if (batch < 0 || mask_heads < 1 || seqlen_k < 0) return FM_ERR_SHAPE;
+  if (n_chunks < 1 || n_chunks > fm::kMaxLocalChunks) return FM_ERR_SHAPE;
+  if (!chunk_start || !chunk_len) return FM_ERR_NULL;
+  fm::LocalizeArgs a;
+  a.n_chunks = n_chunks;
+  long off = 0, prev_end = 0;
+  for (int c = 0; c < n_chunks; ++c) {
+    const long s = chunk_start[c], l = chunk_len[c];
+    if (s < 0 || l < 0 || s < prev_end) return FM_ERR_SHAPE;   // increasing, disjoint
+    prev_end = s + l;
+    if (prev_end > INT32_MAX) return FM_ERR_SHAPE;
+    a.start[c] = (int)s;
+    a.len[c] = (int)l;
+    a.off[c] = (int)off;
+    off += l;
+  }
+  if (off > kMaxSeq) return FM_ERR_SHAPE;                         // local rows must fit one problem
+  const long n = (long)batch * mask_heads * seqlen_k;
+  if (n > 0 && (!global_bounds || !local_bounds)) return FM_ERR_NULL;
+  if (!aligned(global_bounds, 16) || !aligned(local_bounds, 16)) return FM_ERR_ALIGN;
+  return fm::launch_localize(reinterpret_cast<const int4*>(global_bounds), reinterpret_cast<int4*>(local_bounds),
+                             n, a, (hipStream_t)stream) == hipSuccess
+             ? FM_OK
+             : FM_ERR_HIP;
 }
 
 fm_status fm_device_cu_count(int32_t* cus) {
@@ -222,8 +266,10 @@ fm_status fm_tile_bounds(const fm_problem* p, const int32_t* bounds, void* tilei
   a.cnt_k = at<int>(tileinfo, L.cnt_k);
   a.list_q = at<uint16_t>(tileinfo, L.list_q);
   a.list_k = at<uint16_t>(tileinfo, L.list_k);
+  a.cpos = at<uint16_t>(tileinfo, L.cpos);
   a.fwd_queue = at<uint32_t>(tileinfo, L.fwd_queue);
   a.bwd_queue = at<uint32_t>(tileinfo, L.bwd_queue);
+  a.colbase = at<uint32_t>(tileinfo, L.colbase);
   a.counters = at<uint32_t>(tileinfo, L.counters);
   a.B = p->batch; a.H = p->heads; a.Hm = p->mask_heads;
   a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
@@ -327,8 +373,8 @@ fm_status fm_attn_fwd_fp8(const fm_problem* p, const void* q, const void* k, con
 static fm_status attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
                           const void* o, const void* dout, const float* lse,
                           const int32_t* bounds, void* tileinfo,
-                          void* dq, void* dk, void* dv, void* workspace, bool use_scratch,
-                          void* stream) {
+                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                          bool use_scratch, void* stream) {
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
   if (use_scratch && (long)p->batch * p->heads * p->seqlen_q > kScratchRows) return FM_ERR_SCRATCH;
@@ -376,6 +422,15 @@ static fm_status attn_bwd(const fm_problem* p, const void* q, const void* k, con
   a.dk = static_cast<__bf16*>(dk);
   a.dv = static_cast<__bf16*>(dv);
   a.delta = static_cast<float*>(workspace);
+  // the tile cache: whatever the workspace holds beyond Delta, in whole tiles
+  const size_t delta_bytes = align256((size_t)p->batch * p->heads * p->seqlen_q * sizeof(float));
+  const size_t cache_tiles = !use_scratch && workspace_bytes > delta_bytes
+                                 ? (workspace_bytes - delta_bytes) / fm::kTileBytes
+                                 : 0;
+  a.ds_cap = (uint32_t)(cache_tiles < 0xFFFFFFFEu ? cache_tiles : 0xFFFFFFFEu);
+  a.ds = a.ds_cap > 0 ? reinterpret_cast<__bf16*>(static_cast<char*>(workspace) + delta_bytes) : nullptr;
+  a.colbase = at<uint32_t>(tileinfo, L.colbase);
+  a.cpos = at<uint16_t>(tileinfo, L.cpos);
   a.B = p->batch; a.H = p->heads; a.Hm = p->mask_heads;
   a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
   a.scale = p->softmax_scale;
@@ -392,15 +447,17 @@ static fm_status attn_bwd(const fm_problem* p, const void* q, const void* k, con
 fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
                       const void* o, const void* dout, const float* lse,
                       const int32_t* bounds, void* tileinfo,
-                      void* dq, void* dk, void* dv, void* workspace, void* stream) {
-  return attn_bwd(p, q, k, v, o, dout, lse, bounds, tileinfo, dq, dk, dv, workspace, false, stream);
+                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return attn_bwd(p, q, k, v, o, dout, lse, bounds, tileinfo, dq, dk, dv, workspace, workspace_bytes, false,
+                  stream);
 }
 
 fm_status fm_attn_bwd_noalloc(const fm_problem* p, const void* q, const void* k, const void* v,
                               const void* o, const void* dout, const float* lse,
                               const int32_t* bounds, void* tileinfo,
                               void* dq, void* dk, void* dv, void* stream) {
-  return attn_bwd(p, q, k, v, o, dout, lse, bounds, tileinfo, dq, dk, dv, nullptr, true, stream);
+  return attn_bwd(p, q, k, v, o, dout, lse, bounds, tileinfo, dq, dk, dv, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

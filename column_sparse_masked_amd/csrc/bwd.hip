@@ -256,6 +256,7 @@ struct BwdItem {
   long bh, bhm;
   const uint16_t* lst;    // the key block's list of non-skipped query blocks
   BufRsrc qbase, obase, kbase, vbase, lbase, dbase;
+  BufRsrc dsrc;           // the item's tiles in the tile cache (empty when it is off)
 
   // List word of chunk c (clamped to the last chunk: entries past the end
   // are loaded but not used).  Each item starts its walk at block kb % cnt
@@ -268,7 +269,7 @@ struct BwdItem {
 };
 
 template <int D>
-__device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, const uint32_t (&hdr)[4]) {
+__device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, const uint32_t (&hdr)[4], bool cache) {
   // values read from LDS are not known to be uniform: broadcast them, so that
   // the buffer resources built from them stay in scalar registers
   BwdItem x;
@@ -290,7 +291,37 @@ __device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, const uint32_t (&h
   x.vbase = make_rsrc(a.v + x.bh * Sk * (long)D, (uint32_t)Sk * D * 2u);
   x.lbase = make_rsrc(a.lse + x.bh * Sq, (uint32_t)Sq * 4u);
   x.dbase = make_rsrc(a.delta + x.bh * Sq, (uint32_t)Sq * 4u);
+  // the item's tiles take consecutive slots from colbase[it], in list order;
+  // with the cache off the range is empty and the stores are dropped
+  // (`it` is already clamped to a valid item; an item whose slots would run
+  // past the cache gets an empty range, so no store can leave the cache)
+  const uint32_t cb = cache ? *(const_u32*)(a.colbase + it) : 0u;
+  const bool fits = cache && (uint64_t)cb + (uint32_t)x.cnt <= a.ds_cap;
+  x.dsrc = make_rsrc(a.ds + (fits ? (size_t)cb * (BQ * BK) : 0), fits ? (uint32_t)x.cnt * kTileBytes : 0u);
   return x;
+}
+
+// This wave's scale * dS of one chunk into the item's tile of the cache.  A
+// tile is stored as the waves hold it: for chunk c2 (two per tile), wave
+// (g, m) and register pair rr, a block of 512 bytes in which lane l (key
+// 32 g + l % 32) has 8 bytes, rows 32 m + 8 rr + 4 (l / 32) + q (q = 0..3)
+// of the chunk.  Block (c2, m, g, rr) is at ((c2 * 2 + m) * 4 + g) * 4 + rr
+// times 512 bytes, so every store instruction writes 512 contiguous bytes
+// (whole cache lines) straight from the packed registers.  `soff` is the byte
+// offset of the chunk's blocks in the item's tiles.
+__device__ __forceinline__ void store_ds_tile(BufRsrc r, const bf16x8 (&dsb)[2], int g, int m, int soff,
+                                              int salt) {
+  const int ln = lane_in(salt);
+  const uint32_t lane_off = (uint32_t)(((m * 4 + g) * 4) * 512 + 8 * ln);
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const i32x4 wv = __builtin_bit_cast(i32x4, dsb[rr >> 1]);
+    u32x2 x;
+    x[0] = (unsigned)((rr & 1) ? wv[2] : wv[0]);
+    x[1] = (unsigned)((rr & 1) ? wv[3] : wv[1]);
+    __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)(lane_off + 512 * rr), soff, 0);
+  }
 }
 
 template <int D>
@@ -322,6 +353,7 @@ void attn_bwd_kernel(const BwdArgs a) {
   const int Sq = a.Sq, Sk = a.Sk;
 
   const ItemQueue iq{&a.counters[kCtrBwdNext], a.queue, a.cnt_k, n_items, max_items, a.nK, a.H, a.Hm, a.nQ};
+  const bool cache = tile_cache_on(a.counters, a.ds_cap);
   zero_row_terms<D>(sm, t);
   if (t == 0) iq.first(lds_hdr[0]);
   __syncthreads();
@@ -370,7 +402,7 @@ void attn_bwd_kernel(const BwdArgs a) {
     }
     load_chunk<D>(r0, x.qbase, x.obase, x.lbase, x.dbase, bq0, t);
   };
-  BwdItem cur = bwd_item<D>(a, lds_hdr[0]);
+  BwdItem cur = bwd_item<D>(a, lds_hdr[0], cache);
   if (cur.idx < n_items) {
     pf.take(iq, t);   // the ticket of the next item, before the item's loads
     preload(cur);
@@ -483,6 +515,13 @@ void attn_bwd_kernel(const BwdArgs a) {
         for (int t2 = 0; t2 < 2; ++t2) {
           sm.pds[g][m][0][t2][lane] = pb[t2];
           sm.pds[g][m][1][t2][lane] = dsb[t2];
+        }
+        {
+          // the chunk's scale * dS into the tile cache: tile j of the item is
+          // its j-th list entry (the walk starts at entry rot)
+          int j = c / CPB + cur.rot;
+          j = j < cnt ? j : j - cnt;
+          store_ds_tile(cur.dsrc, dsb, g, m, j * kTileBytes + (c % CPB) * (kTileBytes / CPB), c);
         }
         // ---- dV += P^T dO, dK += dS^T Q, head-dim half m, own rows ----
         constexpr int NP = NDH * 2;   // product pairs per half: (dd, t2)
@@ -617,7 +656,7 @@ void attn_bwd_kernel(const BwdArgs a) {
         }
     }
     __syncthreads();   // the tile and the next item's header are in LDS
-    const BwdItem nxt = bwd_item<D>(a, lds_hdr[(n + 1) & 1]);
+    const BwdItem nxt = bwd_item<D>(a, lds_hdr[(n + 1) & 1], cache);
     {
       // rows past the end of the keys fall outside the buffer range: the
       // stores are dropped
@@ -680,6 +719,10 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, int dq_grid
   }
   if (ev.end && (err = hipEventRecord(ev.end, stream)) != hipSuccess) return err;
   if (ev.begin2 && (err = hipEventRecord(ev.begin2, stream)) != hipSuccess) return err;
+  // dQ: from the tile cache when it is on, else recomputed; each of the two
+  // kernels reads the tile count and leaves at once when it is not the one
+  // (the cached kernel is launched only when the workspace holds a cache)
+  if ((err = launch_attn_bwd_dq_cached(a, head_dim, stream)) != hipSuccess) return err;
   if ((err = launch_attn_bwd_dq(a, head_dim, dq_grid, stream)) != hipSuccess) return err;
   if (ev.end2 && (err = hipEventRecord(ev.end2, stream)) != hipSuccess) return err;
   return hipSuccess;

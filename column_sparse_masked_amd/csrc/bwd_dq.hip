@@ -146,6 +146,9 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
   constexpr int NS = D / 16, ND = D / 32;
   constexpr int KST = DqSmem<D>::KST, KTS = DqSmem<D>::KTS;
   __shared__ DqSmem<D> sm;
+  // with the tile cache on, the cached kernel computes dQ from the stored
+  // scale * dS instead (the queue counters are left untouched)
+  if (tile_cache_on(a.counters, a.ds_cap)) return;
 
   const unsigned t = threadIdx.x;
   const int lane = (int)(t & 63), w = (int)(t >> 6);

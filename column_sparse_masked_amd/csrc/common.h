@@ -17,7 +17,12 @@ constexpr int kListIndex = 0x7fff;
 // counters[] slots inside the tileinfo buffer
 constexpr int kCtrFwdItems = 0, kCtrBwdItems = 1, kCtrFwdNext = 2, kCtrBwdNext = 3,
               kCtrFwdExit = 4, kCtrBwdExit = 5, kCtrDqNext = 6, kCtrDqExit = 7,
-              kCtrFwdSplit = 8;   // forward items split in two (the first of the queue)
+              kCtrFwdSplit = 8,   // forward items split in two (the first of the queue)
+              kCtrTiles = 9,      // non-skipped tiles over all (batch, head) pairs (saturating)
+              kCtrRowDone = 10;   // tile pass: row-kernel workgroups finished
+
+// Bytes of one cached tile of scale * dS (bf16, BQ rows of BK keys).
+constexpr int kTileBytes = BQ * BK * 2;
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -283,6 +288,13 @@ struct ItemPrefetch {
     publish(q, hdr, t);
   }
 };
+
+// Whether the backward runs with the tile cache: the caller gave room for
+// it and the tile pass counted no more tiles than that (same in every
+// thread: both values are uniform).
+__device__ __forceinline__ bool tile_cache_on(const uint32_t* counters, uint32_t cap) {
+  return cap > 0 && *(const_u32*)(counters + kCtrTiles) <= cap;
+}
 
 __device__ __forceinline__ const bf16x8& as_bf16x8(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);

@@ -484,7 +484,6 @@ hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t
       attn_fwd_kernel<64, false><<<grid, 256, 0, stream>>>(a);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (ev.end && (err = hipEventRecord(ev.end, stream)) != hipSuccess) return err;
   if (a.split_cap > 0 && grid > 0) {
     // the number of split items is on the device: one workgroup per
     // possible split item, up to the grid size, each looping
@@ -495,6 +494,8 @@ hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t
       fwd_merge_kernel<64><<<mgrid, 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  // the end event covers the merge of split items too: it is part of the forward
+  if (ev.end && (err = hipEventRecord(ev.end, stream)) != hipSuccess) return err;
   return hipSuccess;
 }
 

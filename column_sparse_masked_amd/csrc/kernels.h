@@ -14,8 +14,10 @@ struct TileArgs {
   int* cnt_k;
   uint16_t* list_q;
   uint16_t* list_k;
+  uint16_t* cpos;       // [B*Hm][nK][nQ]: position of a listed tile in its key block's list
   uint32_t* fwd_queue;
   uint32_t* bwd_queue;
+  uint32_t* colbase;    // [B*H*nK]: first tile slot of each backward item
   uint32_t* counters;
   int B, H, Hm, Sq, Sk, nQ, nK;
   int fwd_slots;   // workgroups of the forward's persistent grid
@@ -75,12 +77,31 @@ struct BwdArgs {
   __bf16* dk;
   __bf16* dv;
   float* delta;       // fp32 [B][H][Sq]
+  // Tile cache: scale * dS of every non-skipped tile, bf16 [slot][BQ rows][BK keys],
+  // written by the key-stationary kernel and read by the dQ kernel.  Used
+  // when ds_cap > 0 and the tile pass counted at most ds_cap tiles.
+  __bf16* ds;
+  uint32_t ds_cap;
+  const uint32_t* colbase;   // first slot of each backward item
+  const uint16_t* cpos;      // [B*Hm][nK][nQ]: position of a tile in its key block's list
   int B, H, Hm, Sq, Sk, nQ, nK;
   float scale;        // softmax_scale
   float scale_log2;   // softmax_scale * log2(e)
 };
 
 hipError_t launch_tile_bounds(const TileArgs& a, hipStream_t stream);
+
+// Context-parallel localisation of the bounds (kernel in localize.hip): a
+// rank's query chunks, in increasing global order, and each chunk's first
+// local row.
+constexpr int kMaxLocalChunks = 64;
+struct LocalizeArgs {
+  int n_chunks;
+  int start[kMaxLocalChunks];
+  int len[kMaxLocalChunks];
+  int off[kMaxLocalChunks];
+};
+hipError_t launch_localize(const int4* gb, int4* lb, long n, const LocalizeArgs& a, hipStream_t stream);
 // Optional events recorded right before / after the main attention kernel
 // (the forward kernel, the backward's dK/dV kernel) and around the backward's
 // dQ kernel (null: not recorded).
@@ -95,6 +116,7 @@ hipError_t launch_attn_fwd_fp8(const Fp8FwdArgs& a, int grid, hipStream_t stream
 hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, int dq_grid,
                            hipStream_t stream, const KernelEvents& ev);
 hipError_t launch_attn_bwd_dq(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
+hipError_t launch_attn_bwd_dq_cached(const BwdArgs& a, int head_dim, hipStream_t stream);
 // Zero-fills `bytes` (a multiple of 16) at the 16-byte aligned `p`.
 hipError_t launch_zero16(void* p, size_t bytes, hipStream_t stream);
 

@@ -1,70 +1,20 @@
 // Tile classification for the column-sparse mask (FlashMask-3 paper summary,
 // abstract: per key column, the mask keeps the bounds of the query-row ranges
-// it hides).  Three kernels:
-//   kbsum_kernel     per key block, min and max of each clamped bound;
-//   classify_kernel  class of every (query block, key block) tile plus, per
-//                    query block and per key block, the list of tiles that are
-//                    not skipped (the loops of the forward and backward);
-//   queue_kernel     forward and backward work items sorted by tile count,
-//                    heaviest first, for the persistent kernels.
+// it hides).  Two kernels:
+//   column_kernel  per key block, the min and max of each clamped bound, then
+//                  the block's column of tiles: which query blocks see it
+//                  (list_k, cnt_k) and each listed tile's place in that list;
+//   row_kernel     per query block, the class of every tile of its row (cls)
+//                  and its non-skipped key blocks (list_q, cnt_q); the last
+//                  workgroup to finish then sorts the forward and backward
+//                  work items by tile count, heaviest first, for the
+//                  persistent kernels, and lays out the backward's tile slots.
 #include <climits>
 
 #include "common.h"
 #include "kernels.h"
 
 namespace fm {
-
-// One workgroup of BK threads per (key block, batch*mask head); thread t owns
-// column kb*BK + t.  Output: 8 int32 per block (min/max of LTS, LTE, UTS, UTE
-// after clamping to [0, Sq]); columns >= Sk do not take part.
-__global__ __launch_bounds__(BK) void kbsum_kernel(const int4* __restrict__ bounds,
-                                                   int* __restrict__ kbsum, int Sq, int Sk,
-                                                   int nK) {
-  const int kb = blockIdx.x;
-  const long bhm = blockIdx.y;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int col = kb * BK + t;
-  int mn[4], mx[4];
-  if (col < Sk) {
-    int4 b = bounds[bhm * Sk + col];
-    int v[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      int x = min(max(v[c], 0), Sq);
-      mn[c] = x;
-      mx[c] = x;
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      mn[c] = INT_MAX;
-      mx[c] = INT_MIN;
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      mn[c] = min(mn[c], __shfl_xor(mn[c], off));
-      mx[c] = max(mx[c], __shfl_xor(mx[c], off));
-    }
-  }
-  __shared__ int red[BK / 64][8];
-  if (lane == 0) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      red[wave][2 * c] = mn[c];
-      red[wave][2 * c + 1] = mx[c];
-    }
-  }
-  __syncthreads();
-  if (t < 8) {
-    int r = red[0][t];
-#pragma unroll
-    for (int w = 1; w < BK / 64; ++w) r = (t & 1) ? max(r, red[w][t]) : min(r, red[w][t]);
-    kbsum[(bhm * nK + kb) * 8 + t] = r;
-  }
-}
 
 // Class of query rows [q0, q1) against a key-block summary.
 //   skip:    one interval covers the whole tile in every column
@@ -85,62 +35,6 @@ __device__ __forceinline__ void load_ks(const int* kbsum, long idx, int* ks) {
   int4 a = p[0], b = p[1];
   ks[0] = a.x; ks[1] = a.y; ks[2] = a.z; ks[3] = a.w;
   ks[4] = b.x; ks[5] = b.y; ks[6] = b.z; ks[7] = b.w;
-}
-
-// grid (nQ + nK, B*Hm), 256 threads.  Blocks x < nQ classify one query block's
-// row of tiles (writing cls, list_q, cnt_q); blocks x >= nQ one key block's
-// column (writing list_k, cnt_k).  Lists keep increasing block order; the
-// compaction uses a wave ballot and a 4-wave prefix.
-__global__ __launch_bounds__(256) void classify_kernel(const int* __restrict__ kbsum,
-                                                       uint8_t* __restrict__ cls,
-                                                       int* __restrict__ cnt_q,
-                                                       int* __restrict__ cnt_k,
-                                                       uint16_t* __restrict__ list_q,
-                                                       uint16_t* __restrict__ list_k, int Sq,
-                                                       int nQ, int nK) {
-  const long bhm = blockIdx.y;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  __shared__ int wsum[4];
-  const bool row_mode = (int)blockIdx.x < nQ;
-  const int blk = row_mode ? (int)blockIdx.x : (int)blockIdx.x - nQ;
-  const int n_other = row_mode ? nK : nQ;
-  uint16_t* list = row_mode ? list_q + (bhm * nQ + blk) * (long)nK
-                            : list_k + (bhm * nK + blk) * (long)nQ;
-  int ks_col[8];
-  if (!row_mode) load_ks(kbsum, bhm * nK + blk, ks_col);
-  int base = 0;
-  for (int o0 = 0; o0 < n_other; o0 += 256) {
-    const int o = o0 + t;
-    int c = 0;
-    if (o < n_other) {
-      if (row_mode) {
-        int ks[8];
-        load_ks(kbsum, bhm * nK + o, ks);
-        const int q0 = blk * BQ;
-        c = tile_class(ks, q0, min(Sq, q0 + BQ));
-        cls[(bhm * nQ + blk) * (long)nK + o] = (uint8_t)c;
-      } else {
-        const int q0 = o * BQ;
-        c = tile_class(ks_col, q0, min(Sq, q0 + BQ));
-      }
-    }
-    const bool keep = (o < n_other) && c != 0;
-    const unsigned long long m = __ballot(keep);
-    const int pos = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wave] = __popcll(m);
-    __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += wsum[w];
-    if (keep) list[off + pos] = (uint16_t)(o | (c == 2 ? kListPartial : 0));
-    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-  }
-  if (t == 0) {
-    if (row_mode)
-      cnt_q[bhm * nQ + blk] = base;
-    else
-      cnt_k[bhm * nK + blk] = base;
-  }
 }
 
 constexpr int kQueueThreads = 1024;
@@ -203,18 +97,41 @@ struct SplitRule {
   long* scratch;   // kQueueThreads / 64 longs
 };
 
+
+// atomicAdd(&hist[bucket], 1) for every active lane; returns the old value.
+// When every active lane of the wave has the same bucket (common: many
+// items share a tile count) that is one LDS atomic for the wave instead of
+// up to 64 on one address.
+__device__ __forceinline__ int wave_bucket_add(int* hist, int bucket, bool active) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long act = __ballot(active);
+  if (act == 0) return 0;
+  const int leader = __ffsll((long long)act) - 1;
+  const int b0 = __shfl(bucket, leader);
+  if (__ballot(active && bucket == b0) == act) {
+    int base = 0;
+    if (lane == leader) base = atomicAdd(&hist[b0], __popcll(act));
+    return __shfl(base, leader) + __popcll(act & ((1ull << lane) - 1ull));
+  }
+  return active ? atomicAdd(&hist[bucket], 1) : 0;
+}
+
 __device__ void sort_items(const int* __restrict__ cnt, uint32_t* __restrict__ queue, int B,
                            int H, int Hm, int nBlk, int* hist, int* scratch, const SplitRule* split) {
   const int t = threadIdx.x;
   const long n = (long)B * H * nBlk;
   for (int i = t; i < kBuckets; i += kQueueThreads) hist[i] = 0;
   __syncthreads();
-  for (long it = t; it < n; it += kQueueThreads) {
-    const long bh = it / nBlk;
-    const int blk = (int)(it % nBlk);
-    const int b = (int)(bh / H), h = (int)(bh % H);
-    const int c = cnt[((long)b * Hm + (Hm == 1 ? 0 : h)) * nBlk + blk];
-    atomicAdd(&hist[min(c, kBuckets - 1)], 1);
+  for (long i0 = 0; i0 < n; i0 += kQueueThreads) {
+    const long it = i0 + t;
+    int c = 0;
+    if (it < n) {
+      const long bh = it / nBlk;
+      const int blk = (int)(it % nBlk);
+      const int b = (int)(bh / H), h = (int)(bh % H);
+      c = cnt[((long)b * Hm + (Hm == 1 ? 0 : h)) * nBlk + blk];
+    }
+    wave_bucket_add(hist, min(c, kBuckets - 1), it < n);
   }
   __syncthreads();
   if (split) {
@@ -248,46 +165,225 @@ __device__ void sort_items(const int* __restrict__ cnt, uint32_t* __restrict__ q
     run += local[u];
   }
   __syncthreads();
-  for (long it = t; it < n; it += kQueueThreads) {
-    const long bh = it / nBlk;
-    const int blk = (int)(it % nBlk);
-    const int b = (int)(bh / H), h = (int)(bh % H);
-    const int c = cnt[((long)b * Hm + (Hm == 1 ? 0 : h)) * nBlk + blk];
-    const int pos = atomicAdd(&hist[min(c, kBuckets - 1)], 1);
-    queue[pos] = (uint32_t)it;
+  for (long i0 = 0; i0 < n; i0 += kQueueThreads) {
+    const long it = i0 + t;
+    int c = 0;
+    if (it < n) {
+      const long bh = it / nBlk;
+      const int blk = (int)(it % nBlk);
+      const int b = (int)(bh / H), h = (int)(bh % H);
+      c = cnt[((long)b * Hm + (Hm == 1 ? 0 : h)) * nBlk + blk];
+    }
+    const int pos = wave_bucket_add(hist, min(c, kBuckets - 1), it < n);
+    if (it < n) queue[pos] = (uint32_t)it;
   }
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kQueueThreads) void queue_kernel(
-    const int* __restrict__ cnt_q, const int* __restrict__ cnt_k, uint32_t* __restrict__ fwd_q,
-    uint32_t* __restrict__ bwd_q, uint32_t* __restrict__ counters, int B, int H, int Hm, int nQ,
-    int nK, int fwd_slots, int split_cap) {
-  // workgroup 0 sorts the forward (and dQ) queue, workgroup 1 the backward one
+// First tile slot of every backward item it = (b * H + h) * nK + kb: the
+// exclusive prefix sum of the items' tile counts in item order, so that the
+// tiles of one item (its list of query blocks, in list order) are
+// consecutive slots.  The total goes to counters[kCtrTiles]; sums beyond
+// 2^32 - 1 saturate there (no cache is that large).
+__device__ void tile_slots(const int* __restrict__ cnt, uint32_t* __restrict__ base, int B, int H,
+                           int Hm, int nBlk, uint32_t* total_out, int* scratch) {
+  const int t = threadIdx.x;
+  const long n = (long)B * H * nBlk;
+  unsigned long long run = 0;   // the same in every thread
+  for (long i0 = 0; i0 < n; i0 += kQueueThreads) {
+    const long it = i0 + t;
+    int c = 0;
+    if (it < n) {
+      const long bh = it / nBlk;
+      const int blk = (int)(it % nBlk);
+      const int b = (int)(bh / H), h = (int)(bh % H);
+      c = cnt[((long)b * Hm + (Hm == 1 ? 0 : h)) * nBlk + blk];
+    }
+    int chunk_total;
+    const int excl = block_exclusive_scan(c, scratch, &chunk_total);
+    if (it < n) base[it] = (uint32_t)min(run + (unsigned long long)excl, 0xFFFFFFFFull);
+    run += (unsigned long long)chunk_total;
+  }
+  if (t == 0) *total_out = (uint32_t)min(run, 0xFFFFFFFFull);
+}
+
+// Compaction of one list: NT threads each hold one candidate entry (keep);
+// the kept ones are written in thread order from list[base].  Returns the
+// number kept (the same in every thread).  wsum: NT / 64 ints of LDS.
+template <int NT>
+__device__ __forceinline__ int compact(bool keep, int* wsum, int base, int* pos_out) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const unsigned long long m = __ballot(keep);
+  const int pos = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) wsum[wave] = __popcll(m);
+  __syncthreads();
+  int off = base, total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int x = wsum[w];
+    off += w < wave ? x : 0;
+    total += x;
+  }
+  *pos_out = off + pos;
+  __syncthreads();
+  return total;
+}
+
+// grid (max(nK, 1), max(B*Hm, 1)), 256 threads.  Workgroup (kb, bhm): the
+// summary of key block kb (threads < BK own one column each; columns >= Sk
+// do not take part) into kbsum, then the block's column of tiles: for every
+// query block that is not skipped, its entry in list_k (increasing order,
+// bit 15 if partial) and, in cpos, that entry's position; cnt_k.  Workgroup
+// (0, 0) also zeroes the counter the row kernel's workgroups count off on.
+__global__ __launch_bounds__(256) void column_kernel(const int4* __restrict__ bounds, int* __restrict__ kbsum,
+                                                     int* __restrict__ cnt_k, uint16_t* __restrict__ list_k,
+                                                     uint16_t* __restrict__ cpos, uint32_t* __restrict__ counters,
+                                                     int Sq, int Sk, int nQ, int nK, long bhm_total) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) counters[kCtrRowDone] = 0;
+  const int kb = blockIdx.x;
+  const long bhm = blockIdx.y;
+  if (kb >= nK || bhm >= bhm_total) return;
+  // ---- key-block summary ----
+  const int col = kb * BK + t;
+  int mn[4], mx[4];
+  if (t < BK && col < Sk) {
+    const int4 b = bounds[bhm * Sk + col];
+    const int v[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mn[c] = mx[c] = min(max(v[c], 0), Sq);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      mn[c] = INT_MAX;
+      mx[c] = INT_MIN;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      mn[c] = min(mn[c], __shfl_xor(mn[c], off));
+      mx[c] = max(mx[c], __shfl_xor(mx[c], off));
+    }
+  }
+  __shared__ int red[4][8];
+  __shared__ int ks[8];
+  __shared__ int wsum[4];
+  if (lane == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      red[wave][2 * c] = mn[c];
+      red[wave][2 * c + 1] = mx[c];
+    }
+  }
+  __syncthreads();
+  if (t < 8) {
+    int r = red[0][t];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) r = (t & 1) ? max(r, red[w][t]) : min(r, red[w][t]);
+    ks[t] = r;
+    kbsum[(bhm * nK + kb) * 8 + t] = r;
+  }
+  __syncthreads();
+  int ksc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) ksc[c] = ks[c];
+  // ---- the block's column of tiles ----
+  uint16_t* list = list_k + (bhm * nK + kb) * (long)nQ;
+  uint16_t* cp = cpos + (bhm * nK + kb) * (long)nQ;
+  int base = 0;
+  for (int o0 = 0; o0 < nQ; o0 += 256) {
+    const int o = o0 + t;
+    int c = 0;
+    if (o < nQ) c = tile_class(ksc, o * BQ, min(Sq, o * BQ + BQ));
+    const bool keep = o < nQ && c != 0;
+    int at;
+    const int n = compact<256>(keep, wsum, base, &at);
+    if (keep) {
+      list[at] = (uint16_t)(o | (c == 2 ? kListPartial : 0));
+      cp[o] = (uint16_t)at;
+    }
+    base += n;
+  }
+  if (t == 0) cnt_k[bhm * nK + kb] = base;
+}
+
+// grid (max(nQ, 1), max(B*Hm, 1)), kQueueThreads threads.  Workgroup
+// (qb, bhm): the class of every tile of query block qb (cls) from the key
+// block summaries, and its list of non-skipped key blocks (list_q, cnt_q).
+// The last workgroup to finish (counted on counters[kCtrRowDone], zeroed by
+// the column kernel) then builds, with every count in place, the forward
+// queue (and how many of its items to split), the backward queue, the
+// backward items' first tile slots, and the counters the attention kernels
+// start from.
+__global__ __launch_bounds__(kQueueThreads) void row_kernel(
+    const int* __restrict__ kbsum, uint8_t* __restrict__ cls, int* __restrict__ cnt_q,
+    const int* __restrict__ cnt_k, uint16_t* __restrict__ list_q, uint32_t* __restrict__ fwd_q,
+    uint32_t* __restrict__ bwd_q, uint32_t* __restrict__ colbase, uint32_t* __restrict__ counters, int B, int H,
+    int Hm, int Sq, int nQ, int nK, int fwd_slots, int split_cap) {
   __shared__ int hist[kBuckets];
   __shared__ int scratch[kQueueThreads / 64 + 1];
   __shared__ long lscratch[kQueueThreads / 64];
-  if (blockIdx.x == 0) {
-    __shared__ uint32_t nsplit;
-    if (threadIdx.x == 0) nsplit = 0;
-    const SplitRule rule{fwd_slots, split_cap, &nsplit, lscratch};
-    if (nQ > 0) sort_items(cnt_q, fwd_q, B, H, Hm, nQ, hist, scratch, split_cap > 0 ? &rule : nullptr);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      counters[kCtrFwdItems] = (uint32_t)((long)B * H * nQ);
-      counters[kCtrFwdSplit] = nsplit;
-      counters[kCtrFwdNext] = 0;
-      counters[kCtrFwdExit] = 0;
-      counters[kCtrDqNext] = 0;
-      counters[kCtrDqExit] = 0;
+  __shared__ uint32_t last, nsplit, ntiles;
+  const int t = threadIdx.x;
+  const int qb = blockIdx.x;
+  const long bhm = blockIdx.y;
+  if (qb < nQ && bhm < (long)B * Hm) {
+    uint16_t* list = list_q + (bhm * nQ + qb) * (long)nK;
+    const int q0 = qb * BQ, q1 = min(Sq, q0 + BQ);
+    int base = 0;
+    for (int o0 = 0; o0 < nK; o0 += kQueueThreads) {
+      const int o = o0 + t;
+      int c = 0;
+      if (o < nK) {
+        int ks[8];
+        load_ks(kbsum, bhm * nK + o, ks);
+        c = tile_class(ks, q0, q1);
+        cls[(bhm * nQ + qb) * (long)nK + o] = (uint8_t)c;
+      }
+      const bool keep = o < nK && c != 0;
+      int at;
+      const int n = compact<kQueueThreads>(keep, scratch, base, &at);
+      if (keep) list[at] = (uint16_t)(o | (c == 2 ? kListPartial : 0));
+      base += n;
     }
-  } else {
-    if (nK > 0) sort_items(cnt_k, bwd_q, B, H, Hm, nK, hist, scratch, nullptr);
-    if (threadIdx.x == 0) {
-      counters[kCtrBwdItems] = (uint32_t)((long)B * H * nK);
-      counters[kCtrBwdNext] = 0;
-      counters[kCtrBwdExit] = 0;
+    // the row's count as an atomic, performed (the value returned) before
+    // this workgroup is counted as finished
+    if (t == 0) {
+      const int old = atomicExch(&cnt_q[bhm * nQ + qb], base);
+      asm volatile("s_waitcnt vmcnt(0)" ::"v"(old) : "memory");
     }
+  }
+  // ---- the last workgroup to finish builds the queues ----
+  // Only the counts cross between workgroups here (the lists and classes
+  // are read by later kernels).  They are written by atomics, which take
+  // effect where every workgroup's atomics do, so no cache write-back is
+  // needed for them; the last workgroup drops its own cached copies (an
+  // acquire fence) before it reads them.
+  if (t == 0) last = atomicAdd(&counters[kCtrRowDone], 1u) == gridDim.x * gridDim.y - 1 ? 1u : 0u;
+  __syncthreads();
+  if (!last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (t == 0) nsplit = 0;
+  __syncthreads();
+  const SplitRule rule{fwd_slots, split_cap, &nsplit, lscratch};
+  if (nQ > 0) sort_items(cnt_q, fwd_q, B, H, Hm, nQ, hist, scratch, split_cap > 0 ? &rule : nullptr);
+  if (nK > 0) sort_items(cnt_k, bwd_q, B, H, Hm, nK, hist, scratch, nullptr);
+  tile_slots(cnt_k, colbase, B, H, Hm, nK, &ntiles, scratch);
+  __syncthreads();
+  if (t == 0) {
+    counters[kCtrFwdItems] = (uint32_t)((long)B * H * nQ);
+    counters[kCtrFwdSplit] = nsplit;
+    counters[kCtrFwdNext] = 0;
+    counters[kCtrFwdExit] = 0;
+    counters[kCtrDqNext] = 0;
+    counters[kCtrDqExit] = 0;
+    counters[kCtrBwdItems] = (uint32_t)((long)B * H * nK);
+    counters[kCtrBwdNext] = 0;
+    counters[kCtrBwdExit] = 0;
+    counters[kCtrTiles] = ntiles;
+    counters[kCtrRowDone] = 0;
   }
 }
 
@@ -308,20 +404,17 @@ hipError_t launch_zero16(void* p, size_t bytes, hipStream_t stream) {
 }
 
 hipError_t launch_tile_bounds(const TileArgs& a, hipStream_t stream) {
-  const unsigned bhm = (unsigned)((long)a.B * a.Hm);
-  if (bhm > 0 && a.nK > 0) {
-    kbsum_kernel<<<dim3(a.nK, bhm), BK, 0, stream>>>(a.bounds, a.kbsum, a.Sq, a.Sk, a.nK);
-  }
-  if (bhm > 0 && a.nQ + a.nK > 0) {
-    classify_kernel<<<dim3(a.nQ + a.nK, bhm), 256, 0, stream>>>(a.kbsum, a.cls, a.cnt_q, a.cnt_k,
-                                                                a.list_q, a.list_k, a.Sq, a.nQ, a.nK);
-  }
-  // always, also for empty problems: it leaves (empty) queues and zeroed
-  // counters behind, with a kernel rather than a memset, which stays correct
-  // when a caller replays the calls as a captured graph
-  queue_kernel<<<2, kQueueThreads, 0, stream>>>(a.cnt_q, a.cnt_k, a.fwd_queue, a.bwd_queue,
-                                                a.counters, a.B, a.H, a.Hm, a.nQ, a.nK, a.fwd_slots,
-                                                a.split_cap);
+  // both kernels always run, with at least one workgroup, also for empty
+  // problems: they leave (empty) queues and zeroed counters behind, with
+  // kernels rather than a memset, which stays correct when a caller replays
+  // the calls as a captured graph
+  const long bhm = (long)a.B * a.Hm;
+  const unsigned gy = (unsigned)(bhm > 0 ? bhm : 1);
+  column_kernel<<<dim3((unsigned)(a.nK > 0 ? a.nK : 1), gy), 256, 0, stream>>>(
+      a.bounds, a.kbsum, a.cnt_k, a.list_k, a.cpos, a.counters, a.Sq, a.Sk, a.nQ, a.nK, bhm);
+  row_kernel<<<dim3((unsigned)(a.nQ > 0 ? a.nQ : 1), gy), kQueueThreads, 0, stream>>>(
+      a.kbsum, a.cls, a.cnt_q, a.cnt_k, a.list_q, a.fwd_queue, a.bwd_queue, a.colbase, a.counters, a.B, a.H,
+      a.Hm, a.Sq, a.nQ, a.nK, a.fwd_slots, a.split_cap);
   return hipGetLastError();
 }
 

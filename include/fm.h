@@ -73,7 +73,9 @@ typedef struct {
  *   counters  uint32[16]: [0] forward items, [1] backward items,
  *             [2],[3] forward / backward next-item counters, [4],[5] exit counters,
  *             [6],[7] the dQ kernel's next-item and exit counters,
- *             [8] forward items split in two (the first entries of fwd_queue)
+ *             [8] forward items split in two (the first entries of fwd_queue),
+ *             [9] non-skipped tiles over every (batch, head) pair (saturating),
+ *             [10] the tile pass's own count of finished workgroups (left at 0)
  *   kbsum     int32 [B][Hm][nK][8]  per key block, over its columns j < Sk, the
  *             min and max of each bound clamped to [0, Sq]:
  *             LTS min, LTS max, LTE min, LTE max, UTS min, UTS max, UTE min, UTE max
@@ -87,10 +89,18 @@ typedef struct {
  *   bwd_queue uint32[B*H*nK]         backward items (b*H+h)*nK+kb, most tiles first
  *   fwd_partials bf16[2*C][block_q][D] then float[2*C][block_q], C = min(B*H*nQ, 512):
  *             for each split forward item, the output and LSE of each half of
- *             its key blocks (scratch of fm_attn_fwd; no meaning between calls) */
+ *             its key blocks (scratch of fm_attn_fwd; no meaning between calls)
+ *   cpos      uint16[B][Hm][nK][nQ] for each non-skipped tile (qb, kb), the
+ *             position of qb in list_k of kb (other entries are not written)
+ *   colbase   uint32[B*H*nK]       first tile slot of each backward item
+ *             (b*H+h)*nK+kb: the prefix sum of the items' tile counts in item
+ *             order, so that the tiles of item i, in its list order, take
+ *             slots colbase[i] .. colbase[i] + cnt - 1 of the backward's tile
+ *             cache; counters[9] holds the total (saturating at 2^32 - 1) */
 typedef struct {
   int32_t block_q, block_k, n_qblocks, n_kblocks;
   size_t counters, kbsum, cls, cnt_q, cnt_k, list_q, list_k, fwd_queue, bwd_queue, fwd_partials;
+  size_t cpos, colbase;
   size_t total;           /* bytes the caller must allocate                     */
 } fm_tileinfo_layout;
 
@@ -107,15 +117,23 @@ fm_status fm_tileinfo_layout_query(const fm_problem* p, fm_tileinfo_layout* out)
  * Delta (host only). */
 fm_status fm_bwd_workspace_bytes(const fm_problem* p, size_t* bytes);
 
+/* Bytes of a fm_attn_bwd workspace that also holds the tile cache for
+ * n_tiles non-skipped tiles (32 KiB each: scale * dS in bf16), after the Delta
+ * row terms: the size at which the backward computes dQ from the cache.  The
+ * tile count of a problem is counter 9 of its tileinfo after fm_tile_bounds
+ * (host only; FM_ERR_SHAPE for n_tiles >= 2^32 - 1). */
+fm_status fm_bwd_cache_bytes(const fm_problem* p, uint64_t n_tiles, size_t* bytes);
+
 /* Number of compute units of the current device (queried once, then cached). */
 fm_status fm_device_cu_count(int32_t* cus);
 
 /* Benchmark hook.  While set, every fm_attn_fwd / fm_attn_bwd call made from
  * this host thread records the caller's hipEvent_t `begin` on its stream right
  * before launching its main attention kernel (the forward kernel; the
- * backward's dK/dV kernel) and `end` right after it, and `begin2` / `end2`
- * around the backward's dQ kernel, so that hipEventElapsedTime(begin, end)
- * spans exactly one kernel (the backward's Delta prologue falls outside).
+ * backward's dK/dV kernel) and `end` right after it (for the forward, after
+ * the merge of split items), and `begin2` / `end2` around the backward's dQ
+ * kernels, so that hipEventElapsedTime(begin, end) spans the main kernel (the
+ * backward's Delta prologue falls outside).
  * Events must have been created with timing enabled.  All null turns the hook
  * off; either pair may be null; giving only one event of a pair is
  * FM_ERR_NULL.  Nothing else about the calls changes; a failed record makes
@@ -128,8 +146,10 @@ fm_status fm_set_kernel_events(void* begin, void* end, void* begin2, void* end2)
  * query-row ranges it hides, which lets whole tiles be
  * recognised as fully masked (skipped), unmasked (full) or mixed (partial).
  * Reads `bounds`; writes every part of `tileinfo` and zeroes its counters.
- * Three kernels: key-block min/max, tile classification with per-block lists,
- * and the cost-sorted work queues (heaviest items first).
+ * Two kernels: per key block, its min/max summary and its column of tiles
+ * (list_k, cpos); per query block, its row of tiles (cls, list_q), after
+ * which the last workgroup to finish sorts the work queues (heaviest items
+ * first) and lays out the backward's tile slots (colbase).
  */
 fm_status fm_tile_bounds(const fm_problem* p, const int32_t* bounds, void* tileinfo, void* stream);
 
@@ -198,12 +218,20 @@ fm_status fm_attn_fwd_fp8(const fm_problem* p, const void* q, const void* k, con
  * fp32 [B][H][Sq] (`o` and `lse` the forward's outputs), bounds int32
  * [B][Hm][Sk][4], tileinfo from fm_tile_bounds (all device, read; the
  * tileinfo's backward counters are written); dq bf16 [B][H][Sq][D], dk, dv
- * bf16 [B][H][Sk][D] (device, written).  `workspace` must hold
- * fm_bwd_workspace_bytes bytes, 16-byte aligned; its contents on entry do not
- * matter.  All are caller-owned.  Three kernels: Delta; dK and dV
- * key-stationary over the tiles of each key block; dQ query-stationary over
- * the tiles of each query block (S and dP recomputed, no atomics).  The
- * results are deterministic.
+ * bf16 [B][H][Sk][D] (device, written).  `workspace` (device, 16-byte
+ * aligned, caller-owned, contents on entry irrelevant) holds
+ * `workspace_bytes` bytes, at least fm_bwd_workspace_bytes: the Delta row
+ * terms, then optionally the tile cache.  Kernels: Delta; dK and dV
+ * key-stationary over the tiles of each key block, which forms scale * dS
+ * of every tile; dQ query-stationary over the tiles of each query block.
+ * When the workspace holds the tile cache for every non-skipped tile
+ * (fm_bwd_cache_bytes of the tile count the tile pass leaves in tileinfo
+ * counter 9), the dK/dV kernel also stores scale * dS there (bf16) and dQ is
+ * its product with K, read back from the cache; otherwise dQ recomputes S
+ * and dP.  The choice is made on the device from the tile count, so a cache
+ * sized for other bounds is never overrun: the call falls back to the
+ * recompute.  No atomics; the results are deterministic (the two dQ paths
+ * round dS identically but may differ in the last bits).
  * Errors: FM_ERR_NULL for a missing tensor that the problem needs,
  * FM_ERR_ALIGN as fm_attn_fwd (workspace: 16 bytes), the problem's own
  * checks, FM_ERR_HIP for a launch the runtime rejects.  With Sq = 0, dK and
@@ -212,7 +240,34 @@ fm_status fm_attn_fwd_fp8(const fm_problem* p, const void* q, const void* k, con
 fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v,
                       const void* o, const void* dout, const float* lse,
                       const int32_t* bounds, void* tileinfo,
-                      void* dq, void* dk, void* dv, void* workspace, void* stream);
+                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * fm_localize_bounds - one context-parallel rank's bounds from the global ones.
+ * "FlashMask-3 targets masked distributed attention on Hopper GPUs",
+ * In-depth insight (the abstract): under any multi-chunk context-parallel
+ * assignment, per-rank mask localisation is a clip-shift-max on the boundary
+ * vectors that needs no communication, and its result feeds the single-GPU
+ * kernel unchanged.
+ * The rank holds n_chunks query chunks [chunk_start[c], chunk_start[c] +
+ * chunk_len[c]) of the global rows (HOST arrays, 1 <= n_chunks <= 64, starts
+ * and lengths >= 0, in increasing global order and disjoint), stacked in
+ * that order as its local rows 0 .. Sq_local - 1 (Sq_local = sum of the
+ * lengths).  Every bound g of global_bounds (device, int32
+ * [batch][mask_heads][seqlen_k][4], any int32 values) becomes, in
+ * local_bounds (device, same shape; may not alias), the number of local rows
+ * whose global index is below g: the maximum over chunks starting at or
+ * before g of the chunk's first local row plus g clipped into the chunk
+ * (0 if no chunk starts at or before g).  A local row is then masked for a
+ * key exactly when its global row is.  The key axis is unchanged.  Both
+ * pointers 16-byte aligned.  Errors: FM_ERR_SHAPE for bad sizes or chunks
+ * (overlapping, decreasing, more than 64, Sq_local beyond the library's
+ * limit), FM_ERR_NULL, FM_ERR_ALIGN, FM_ERR_HIP.  One kernel on `stream`.
+ */
+fm_status fm_localize_bounds(int32_t batch, int32_t mask_heads, int32_t seqlen_k, const int32_t* global_bounds,
+                             int32_t n_chunks, const int32_t* chunk_start, const int32_t* chunk_len,
+                             int32_t* local_bounds, void* stream);
 
 /*
  * fm_attn_bwd_noalloc - fm_attn_bwd without a workspace argument, for callers

@@ -244,6 +244,24 @@ def rows_seeing(bounds_h, Sq, cols) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------- #
+# context-parallel localisation                                               #
+# --------------------------------------------------------------------------- #
+def localize_bounds(global_bounds, chunk_start, chunk_len):
+    """One context-parallel rank's bounds (FlashMask-3 paper summary,
+    abstract: a rank's mask comes from the global boundary vectors without
+    communication).  The rank's local rows are its chunks' global rows
+    stacked in the given (increasing) order; a global bound g becomes the
+    number of local rows whose global index is below g, counted directly:
+    the plain definition, which makes a local row masked exactly when its
+    global row is.  Returns int64 values of the same shape."""
+    rows = np.concatenate([np.arange(int(s), int(s) + int(n), dtype=np.int64)
+                           for s, n in zip(chunk_start, chunk_len)] + [np.zeros(0, np.int64)])
+    g = np.asarray(global_bounds, dtype=np.int64)
+    # count of rows < g for every bound: searchsorted on the sorted rows
+    return np.searchsorted(np.sort(rows), g, side="left").astype(np.int64)
+
+
+# --------------------------------------------------------------------------- #
 # tile classification                                                         #
 # --------------------------------------------------------------------------- #
 SKIP, FULL, PARTIAL = 0, 1, 2

@@ -25,9 +25,12 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(w, tensors=None, device="cuda", want_bwd=True):
+def run_gpu(w, tensors=None, device="cuda", want_bwd=True, both_paths=False):
     """Upload a workload, run tile pass + forward (+ backward) on the GPU and
-    return numpy results (float64) and the tileinfo dictionary."""
+    return numpy results (float64) and the tileinfo dictionary.  The backward
+    runs with the tile cache (dQ from the cached scale * dS, as the benchmark
+    runs it); with both_paths it runs again without the cache (dQ recomputed)
+    into dq_rc, dk_rc, dv_rc."""
     import torch
     from column_sparse_masked_amd.api import MaskedAttention, to_device_bf16, to_device_bounds
     q, k, v, do = tensors if tensors is not None else w.draw()
@@ -38,8 +41,13 @@ def run_gpu(w, tensors=None, device="cuda", want_bwd=True):
     o, lse = att.forward(tq, tk, tv, tb)
     res = {"o": o, "lse": lse}
     if want_bwd:
+        att.reserve_tile_cache()
         dq, dk, dv = att.backward(tq, tk, tv, o, tdo, lse, tb)
         res.update(dq=dq, dk=dk, dv=dv)
+        if both_paths:
+            att.drop_tile_cache()
+            dq2, dk2, dv2 = att.backward(tq, tk, tv, o, tdo, lse, tb)
+            res.update(dq_rc=dq2, dk_rc=dk2, dv_rc=dv2)
     torch.cuda.synchronize()
     out = {n: t.float().cpu().numpy().astype(np.float64) for n, t in res.items()}
     out["tileinfo"] = att.read_tileinfo()
@@ -71,10 +79,14 @@ def check_full(w, got, tensors, label=""):
     assert err_o <= O_TOL, f"{label} O max-abs {err_o}"
     check_lse(got["lse"], rl)
     errs = {}
-    for n, r in (("dq", rdq), ("dk", rdk), ("dv", rdv)):
+    for n, r in (("dq", rdq), ("dk", rdk), ("dv", rdv), ("dq_rc", rdq), ("dk_rc", rdk), ("dv_rc", rdv)):
         if n in got:
             errs[n] = rel_l2(got[n], r)
             assert errs[n] <= GRAD_TOL, f"{label} {n} rel-L2 {errs[n]}"
+    # the two backward paths run the same dK / dV kernel: identical dK, dV
+    for n in ("dk", "dv"):
+        if n + "_rc" in got:
+            assert np.array_equal(got[n], got[n + "_rc"]), f"{label} {n} differs between the dQ paths"
     say(f"{label}: O max-abs {err_o:.3e} " + " ".join(f"{n} {e:.3e}" for n, e in errs.items()))
     return err_o, errs
 
@@ -111,6 +123,20 @@ def check_tileinfo(w, ti):
     c = ti["counters"]
     assert c[0] == B * H * nQ and c[1] == B * H * nK and c[2] == 0 and c[3] == 0
     assert c[8] == expected_split_count(cq, H, Hm), "number of split forward items differs"
+    # the backward's tile slots: each listed tile's position in its key
+    # block's list, and each backward item's first slot (the running total
+    # of the items' tile counts in item order)
+    for b in range(B):
+        for hm in range(Hm):
+            for kb in range(nK):
+                qbs = np.nonzero(cls[b, hm, :, kb])[0]
+                assert np.array_equal(ti["cpos"][b, hm, kb, qbs], np.arange(qbs.size)), ("cpos", b, hm, kb)
+    per_item = np.repeat(ck, H // Hm, axis=1) if Hm == 1 else ck      # [B][H][nK]
+    flat = per_item.reshape(-1).astype(np.int64)
+    want = np.concatenate([[0], np.cumsum(flat)[:-1]]) if flat.size else flat
+    assert np.array_equal(ti["colbase"].astype(np.int64), want), "colbase differs"
+    assert c[9] == int(flat.sum()), "tile count differs"
+    assert c[10] == 0
 
 
 def expected_split_count(cq, H, Hm):

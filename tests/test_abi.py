@@ -30,7 +30,7 @@ def test_every_declared_function_is_exported():
 
 def test_struct_sizes_match_header():
     assert ctypes.sizeof(L.Problem) == 28
-    assert ctypes.sizeof(L.TileinfoLayout) == 16 + 11 * 8
+    assert ctypes.sizeof(L.TileinfoLayout) == 16 + 13 * 8
 
 
 def _p(**kw):
@@ -65,7 +65,7 @@ def test_bad_problems_rejected_everywhere(kw, code):
     fake = ctypes.c_void_p(1 << 20)
     assert L.lib.fm_tile_bounds(ctypes.byref(p), fake, fake, None) == code
     assert L.lib.fm_attn_fwd(ctypes.byref(p), *([fake] * 7), None) == code
-    assert L.lib.fm_attn_bwd(ctypes.byref(p), *([fake] * 12), None) == code
+    assert L.lib.fm_attn_bwd(ctypes.byref(p), *([fake] * 12), 1 << 20, None) == code
 
 
 def test_null_problem_and_outputs():
@@ -91,7 +91,7 @@ def test_null_tensors_rejected_before_launch():
     for i in range(12):
         a = list(args)
         a[i] = None
-        assert L.lib.fm_attn_bwd(ctypes.byref(p), *a, None) == L.FM_ERR_NULL, i
+        assert L.lib.fm_attn_bwd(ctypes.byref(p), *a, 1 << 20, None) == L.FM_ERR_NULL, i
 
 
 def test_misaligned_tensors_rejected_before_launch():
@@ -112,7 +112,7 @@ def test_misaligned_tensors_rejected_before_launch():
         a[i] = bad
         if i == 5:     # lse
             continue
-        assert L.lib.fm_attn_bwd(ctypes.byref(p), *a, None) == L.FM_ERR_ALIGN, i
+        assert L.lib.fm_attn_bwd(ctypes.byref(p), *a, 1 << 20, None) == L.FM_ERR_ALIGN, i
 
 
 def test_status_strings():
@@ -136,7 +136,8 @@ def test_tileinfo_layout(B, H, Hm, Sq, Sk):
              ("fwd_queue", B * H * nQ * 4), ("bwd_queue", B * H * nK * 4),
              # two partial-result slots (bf16 O, fp32 LSE of 128 rows) per forward
              # item that may be split, at most 512 of them
-             ("fwd_partials", 2 * min(B * H * nQ, 512) * 128 * (128 * 2 + 4))]
+             ("fwd_partials", 2 * min(B * H * nQ, 512) * 128 * (128 * 2 + 4)),
+             ("cpos", B * Hm * nK * nQ * 2), ("colbase", B * H * nK * 4)]
     end = 0
     for name, size in parts:
         off = getattr(lay, name)
@@ -145,6 +146,9 @@ def test_tileinfo_layout(B, H, Hm, Sq, Sk):
     assert lay.total >= end
     ws = L.bwd_workspace_bytes(p)
     assert ws >= B * H * Sq * 4   # Delta of every row
+    # the tile cache follows Delta at a 256-byte boundary, 32 KiB per tile
+    assert L.bwd_cache_bytes(p, 0) == ws
+    assert L.bwd_cache_bytes(p, 37) == ws + 37 * 128 * 128 * 2
 
 
 def test_fp8_forward_validation():
@@ -283,3 +287,37 @@ def test_noalloc_backward_validation():
         a = [fake] * 11
         a[i] = bad
         assert L.lib.fm_attn_bwd_noalloc(ctypes.byref(p), *a, None) == L.FM_ERR_ALIGN, i
+
+
+def test_cache_bytes_validation():
+    p = _p()
+    n = ctypes.c_size_t()
+    assert L.lib.fm_bwd_cache_bytes(ctypes.byref(p), ctypes.c_uint64(1), None) == L.FM_ERR_NULL
+    assert L.lib.fm_bwd_cache_bytes(ctypes.byref(p), ctypes.c_uint64(1 << 32), ctypes.byref(n)) == L.FM_ERR_SHAPE
+    bad = _p(head_dim=96)
+    assert L.lib.fm_bwd_cache_bytes(ctypes.byref(bad), ctypes.c_uint64(1), ctypes.byref(n)) == L.FM_ERR_UNSUPPORTED
+
+
+def test_localize_validation():
+    """fm_localize_bounds rejects bad sizes and chunk lists (decreasing,
+    overlapping, negative, none, more than 64) before any HIP call."""
+    fake = ctypes.c_void_p(1 << 20)
+    I = ctypes.c_int32
+
+    def call(B, Hm, Sk, starts, lens, gb=fake, lb=fake):
+        n = len(starts)
+        s = (I * max(n, 1))(*starts)
+        l_ = (I * max(n, 1))(*lens)
+        return L.lib.fm_localize_bounds(B, Hm, Sk, gb, n, s, l_, lb, None)
+
+    assert call(1, 1, 8, [5, 0], [2, 2]) == L.FM_ERR_SHAPE      # decreasing
+    assert call(1, 1, 8, [0, 3], [5, 1]) == L.FM_ERR_SHAPE      # overlapping
+    assert call(1, 1, 8, [-1], [3]) == L.FM_ERR_SHAPE
+    assert call(1, 1, 8, [0], [-2]) == L.FM_ERR_SHAPE
+    assert call(1, 1, 8, [], []) == L.FM_ERR_SHAPE
+    assert call(1, 1, 8, list(range(0, 130, 2)), [1] * 65) == L.FM_ERR_SHAPE
+    assert call(-1, 1, 8, [0], [3]) == L.FM_ERR_SHAPE
+    assert call(1, 0, 8, [0], [3]) == L.FM_ERR_SHAPE
+    assert call(1, 1, 8, [0], [3], gb=None) == L.FM_ERR_NULL
+    assert call(1, 1, 8, [0], [3], lb=ctypes.c_void_p((1 << 20) + 4)) == L.FM_ERR_ALIGN
+    assert L.lib.fm_localize_bounds(1, 1, 8, fake, 1, None, None, fake, None) == L.FM_ERR_NULL

@@ -91,6 +91,7 @@ def _run(w, tensors):
     tb = to_device_bounds(w.bounds)
     att = MaskedAttention.for_workload(w)
     att.tile_bounds(tb)
+    att.reserve_tile_cache()      # the benchmark's configuration: dQ from the tile cache
     o, lse = att.forward(tq, tk, tv, tb)
     dq, dk, dv = att.backward(tq, tk, tv, o, tdo, lse, tb)
     torch.cuda.synchronize()
@@ -219,9 +220,10 @@ def test_context_parallel_shares_add_up():
     global call: each rank's O and LSE equal the global rows, and the ranks'
     dK, dV add up to the global dK, dV (FlashMask-3 paper summary, abstract:
     the per-rank localisation needs no communication and feeds the same
-    single-GPU kernel)."""
+    single-GPU kernel).  Each rank's bounds come from fm_localize_bounds on
+    the device."""
     import torch
-    from column_sparse_masked_amd.api import MaskedAttention, to_device_bf16, to_device_bounds
+    from column_sparse_masked_amd.api import MaskedAttention, localize_bounds, to_device_bf16, to_device_bounds
     H, S, D, world = 16, 65536, 128, 8
     base = M.cp_rank_share(H=H, S=S, D=D, world=world, rank=0, seed=5)
     gb = base.structure["global_bounds"]
@@ -233,6 +235,7 @@ def test_context_parallel_shares_add_up():
     gatt = MaskedAttention.for_workload(glob)
     tgb = to_device_bounds(glob.bounds)
     gatt.tile_bounds(tgb)
+    gatt.reserve_tile_cache()
     go, glse = gatt.forward(tq, tk, tv, tgb)
     gdq, gdk, gdv = gatt.backward(tq, tk, tv, go, tdo, glse, tgb)
     sum_dk = torch.zeros_like(gdk, dtype=torch.float32)
@@ -243,8 +246,11 @@ def test_context_parallel_shares_add_up():
         idx = torch.as_tensor(share.structure["global_rows"], device=tq.device)
         lq, ldo = tq[:, :, idx].contiguous(), tdo[:, :, idx].contiguous()
         att = MaskedAttention.for_workload(share)
-        tb = to_device_bounds(share.bounds)
+        # the rank's bounds localised on the device from the global ones
+        tb = localize_bounds(tgb, [r * C, (2 * world - 1 - r) * C], [C, C])
+        assert np.array_equal(tb.cpu().numpy(), share.bounds), f"rank {r}: localised bounds differ"
         att.tile_bounds(tb)
+        att.reserve_tile_cache()
         lo, llse = att.forward(lq, tk, tv, tb)
         ldq, ldk, ldv = att.backward(lq, tk, tv, lo, ldo, llse, tb)
         torch.cuda.synchronize()

@@ -11,7 +11,8 @@ from column_sparse_masked_amd import masks as M
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("cache", [True, False], ids=["tile_cache", "recompute"])
+def test_graph_replays_match_eager(cache):
     import torch
     from column_sparse_masked_amd.api import MaskedAttention, to_device_bf16, to_device_bounds
     from _parity import say
@@ -31,6 +32,9 @@ def test_graph_replays_match_eager():
 
     ref = [torch.empty_like(x) for x in outs]
     step(*ref)
+    if cache:
+        att.reserve_tile_cache()
+        step(*ref)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):

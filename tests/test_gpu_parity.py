@@ -93,7 +93,7 @@ CASES = _cases()
 def test_small_problem_parity(name):
     w = CASES[name]()
     say(f"[parity] {name}: B={w.B} H={w.H} Hm={w.Hm} Sq={w.Sq} Sk={w.Sk} D={w.D}")
-    got, tensors = run_gpu(w)
+    got, tensors = run_gpu(w, both_paths=True)
     check_tileinfo(w, got["tileinfo"])
     check_full(w, got, tensors, name)
 
@@ -174,12 +174,12 @@ def test_large_logit_parity(name):
     ro, rl, rdq, rdk, rdv = oracle.attention(up(q), up(k), up(v), up(do), w.bounds, w.scale)
     fin = np.isfinite(rl)
     assert np.abs(rl[fin]).max() / w.scale > 200, "the case does not reach large logits"
-    got, _ = run_gpu(w, (q, k, v, do))
+    got, _ = run_gpu(w, (q, k, v, do), both_paths=True)
     bound = _o_bound_large_logits(w, q, k, v, rl) + 2.0 ** -8 * np.abs(ro) + 1e-4 * np.abs(up(v)).max()
     err = np.abs(got["o"] - ro)
     ratio = float((err / bound).max())
     check_lse(got["lse"], rl)
-    errs = {n: rel_l2(got[n], r) for n, r in (("dq", rdq), ("dk", rdk), ("dv", rdv))}
+    errs = {n: rel_l2(got[n], r) for n, r in (("dq", rdq), ("dk", rdk), ("dv", rdv), ("dq_rc", rdq))}
     say(f"{name}: O max-abs {err.max():.3e}, max error/bound {ratio:.3f}, "
         + " ".join(f"{n} {e:.3e}" for n, e in errs.items()))
     assert ratio <= 1.0, f"O error above its bound ({ratio})"
@@ -191,8 +191,9 @@ def test_empty_key_set():
     """Sk = 0: every row is fully masked: O = 0, LSE = +inf, dQ = 0."""
     w = M.custom(np.zeros((0, 4), np.int32), B=1, H=2, Sq=200, D=128, seed=40)
     say("[parity] empty key set")
-    got, _ = run_gpu(w)
+    got, _ = run_gpu(w, both_paths=True)
     assert (got["o"] == 0).all() and np.isposinf(got["lse"]).all() and (got["dq"] == 0).all()
+    assert (got["dq_rc"] == 0).all()
     assert got["dk"].size == 0
 
 
@@ -207,7 +208,7 @@ def test_empty_problem_zeroes_counters():
     att.buf.tileinfo.fill_(0xFF)
     att.tile_bounds(to_device_bounds(w.bounds))
     torch.cuda.synchronize()
-    assert att.read_tileinfo()["counters"].tolist() == [0] * 9 + [0xFFFFFFFF] * 7
+    assert att.read_tileinfo()["counters"].tolist() == [0] * 11 + [0xFFFFFFFF] * 5
 
 
 def test_empty_query_set():
@@ -243,6 +244,7 @@ def test_repeated_calls_reuse_tileinfo():
     tb = to_device_bounds(w.bounds)
     tq, tk, tv, tdo = (to_device_bf16(x) for x in (q, k, v, do))
     att.tile_bounds(tb)
+    att.reserve_tile_cache()
     outs = []
     for _ in range(3):
         o, lse = att.forward(tq, tk, tv, tb)
@@ -254,3 +256,33 @@ def test_repeated_calls_reuse_tileinfo():
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{name} differs between calls"
     ti = att.read_tileinfo()
     assert ti["counters"][2:8].tolist() == [0] * 6
+
+
+def test_tile_cache_too_small_falls_back():
+    """A workspace whose tile cache holds fewer tiles than the tile pass
+    counted (a cache sized for other bounds): the backward must not overrun
+    it and falls back to recomputing dQ, bit-identical to the call without a
+    cache; a cache of exactly the tile count gives the cached result."""
+    import torch
+    from column_sparse_masked_amd.api import MaskedAttention, to_device_bf16, to_device_bounds
+    w = M.custom(M.causal_document_bounds([700, 500, 300]), B=1, H=3, Sq=1500, D=128, seed=47)
+    say("[parity] tile cache too small")
+    q, k, v, do = w.draw()
+    att = MaskedAttention.for_workload(w)
+    tb = to_device_bounds(w.bounds)
+    tq, tk, tv, tdo = (to_device_bf16(x) for x in (q, k, v, do))
+    att.tile_bounds(tb)
+    o, lse = att.forward(tq, tk, tv, tb)
+    n = att.tile_count()
+    ref = [x.clone() for x in att.backward(tq, tk, tv, o, tdo, lse, tb)]          # no cache
+    att.reserve_tile_cache(n - 1)
+    small = [x.clone() for x in att.backward(tq, tk, tv, o, tdo, lse, tb)]
+    att.reserve_tile_cache(n)
+    full = [x.clone() for x in att.backward(tq, tk, tv, o, tdo, lse, tb)]
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), ref, small):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name}: fallback differs"
+    for name, a, b in zip(("dk", "dv"), ref[1:], full[1:]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name}: cached path differs"
+    rel = ((full[0].float() - ref[0].float()).norm() / ref[0].float().norm()).item()
+    assert 0 < rel < 2e-3, f"cached dQ vs recomputed dQ: rel-L2 {rel}"

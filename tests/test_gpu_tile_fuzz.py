@@ -1,0 +1,63 @@
+"""GPU fuzz of the tile pass: a few hundred random small problems in one
+process, each compared bit for bit with the oracle's key-block summaries and
+tile classes, and checked for exact lists, counts, queues, tile slots and
+counters (stops at the first mismatch).
+
+FlashMask-3 paper summary, abstract: the four boundary vectors compress the
+mask to O(n), which is what lets whole tiles be classified from per-block
+minima and maxima."""
+import numpy as np
+import pytest
+
+from column_sparse_masked_amd import masks as M
+from _parity import check_tileinfo, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _random_problem(rng):
+    B = int(rng.integers(1, 3))
+    H = int(rng.integers(1, 5))
+    Hm = H if rng.random() < 0.3 else 1
+    small = rng.random() < 0.6
+    Sq = int(rng.integers(0, 400 if small else 1500))
+    Sk = int(rng.integers(0, 400 if small else 1500))
+    kind = rng.integers(0, 5)
+    if kind == 0:      # arbitrary intervals, also far outside [0, Sq)
+        b = rng.integers(-100, Sq + 100, size=(B, Hm, Sk, 4))
+    elif kind == 1:    # int32 extremes mixed in
+        b = rng.integers(-2 ** 31, 2 ** 31 - 1, size=(B, Hm, Sk, 4), dtype=np.int64)
+        b = np.where(rng.random(b.shape) < 0.5, rng.integers(0, max(Sq, 1), size=b.shape), b)
+    elif kind == 2:    # causal documents (Sq = Sk)
+        Sk = Sq
+        cuts = M.composition(rng, Sq, int(rng.integers(1, 6))) if Sq > 6 else [Sq] if Sq else []
+        b = np.broadcast_to(M.causal_document_bounds(list(cuts)) if Sq else np.zeros((0, 4)), (B, Hm, Sk, 4))
+    elif kind == 3:    # sliding windows
+        Sk = Sq
+        b = np.broadcast_to(M.sliding_window_bounds(Sq, int(rng.integers(1, 300))) if Sq else np.zeros((0, 4)),
+                            (B, Hm, Sk, 4))
+    else:              # block-aligned intervals (full and skipped tiles)
+        lo = rng.integers(0, 12, size=(B, Hm, Sk, 2)) * 128
+        b = np.concatenate([lo, lo + rng.integers(0, 4, size=(B, Hm, Sk, 2)) * 128], axis=-1)[..., [0, 2, 1, 3]]
+    b = np.ascontiguousarray(b, dtype=np.int64).astype(np.int32)
+    return M.custom(None, B=B, H=H, Sq=Sq, D=64, seed=0, per_head_bounds=b)
+
+
+def test_tile_pass_fuzz():
+    import torch
+    from column_sparse_masked_amd.api import MaskedAttention, to_device_bounds
+    rng = np.random.default_rng(2024)
+    n = 300
+    for i in range(n):
+        w = _random_problem(rng)
+        att = MaskedAttention.for_workload(w)
+        att.buf.tileinfo.fill_(0xA5)          # garbage from a previous user
+        att.tile_bounds(to_device_bounds(w.bounds))
+        torch.cuda.synchronize()
+        try:
+            check_tileinfo(w, att.read_tileinfo())
+        except AssertionError as e:
+            raise AssertionError(f"problem {i}: B={w.B} H={w.H} Hm={w.Hm} Sq={w.Sq} Sk={w.Sk}: {e}") from e
+        if i % 50 == 0:
+            say(f"[fuzz] {i} problems bit-exact (last: B={w.B} H={w.H} Hm={w.Hm} Sq={w.Sq} Sk={w.Sk})")
+    say(f"[fuzz] {n} problems bit-exact")

@@ -235,6 +235,54 @@ def test_column_gradients_match_sdpa(family):
     np.testing.assert_allclose(dv, full[4][cols], atol=1e-12)
 
 
+def _random_chunks(rng, S, n):
+    """n disjoint chunks of [0, S) in increasing order (lengths may be 0)."""
+    cuts = np.sort(rng.integers(0, S + 1, size=2 * n))
+    return cuts[0::2].tolist(), (cuts[1::2] - cuts[0::2]).tolist()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_localize_bounds_is_gather_of_global_rows(seed):
+    """Brute force: with the localised bounds, the dense mask of the rank's
+    local rows equals the global dense mask gathered at the rank's global
+    rows, for random bounds (including values far outside [0, S)) and random
+    chunk sets."""
+    rng = np.random.default_rng(seed)
+    S = int(rng.integers(1, 300))
+    gb = rng.integers(-40, S + 40, size=(S + 7, 4))
+    gb[::13] = [-2 ** 31, 2 ** 31 - 1, 0, 0]
+    for n in (1, 2, 3, 5):
+        starts, lens = _random_chunks(rng, S, n)
+        rows = np.concatenate([np.arange(s, s + l) for s, l in zip(starts, lens)] + [np.zeros(0, int)])
+        lb = O.localize_bounds(gb, starts, lens)
+        assert lb.shape == gb.shape
+        assert np.array_equal(O.dense_mask(lb, np.arange(rows.size)), O.dense_mask(gb, rows))
+        assert lb.min() >= 0 and lb.max() <= rows.size
+
+
+def test_localize_bounds_by_hand():
+    """Rows 0..15 in 4 chunks of 4; the rank holds chunks 1 and 2 (global
+    rows 4..11, local rows 0..7).  Bound 0 -> 0, 5 -> 1 (row 4 is below 5),
+    8 -> 4, 10 -> 6, 12 and 100 -> 8, -3 -> 0."""
+    lb = O.localize_bounds(np.array([[0, 5, 8, 10], [12, 100, -3, 4]]), [4, 8], [4, 4])
+    assert lb.tolist() == [[0, 1, 4, 6], [8, 8, 0, 0]]
+
+
+def test_localize_bounds_matches_clip_shift_max():
+    """The paper summary's clip-shift-max on the boundary vectors (the
+    maximum over chunks starting at or before g of the chunk's local offset
+    plus g clipped into the chunk) equals the oracle's count, written out
+    here as a closed form over all int32-range values."""
+    rng = np.random.default_rng(3)
+    starts, lens = [100, 350, 900], [200, 0, 64]
+    g = np.concatenate([rng.integers(-2 ** 31, 2 ** 31 - 1, size=500), np.arange(-5, 1200)])
+    offs = np.cumsum([0] + lens[:-1])
+    csm = np.zeros(g.shape, np.int64)
+    for s, l, o in zip(starts, lens, offs):
+        csm = np.where(g >= s, np.maximum(csm, o + np.clip(g - s, 0, l)), csm)
+    assert np.array_equal(O.localize_bounds(g, starts, lens), csm)
+
+
 # --------------------------------------------------------------------------- #
 # tile classification                                                         #
 # --------------------------------------------------------------------------- #
