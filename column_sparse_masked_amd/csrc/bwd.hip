@@ -301,6 +301,12 @@ __device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, const uint32_t (&h
   return x;
 }
 
+// Cache policy of the tile-cache stores: non-temporal (the tiles are read
+// back only by the next kernel, so they should not displace the Q and dO
+// rows this kernel reuses from the caches; measured 1.5% faster on the
+// kernel at the 128K workload, where the cache is 21 GiB).
+constexpr int kStoreNonTemporal = 2;
+
 // This wave's scale * dS of one chunk into the item's tile of the cache.  A
 // tile is stored as the waves hold it: for chunk c2 (two per tile), wave
 // (g, m) and register pair rr, a block of 512 bytes in which lane l (key
@@ -320,7 +326,7 @@ __device__ __forceinline__ void store_ds_tile(BufRsrc r, const bf16x8 (&dsb)[2],
     u32x2 x;
     x[0] = (unsigned)((rr & 1) ? wv[2] : wv[0]);
     x[1] = (unsigned)((rr & 1) ? wv[3] : wv[1]);
-    __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)(lane_off + 512 * rr), soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)(lane_off + 512 * rr), soff, kStoreNonTemporal);
   }
 }
 
