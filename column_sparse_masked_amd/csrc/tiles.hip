@@ -68,21 +68,6 @@ __device__ int block_exclusive_scan(int x, int* scratch, int* total) {
   return res;
 }
 
-// Counting sort of n items by tile count, descending.  Item it = bh*nBlk+blk
-// has count cnt[(b*Hm + hm)*nBlk + blk].  Order inside a count is arbitrary.
-// Sum over the workgroup of one 64-bit value per thread (every thread gets it).
-__device__ long block_sum(long x, long* scratch) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  if (lane == 0) scratch[wave] = x;
-  __syncthreads();
-  long total = 0;
-  for (int w = 0; w < kQueueThreads / 64; ++w) total += scratch[w];
-  __syncthreads();
-  return total;
-}
-
 // Which forward items to split (split != nullptr: the forward queue).  The
 // forward is a persistent grid of fwd_slots workgroups taking items longest
 // first; when few items share a workgroup, the longest ones set the end of
@@ -94,7 +79,6 @@ __device__ long block_sum(long x, long* scratch) {
 struct SplitRule {
   int fwd_slots, split_cap;
   uint32_t* out;
-  long* scratch;   // kQueueThreads / 64 longs
 };
 
 
@@ -116,95 +100,183 @@ __device__ __forceinline__ int wave_bucket_add(int* hist, int bucket, bool activ
   return active ? atomicAdd(&hist[bucket], 1) : 0;
 }
 
-__device__ void sort_items(const int* __restrict__ cnt, uint32_t* __restrict__ queue, int B,
-                           int H, int Hm, int nBlk, int* hist, int* scratch, const SplitRule* split) {
-  const int t = threadIdx.x;
-  const long n = (long)B * H * nBlk;
-  for (int i = t; i < kBuckets; i += kQueueThreads) hist[i] = 0;
+// Reductions over one part of the workgroup: NT threads (whole waves), tp
+// the thread's index within its part, scratch NT / 64 values of the part.
+// Their barriers are workgroup-wide, so every part calls them together.
+template <int NT>
+__device__ int part_exclusive_scan(int x, int tp, int* scratch, int* total) {
+  const int lane = tp & 63, wave = tp >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) scratch[wave] = incl;
   __syncthreads();
-  for (long i0 = 0; i0 < n; i0 += kQueueThreads) {
-    const long it = i0 + t;
-    int c = 0;
-    if (it < n) {
-      const long bh = it / nBlk;
-      const int blk = (int)(it % nBlk);
-      const int b = (int)(bh / H), h = (int)(bh % H);
-      c = cnt[((long)b * Hm + (Hm == 1 ? 0 : h)) * nBlk + blk];
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int v = scratch[w];
+    base += w < wave ? v : 0;
+    tot += v;
+  }
+  *total = tot;
+  __syncthreads();
+  return base + incl - x;
+}
+
+template <int NT>
+__device__ long part_sum(long x, int tp, long* scratch) {
+  const int lane = tp & 63, wave = tp >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  if (lane == 0) scratch[wave] = x;
+  __syncthreads();
+  long total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) total += scratch[w];
+  __syncthreads();
+  return total;
+}
+
+// The queues and tile slots are built over entries rather than items: entry
+// e = (b*Hm + hm)*nBlk + blk is one block of one mask head, with count
+// cnt[e], and stands for the reps = H / Hm items (b*H + h)*nBlk + blk of the
+// heads h that share that mask head (all H heads when Hm == 1, else h = hm),
+// which all have its count.  Its item r (0 <= r < reps):
+__device__ __forceinline__ uint32_t entry_item(uint32_t e, uint32_t r, uint32_t H, uint32_t Hm, uint32_t nBlk) {
+  const uint32_t bhm = e / nBlk, blk = e - bhm * nBlk;
+  const uint32_t b = bhm / Hm, hm = bhm - b * Hm;
+  return (b * H + (Hm == 1 ? r : hm)) * nBlk + blk;
+}
+
+// Entries per thread and pass whose counts are loaded together: the loads of
+// one pass are then in flight at once instead of one after the other.
+constexpr int kUnroll = 8;
+
+// Counting sort of the B*H*nBlk items by tile count, descending, by one part
+// of the workgroup (NT threads; tp the index within the part).  The m =
+// B*Hm*nBlk entries are sorted, and the reps items of each are written next
+// to each other.  Counts are at most max_cnt (the number of blocks of the
+// other axis); only min(kBuckets, max_cnt + 1) buckets are used, and larger
+// counts share the top one.  Every entry lands in a bucket that was cleared,
+// so the positions written are a permutation of 0 .. B*H*nBlk - 1 whatever
+// the counts hold.  Order inside a count is arbitrary.  The control flow,
+// and so the sequence of barriers, is the same for every part whatever its
+// data, so two parts can sort two queues side by side.
+template <int NT>
+__device__ void sort_items(int tp, const int* __restrict__ cnt, uint32_t* __restrict__ queue, int B, int H,
+                           int Hm, int nBlk, int max_cnt, int* hist, int* scratch, long* lscratch,
+                           const SplitRule* split) {
+  const uint32_t m = nBlk > 0 ? (uint32_t)B * (uint32_t)Hm * (uint32_t)nBlk : 0u;
+  const uint32_t reps = Hm == 1 ? (uint32_t)H : 1u;
+  const int nb = min(kBuckets, max(max_cnt, 0) + 1);
+  for (int i = tp; i < nb; i += NT) hist[i] = 0;
+  __syncthreads();
+  // the counts of kUnroll entries per thread, loaded together, clamped to a bucket
+  auto load_counts = [&](uint32_t e0, int (&c)[kUnroll]) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t e = e0 + (uint32_t)(u * NT + tp);
+      c[u] = e < m ? cnt[e] : 0;
     }
-    wave_bucket_add(hist, min(c, kBuckets - 1), it < n);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) c[u] = min(max(c[u], 0), nb - 1);
+  };
+  for (uint32_t e0 = 0; e0 < m; e0 += NT * kUnroll) {
+    int c[kUnroll];
+    load_counts(e0, c);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) wave_bucket_add(hist, c[u], e0 + (uint32_t)(u * NT + tp) < m);
   }
   __syncthreads();
-  if (split) {
+  {
+    // Which forward items to split, counted in items (the barriers run in
+    // every part).
     long tiles = 0;
-    for (int i = t; i < kBuckets - 1; i += kQueueThreads) tiles += (long)i * hist[i];
-    const long total = block_sum(tiles, split->scratch);
-    const long slots = max(split->fwd_slots, 1);
+    for (int i = tp; i < min(nb, kBuckets - 1); i += NT) tiles += (long)i * hist[i];
+    const long total = part_sum<NT>(tiles, tp, lscratch) * (long)reps;
+    const long slots = split ? max(split->fwd_slots, 1) : 1;
     const long thr = max(16L, (total + 2 * slots - 1) / (2 * slots));
     long above = 0;
-    for (int i = t; i < kBuckets - 1; i += kQueueThreads) above += i > thr ? hist[i] : 0;
-    above = block_sum(above, split->scratch);
-    if (t == 0)
-      *split->out = (hist[kBuckets - 1] > 0 || thr >= kBuckets - 1)
-                        ? 0u
-                        : (uint32_t)min(above, (long)max(split->split_cap, 0));
+    for (int i = tp; i < min(nb, kBuckets - 1); i += NT) above += i > thr ? hist[i] : 0;
+    above = part_sum<NT>(above, tp, lscratch) * (long)reps;
+    const bool top_used = nb == kBuckets && hist[kBuckets - 1] > 0;
+    if (split && tp == 0)
+      *split->out = (top_used || thr >= kBuckets - 1) ? 0u : (uint32_t)min(above, (long)max(split->split_cap, 0));
   }
-  // thread t owns buckets kBuckets-1-4t ... kBuckets-4-4t (descending order)
-  constexpr int per = kBuckets / kQueueThreads;
-  int local[per];
+  // thread tp owns buckets nb-1-per*tp ... nb-per*(tp+1) (descending order)
+  const int per = (nb + NT - 1) / NT;
   int sum = 0;
-#pragma unroll
   for (int u = 0; u < per; ++u) {
-    local[u] = hist[kBuckets - 1 - (per * t + u)];
-    sum += local[u];
+    const int bk = nb - 1 - (per * tp + u);
+    sum += bk >= 0 ? hist[bk] : 0;
   }
   int total;
-  int run = block_exclusive_scan(sum, scratch, &total);
-#pragma unroll
+  int run = part_exclusive_scan<NT>(sum, tp, scratch, &total);
   for (int u = 0; u < per; ++u) {
-    hist[kBuckets - 1 - (per * t + u)] = run;
-    run += local[u];
+    const int bk = nb - 1 - (per * tp + u);
+    if (bk >= 0) {
+      const int c = hist[bk];
+      hist[bk] = run;
+      run += c;
+    }
   }
   __syncthreads();
-  for (long i0 = 0; i0 < n; i0 += kQueueThreads) {
-    const long it = i0 + t;
-    int c = 0;
-    if (it < n) {
-      const long bh = it / nBlk;
-      const int blk = (int)(it % nBlk);
-      const int b = (int)(bh / H), h = (int)(bh % H);
-      c = cnt[((long)b * Hm + (Hm == 1 ? 0 : h)) * nBlk + blk];
+  for (uint32_t e0 = 0; e0 < m; e0 += NT * kUnroll) {
+    int c[kUnroll];
+    load_counts(e0, c);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t e = e0 + (uint32_t)(u * NT + tp);
+      const int pos = wave_bucket_add(hist, c[u], e < m);
+      if (e < m)
+        for (uint32_t r = 0; r < reps; ++r)
+          queue[(uint32_t)pos * reps + r] = entry_item(e, r, (uint32_t)H, (uint32_t)Hm, (uint32_t)nBlk);
     }
-    const int pos = wave_bucket_add(hist, min(c, kBuckets - 1), it < n);
-    if (it < n) queue[pos] = (uint32_t)it;
   }
   __syncthreads();
 }
 
-// First tile slot of every backward item it = (b * H + h) * nK + kb: the
-// exclusive prefix sum of the items' tile counts in item order, so that the
-// tiles of one item (its list of query blocks, in list order) are
-// consecutive slots.  The total goes to counters[kCtrTiles]; sums beyond
-// 2^32 - 1 saturate there (no cache is that large).
+// First tile slot of every backward item.  The slots go to the entries in
+// increasing order, and within an entry to its reps items one after the
+// other: with E(e) the sum of the counts of the entries before e, item r of
+// entry e starts at reps * E(e) + r * cnt[e].  The tiles of one item (its
+// list of query blocks, in list order) are then consecutive slots.  The
+// total goes to counters[kCtrTiles]; values beyond 2^32 - 1 saturate (no
+// cache is that large).  Thread t takes kUnroll consecutive entries of each
+// chunk of kQueueThreads * kUnroll.
 __device__ void tile_slots(const int* __restrict__ cnt, uint32_t* __restrict__ base, int B, int H,
                            int Hm, int nBlk, uint32_t* total_out, int* scratch) {
   const int t = threadIdx.x;
-  const long n = (long)B * H * nBlk;
+  const uint32_t m = nBlk > 0 ? (uint32_t)B * (uint32_t)Hm * (uint32_t)nBlk : 0u;
+  const unsigned long long reps = Hm == 1 ? (unsigned long long)H : 1ull;
   unsigned long long run = 0;   // the same in every thread
-  for (long i0 = 0; i0 < n; i0 += kQueueThreads) {
-    const long it = i0 + t;
-    int c = 0;
-    if (it < n) {
-      const long bh = it / nBlk;
-      const int blk = (int)(it % nBlk);
-      const int b = (int)(bh / H), h = (int)(bh % H);
-      c = cnt[((long)b * Hm + (Hm == 1 ? 0 : h)) * nBlk + blk];
-    }
+  for (uint32_t e0 = 0; e0 < m; e0 += kQueueThreads * kUnroll) {
+    const uint32_t first = e0 + (uint32_t)(t * kUnroll);
+    int c[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) c[u] = first + u < m ? max(cnt[first + u], 0) : 0;
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) mine += c[u];
     int chunk_total;
-    const int excl = block_exclusive_scan(c, scratch, &chunk_total);
-    if (it < n) base[it] = (uint32_t)min(run + (unsigned long long)excl, 0xFFFFFFFFull);
+    int excl = block_exclusive_scan(mine, scratch, &chunk_total);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t e = first + u;
+      if (e < m) {
+        const unsigned long long s0 = reps * (run + (unsigned long long)excl);
+        for (uint32_t r = 0; r < (uint32_t)reps; ++r)
+          base[entry_item(e, r, (uint32_t)H, (uint32_t)Hm, (uint32_t)nBlk)] =
+              (uint32_t)min(s0 + (unsigned long long)r * (unsigned long long)c[u], 0xFFFFFFFFull);
+      }
+      excl += c[u];
+    }
     run += (unsigned long long)chunk_total;
   }
-  if (t == 0) *total_out = (uint32_t)min(run, 0xFFFFFFFFull);
+  if (t == 0) *total_out = (uint32_t)min(reps * run, 0xFFFFFFFFull);
 }
 
 // Compaction of one list: NT threads each hold one candidate entry (keep);
@@ -322,7 +394,7 @@ __global__ __launch_bounds__(kQueueThreads) void row_kernel(
     const int* __restrict__ cnt_k, uint16_t* __restrict__ list_q, uint32_t* __restrict__ fwd_q,
     uint32_t* __restrict__ bwd_q, uint32_t* __restrict__ colbase, uint32_t* __restrict__ counters, int B, int H,
     int Hm, int Sq, int nQ, int nK, int fwd_slots, int split_cap) {
-  __shared__ int hist[kBuckets];
+  __shared__ int hist[2][kBuckets];
   __shared__ int scratch[kQueueThreads / 64 + 1];
   __shared__ long lscratch[kQueueThreads / 64];
   __shared__ uint32_t last, nsplit, ntiles;
@@ -367,9 +439,17 @@ __global__ __launch_bounds__(kQueueThreads) void row_kernel(
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (t == 0) nsplit = 0;
   __syncthreads();
-  const SplitRule rule{fwd_slots, split_cap, &nsplit, lscratch};
-  if (nQ > 0) sort_items(cnt_q, fwd_q, B, H, Hm, nQ, hist, scratch, split_cap > 0 ? &rule : nullptr);
-  if (nK > 0) sort_items(cnt_k, bwd_q, B, H, Hm, nK, hist, scratch, nullptr);
+  {
+    // the two halves of the workgroup sort the two queues side by side
+    constexpr int kHalf = kQueueThreads / 2;
+    const int part = t / kHalf, tp = t % kHalf;
+    const SplitRule rule{fwd_slots, split_cap, &nsplit};
+    int* sc = scratch + part * (kHalf / 64);
+    long* lsc = lscratch + part * (kHalf / 64);
+    // (a forward item's count is at most nK, a backward item's at most nQ)
+    sort_items<kHalf>(tp, part == 0 ? cnt_q : cnt_k, part == 0 ? fwd_q : bwd_q, B, H, Hm, part == 0 ? nQ : nK,
+                      part == 0 ? nK : nQ, hist[part], sc, lsc, part == 0 && split_cap > 0 ? &rule : nullptr);
+  }
   tile_slots(cnt_k, colbase, B, H, Hm, nK, &ntiles, scratch);
   __syncthreads();
   if (t == 0) {

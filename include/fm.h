@@ -93,10 +93,14 @@ typedef struct {
  *   cpos      uint16[B][Hm][nK][nQ] for each non-skipped tile (qb, kb), the
  *             position of qb in list_k of kb (other entries are not written)
  *   colbase   uint32[B*H*nK]       first tile slot of each backward item
- *             (b*H+h)*nK+kb: the prefix sum of the items' tile counts in item
- *             order, so that the tiles of item i, in its list order, take
- *             slots colbase[i] .. colbase[i] + cnt - 1 of the backward's tile
- *             cache; counters[9] holds the total (saturating at 2^32 - 1) */
+ *             (b*H+h)*nK+kb.  Slots go to the entries e = (b*Hm+hm)*nK+kb in
+ *             increasing order and, within an entry, to the R = H/Hm heads
+ *             that share it one after the other: head r of entry e (r = h
+ *             when Hm == 1, else 0) starts at R*E(e) + r*cnt_k[e], E(e) the
+ *             sum of cnt_k over the entries before e.  The tiles of item i,
+ *             in its list order, take slots colbase[i] .. colbase[i] + cnt - 1
+ *             of the backward's tile cache; counters[9] holds the total
+ *             (values saturate at 2^32 - 1) */
 typedef struct {
   int32_t block_q, block_k, n_qblocks, n_kblocks;
   size_t counters, kbsum, cls, cnt_q, cnt_k, list_q, list_k, fwd_queue, bwd_queue, fwd_partials;

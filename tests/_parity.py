@@ -124,18 +124,32 @@ def check_tileinfo(w, ti):
     assert c[0] == B * H * nQ and c[1] == B * H * nK and c[2] == 0 and c[3] == 0
     assert c[8] == expected_split_count(cq, H, Hm), "number of split forward items differs"
     # the backward's tile slots: each listed tile's position in its key
-    # block's list, and each backward item's first slot (the running total
-    # of the items' tile counts in item order)
+    # block's list, and each backward item's first slot.  Slots go to the
+    # (b, mask head, key block) entries in order, and within an entry to the
+    # heads sharing it one after the other: item h of entry e starts at
+    # reps * (tiles of the entries before e) + h * cnt[e], reps = H / Hm.
     for b in range(B):
         for hm in range(Hm):
             for kb in range(nK):
                 qbs = np.nonzero(cls[b, hm, :, kb])[0]
                 assert np.array_equal(ti["cpos"][b, hm, kb, qbs], np.arange(qbs.size)), ("cpos", b, hm, kb)
-    per_item = np.repeat(ck, H // Hm, axis=1) if Hm == 1 else ck      # [B][H][nK]
-    flat = per_item.reshape(-1).astype(np.int64)
-    want = np.concatenate([[0], np.cumsum(flat)[:-1]]) if flat.size else flat
-    assert np.array_equal(ti["colbase"].astype(np.int64), want), "colbase differs"
-    assert c[9] == int(flat.sum()), "tile count differs"
+    reps = H // Hm
+    ent = ck.reshape(-1).astype(np.int64)                             # entries (b, hm, kb)
+    before = np.concatenate([[0], np.cumsum(ent)[:-1]]) if ent.size else ent
+    want = np.zeros((B, H, nK), np.int64)
+    for h in range(H):
+        r, hm = (h, 0) if Hm == 1 else (0, h)
+        want[:, h, :] = (reps * before + r * ent).reshape(B, Hm, nK)[:, hm, :]
+    want = np.minimum(want, 2 ** 32 - 1)
+    # each item's slots are its own: the ranges [start, start + count) tile
+    # 0 .. total - 1 without gaps or overlaps
+    per_item = np.repeat(ck, reps, axis=1) if Hm == 1 else ck        # [B][H][nK]
+    counts = per_item.reshape(-1).astype(np.int64)
+    order = np.lexsort((counts, want.reshape(-1)))      # by start, empty items first
+    starts, counts = want.reshape(-1)[order], counts[order]
+    assert np.array_equal(starts[1:], (starts + counts)[:-1]) and (starts.size == 0 or starts[0] == 0)
+    assert np.array_equal(ti["colbase"].astype(np.int64), want.reshape(-1)), "colbase differs"
+    assert c[9] == int(per_item.sum()), "tile count differs"
     assert c[10] == 0
 
 
