@@ -68,17 +68,17 @@ __device__ int block_exclusive_scan(int x, int* scratch, int* total) {
   return res;
 }
 
-// Which forward items to split (split != nullptr: the forward queue).  The
-// forward is a persistent grid of fwd_slots workgroups taking items longest
-// first; when few items share a workgroup, the longest ones set the end of
-// the kernel.  Items with more than max(16, ceil(total / (2 fwd_slots)))
+// Which forward items to split (on: the forward queue, splitting allowed).
+// The forward is a persistent grid of fwd_slots workgroups taking items
+// longest first; when few items share a workgroup, the longest ones set the
+// end of the kernel.  Items with more than max(16, ceil(total / (2 fwd_slots)))
 // tiles (half the mean load of a workgroup) are split in two halves of their
 // key blocks, at most split_cap of them; they are the first entries of the
 // sorted queue.  Counted from the histogram of tile counts, which is exact
 // below the top bucket; with any item in the top bucket nothing is split.
 struct SplitRule {
+  bool on;
   int fwd_slots, split_cap;
-  uint32_t* out;
 };
 
 
@@ -151,9 +151,39 @@ __device__ __forceinline__ uint32_t entry_item(uint32_t e, uint32_t r, uint32_t 
   return (b * H + (Hm == 1 ? r : hm)) * nBlk + blk;
 }
 
+// x / d for x, d < 2^31, d > 0, given inv = 1.0 / d: the double product is
+// within one of the quotient (its error is below 2^-20), and one step
+// corrects it (q d <= x + d cannot wrap).
+__device__ __forceinline__ uint32_t udiv(uint32_t x, uint32_t d, double inv) {
+  uint32_t q = (uint32_t)((double)x * inv);
+  const uint32_t qd = q * d;
+  if (qd > x) --q;
+  else if (x - qd >= d) ++q;
+  return q;
+}
+
 // Entries per thread and pass whose counts are loaded together: the loads of
 // one pass are then in flight at once instead of one after the other.
 constexpr int kUnroll = 8;
+
+// Where the sort and the slot scan read the entries' tile counts: global
+// memory, or a copy in LDS.  Every global access of the last workgroup is a
+// round trip to memory shared by all dies (the counts were written by other
+// workgroups' atomics), so when both count arrays fit, the workgroup loads
+// them into LDS in one sweep and reads them there.
+struct GlobalCounts {
+  const int* __restrict__ p;
+  __device__ __forceinline__ int operator()(uint32_t e) const { return p[e]; }
+};
+struct LdsCounts {
+  const uint16_t* p;
+  __device__ __forceinline__ int operator()(uint32_t e) const { return (int)p[e]; }
+};
+constexpr int kCountCache = 4096;   // entries per count array held in LDS
+// (sorted entries are held as 16-bit numbers, the running sums of the slot
+// scan in one histogram, and the scan takes all entries in one sweep)
+static_assert(kCountCache <= 65536 && kCountCache <= kBuckets && kCountCache <= kQueueThreads * kUnroll,
+              "count cache size");
 
 // Counting sort of the B*H*nBlk items by tile count, descending, by one part
 // of the workgroup (NT threads; tp the index within the part).  The m =
@@ -165,24 +195,24 @@ constexpr int kUnroll = 8;
 // the counts hold.  Order inside a count is arbitrary.  The control flow,
 // and so the sequence of barriers, is the same for every part whatever its
 // data, so two parts can sort two queues side by side.
-template <int NT>
-__device__ void sort_items(int tp, const int* __restrict__ cnt, uint32_t* __restrict__ queue, int B, int H,
+template <int NT, class Counts>
+__device__ void sort_items(int tp, Counts cnt, uint32_t* __restrict__ queue, int B, int H,
                            int Hm, int nBlk, int max_cnt, int* hist, int* scratch, long* lscratch,
-                           const SplitRule* split) {
+                           SplitRule split, uint32_t* split_out, uint16_t* sorted) {
   const uint32_t m = nBlk > 0 ? (uint32_t)B * (uint32_t)Hm * (uint32_t)nBlk : 0u;
   const uint32_t reps = Hm == 1 ? (uint32_t)H : 1u;
   const int nb = min(kBuckets, max(max_cnt, 0) + 1);
   for (int i = tp; i < nb; i += NT) hist[i] = 0;
   __syncthreads();
-  // the counts of kUnroll entries per thread, loaded together, clamped to a bucket
+  // the counts of kUnroll entries per thread (m > 0), clamped to a bucket.
+  // Every lane loads (from a valid entry) and the result is dropped past
+  // the end: no branch around a load, so the loads are in flight together.
   auto load_counts = [&](uint32_t e0, int (&c)[kUnroll]) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t e = e0 + (uint32_t)(u * NT + tp);
-      c[u] = e < m ? cnt[e] : 0;
-    }
+    for (int u = 0; u < kUnroll; ++u) c[u] = cnt(min(e0 + (uint32_t)(u * NT + tp), m - 1));
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) c[u] = min(max(c[u], 0), nb - 1);
+    for (int u = 0; u < kUnroll; ++u)
+      c[u] = e0 + (uint32_t)(u * NT + tp) < m ? min(max(c[u], 0), nb - 1) : 0;
   };
   for (uint32_t e0 = 0; e0 < m; e0 += NT * kUnroll) {
     int c[kUnroll];
@@ -197,14 +227,14 @@ __device__ void sort_items(int tp, const int* __restrict__ cnt, uint32_t* __rest
     long tiles = 0;
     for (int i = tp; i < min(nb, kBuckets - 1); i += NT) tiles += (long)i * hist[i];
     const long total = part_sum<NT>(tiles, tp, lscratch) * (long)reps;
-    const long slots = split ? max(split->fwd_slots, 1) : 1;
+    const long slots = split.on ? max(split.fwd_slots, 1) : 1;
     const long thr = max(16L, (total + 2 * slots - 1) / (2 * slots));
     long above = 0;
     for (int i = tp; i < min(nb, kBuckets - 1); i += NT) above += i > thr ? hist[i] : 0;
     above = part_sum<NT>(above, tp, lscratch) * (long)reps;
     const bool top_used = nb == kBuckets && hist[kBuckets - 1] > 0;
-    if (split && tp == 0)
-      *split->out = (top_used || thr >= kBuckets - 1) ? 0u : (uint32_t)min(above, (long)max(split->split_cap, 0));
+    if (split.on && tp == 0)
+      *split_out = (top_used || thr >= kBuckets - 1) ? 0u : (uint32_t)min(above, (long)max(split.split_cap, 0));
   }
   // thread tp owns buckets nb-1-per*tp ... nb-per*(tp+1) (descending order)
   const int per = (nb + NT - 1) / NT;
@@ -231,12 +261,31 @@ __device__ void sort_items(int tp, const int* __restrict__ cnt, uint32_t* __rest
     for (int u = 0; u < kUnroll; ++u) {
       const uint32_t e = e0 + (uint32_t)(u * NT + tp);
       const int pos = wave_bucket_add(hist, c[u], e < m);
-      if (e < m)
-        for (uint32_t r = 0; r < reps; ++r)
-          queue[(uint32_t)pos * reps + r] = entry_item(e, r, (uint32_t)H, (uint32_t)Hm, (uint32_t)nBlk);
+      if (e < m) {
+        if (sorted) {
+          sorted[pos] = (uint16_t)e;
+        } else {
+          for (uint32_t r = 0; r < reps; ++r)
+            queue[(uint32_t)pos * reps + r] = entry_item(e, r, (uint32_t)H, (uint32_t)Hm, (uint32_t)nBlk);
+        }
+      }
     }
   }
   __syncthreads();
+  if (sorted) {
+    // the queue in order, position p holding item p % reps of the entry
+    // sorted to p / reps: consecutive threads store consecutive words
+    const double inv_reps = 1.0 / (double)reps, inv_blk = 1.0 / (double)nBlk;
+    const uint32_t n = m * reps;
+    for (uint32_t p = (uint32_t)tp; p < n; p += NT) {
+      const uint32_t k = udiv(p, reps, inv_reps), r = p - k * reps;
+      const uint32_t e = sorted[k];
+      // item r of entry e: (b*H + h)*nBlk + blk with e = (b*Hm + hm)*nBlk + blk
+      const uint32_t it = Hm == 1 ? e + udiv(e, (uint32_t)nBlk, inv_blk) * (uint32_t)(H - 1) * (uint32_t)nBlk + r * (uint32_t)nBlk
+                                  : e;
+      queue[p] = it;
+    }
+  }
 }
 
 // First tile slot of every backward item.  The slots go to the entries in
@@ -247,7 +296,8 @@ __device__ void sort_items(int tp, const int* __restrict__ cnt, uint32_t* __rest
 // total goes to counters[kCtrTiles]; values beyond 2^32 - 1 saturate (no
 // cache is that large).  Thread t takes kUnroll consecutive entries of each
 // chunk of kQueueThreads * kUnroll.
-__device__ void tile_slots(const int* __restrict__ cnt, uint32_t* __restrict__ base, int B, int H,
+template <class Counts>
+__device__ void tile_slots(Counts cnt, uint32_t* __restrict__ base, int B, int H,
                            int Hm, int nBlk, uint32_t* total_out, int* scratch) {
   const int t = threadIdx.x;
   const uint32_t m = nBlk > 0 ? (uint32_t)B * (uint32_t)Hm * (uint32_t)nBlk : 0u;
@@ -257,7 +307,9 @@ __device__ void tile_slots(const int* __restrict__ cnt, uint32_t* __restrict__ b
     const uint32_t first = e0 + (uint32_t)(t * kUnroll);
     int c[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) c[u] = first + u < m ? max(cnt[first + u], 0) : 0;
+    for (int u = 0; u < kUnroll; ++u) c[u] = cnt(min(first + u, m - 1));   // no branch around the loads
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) c[u] = first + u < m ? max(c[u], 0) : 0;
     int mine = 0;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) mine += c[u];
@@ -277,6 +329,42 @@ __device__ void tile_slots(const int* __restrict__ cnt, uint32_t* __restrict__ b
     run += (unsigned long long)chunk_total;
   }
   if (t == 0) *total_out = (uint32_t)min(reps * run, 0xFFFFFFFFull);
+}
+
+// tile_slots for counts in LDS (m <= kQueueThreads * kUnroll entries): the
+// entries' running sums E(e) go to LDS (ebase), and the slots are then
+// written in item order, consecutive threads storing consecutive words.
+__device__ void tile_slots_lds(const uint16_t* cnt, uint32_t* __restrict__ base, int B, int H, int Hm,
+                               int nBlk, uint32_t* total_out, int* scratch, int* ebase) {
+  const int t = threadIdx.x;
+  const uint32_t m = nBlk > 0 ? (uint32_t)B * (uint32_t)Hm * (uint32_t)nBlk : 0u;
+  const uint32_t first = (uint32_t)(t * kUnroll);
+  int c[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) c[u] = first + u < m ? (int)cnt[first + u] : 0;
+  int mine = 0;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) mine += c[u];
+  int total;
+  int excl = block_exclusive_scan(mine, scratch, &total);
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    if (first + u < m) ebase[first + u] = excl;
+    excl += c[u];
+  }
+  __syncthreads();
+  const unsigned long long reps = Hm == 1 ? (unsigned long long)H : 1ull;
+  const uint32_t n = m * (uint32_t)reps;
+  const double inv_blk = 1.0 / (double)nBlk, inv_h = 1.0 / (double)H;
+  for (uint32_t i = (uint32_t)t; i < n; i += kQueueThreads) {
+    // item i = (b*H + h)*nBlk + kb: entry (b*Hm + hm)*nBlk + kb, head r = h when Hm == 1
+    const uint32_t bh = udiv(i, (uint32_t)nBlk, inv_blk), kb = i - bh * (uint32_t)nBlk;
+    const uint32_t b = udiv(bh, (uint32_t)H, inv_h), h = bh - b * (uint32_t)H;
+    const uint32_t e = Hm == 1 ? b * (uint32_t)nBlk + kb : i;
+    const unsigned long long r = Hm == 1 ? h : 0u;
+    base[i] = (uint32_t)min(reps * (unsigned long long)ebase[e] + r * (unsigned long long)cnt[e], 0xFFFFFFFFull);
+  }
+  if (t == 0) *total_out = (uint32_t)min(reps * (unsigned long long)total, 0xFFFFFFFFull);
 }
 
 // Compaction of one list: NT threads each hold one candidate entry (keep);
@@ -395,6 +483,8 @@ __global__ __launch_bounds__(kQueueThreads) void row_kernel(
     uint32_t* __restrict__ bwd_q, uint32_t* __restrict__ colbase, uint32_t* __restrict__ counters, int B, int H,
     int Hm, int Sq, int nQ, int nK, int fwd_slots, int split_cap) {
   __shared__ int hist[2][kBuckets];
+  __shared__ uint16_t ccache[2][kCountCache];
+  __shared__ uint16_t sorted[2][kCountCache];
   __shared__ int scratch[kQueueThreads / 64 + 1];
   __shared__ long lscratch[kQueueThreads / 64];
   __shared__ uint32_t last, nsplit, ntiles;
@@ -443,14 +533,40 @@ __global__ __launch_bounds__(kQueueThreads) void row_kernel(
     // the two halves of the workgroup sort the two queues side by side
     constexpr int kHalf = kQueueThreads / 2;
     const int part = t / kHalf, tp = t % kHalf;
-    const SplitRule rule{fwd_slots, split_cap, &nsplit};
+    const SplitRule sr{part == 0 && split_cap > 0, fwd_slots, split_cap};
     int* sc = scratch + part * (kHalf / 64);
     long* lsc = lscratch + part * (kHalf / 64);
     // (a forward item's count is at most nK, a backward item's at most nQ)
-    sort_items<kHalf>(tp, part == 0 ? cnt_q : cnt_k, part == 0 ? fwd_q : bwd_q, B, H, Hm, part == 0 ? nQ : nK,
-                      part == 0 ? nK : nQ, hist[part], sc, lsc, part == 0 && split_cap > 0 ? &rule : nullptr);
+    const int nBlk = part == 0 ? nQ : nK, max_cnt = part == 0 ? nK : nQ;
+    uint32_t* queue = part == 0 ? fwd_q : bwd_q;
+    const long mq = (long)B * Hm * nQ, mk = (long)B * Hm * nK;
+    if (mq <= kCountCache && mk <= kCountCache) {   // the same in every thread
+      int cq[kCountCache / kQueueThreads], ck[kCountCache / kQueueThreads];
+      // range-checked buffer loads (zero past the end): no branch around
+      // the loads, which are then in flight together
+      const BufRsrc rq = make_rsrc(cnt_q, (uint32_t)mq * 4u), rk = make_rsrc(cnt_k, (uint32_t)mk * 4u);
+#pragma unroll
+      for (int u = 0; u < kCountCache / kQueueThreads; ++u) {
+        const uint32_t off = (uint32_t)(u * kQueueThreads + t) * 4u;
+        cq[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(rq, off, 0, 0);
+        ck[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(rk, off, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kCountCache / kQueueThreads; ++u) {
+        ccache[0][u * kQueueThreads + t] = (uint16_t)min(max(cq[u], 0), 65535);
+        ccache[1][u * kQueueThreads + t] = (uint16_t)min(max(ck[u], 0), 65535);
+      }
+      __syncthreads();
+      sort_items<kHalf>(tp, LdsCounts{ccache[part]}, queue, B, H, Hm, nBlk, max_cnt, hist[part], sc, lsc, sr,
+                        &nsplit, sorted[part]);
+      // (the histograms are free again: they hold the running sums)
+      tile_slots_lds(ccache[1], colbase, B, H, Hm, nK, &ntiles, scratch, hist[0]);
+    } else {
+      sort_items<kHalf>(tp, GlobalCounts{part == 0 ? cnt_q : cnt_k}, queue, B, H, Hm, nBlk, max_cnt, hist[part],
+                        sc, lsc, sr, &nsplit, nullptr);
+      tile_slots(GlobalCounts{cnt_k}, colbase, B, H, Hm, nK, &ntiles, scratch);
+    }
   }
-  tile_slots(cnt_k, colbase, B, H, Hm, nK, &ntiles, scratch);
   __syncthreads();
   if (t == 0) {
     counters[kCtrFwdItems] = (uint32_t)((long)B * H * nQ);

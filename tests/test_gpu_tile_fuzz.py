@@ -61,3 +61,24 @@ def test_tile_pass_fuzz():
         if i % 50 == 0:
             say(f"[fuzz] {i} problems bit-exact (last: B={w.B} H={w.H} Hm={w.Hm} Sq={w.Sq} Sk={w.Sk})")
     say(f"[fuzz] {n} problems bit-exact")
+
+
+@pytest.mark.parametrize("B,H,Hm,Sq,Sk", [(2, 24, 24, 13000, 9000),    # 4896 forward entries
+                                          (48, 2, 1, 9000, 13000),     # 4896 backward entries
+                                          (1, 40, 40, 16384, 16384)])  # 5120 of each
+def test_tile_pass_many_entries(B, H, Hm, Sq, Sk):
+    """More (batch, mask head, block) entries than the sort keeps in LDS: the
+    last workgroup reads the counts from global memory instead."""
+    import torch
+    from column_sparse_masked_amd.api import MaskedAttention, to_device_bounds
+    rng = np.random.default_rng(B * 1000 + H)
+    b = rng.integers(-50, Sq + 50, size=(B, Hm, Sk, 4))
+    w = M.custom(None, B=B, H=H, Sq=Sq, D=64, seed=0,
+                 per_head_bounds=np.ascontiguousarray(b, dtype=np.int64).astype(np.int32))
+    assert w.Sk == Sk
+    say(f"[many entries] B={B} H={H} Hm={Hm} Sq={Sq} Sk={Sk}")
+    att = MaskedAttention.for_workload(w)
+    att.buf.tileinfo.fill_(0xA5)
+    att.tile_bounds(to_device_bounds(w.bounds))
+    torch.cuda.synchronize()
+    check_tileinfo(w, att.read_tileinfo())
