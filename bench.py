@@ -271,7 +271,7 @@ def run_workload(cfg, seed, args, dev, with_fp8):
             ev["s3"].record()
 
     # The backward's workspace holds the tile cache for every non-skipped
-    # tile (dQ from the cached scale * dS); it is sized from one tile pass,
+    # tile (dQ from the cached dS / scale); it is sized from one tile pass,
     # before any timed work.
     att.tile_bounds(tb)
     cache_bytes = att.reserve_tile_cache() if not args.no_tile_cache else 0
@@ -336,7 +336,7 @@ def run_workload(cfg, seed, args, dev, with_fp8):
     # accounting: the forward (with its merge of split items) S and PV,
     # 4 D nnz; the dK/dV kernel S, dP, dV, dK, 8 D nnz.  dQ: from the tile
     # cache it is bound by reading the cached tiles, so its roofline is HBM
-    # bytes (every cached tile of scale * dS, K once, dQ written); without the
+    # bytes (every cached tile of dS / scale, K once, dQ written); without the
     # cache it recomputes S and dP and is credited with its dQ product only,
     # 2 D nnz (its hardware flops are 6 D nnz).  The dominant kernel is the
     # longest.

@@ -139,7 +139,7 @@ class MaskedAttention:
     def reserve_tile_cache(self, n_tiles=None):
         """Grow the backward workspace to hold the tile cache for n_tiles
         tiles (default: the last tile pass's count), so that the backward
-        computes dQ from cached scale * dS instead of recomputing S and dP.
+        computes dQ from cached dS / scale instead of recomputing S and dP.
         Returns the workspace size in bytes."""
         n = self.tile_count() if n_tiles is None else int(n_tiles)
         need = _lib.bwd_cache_bytes(self.p, n)

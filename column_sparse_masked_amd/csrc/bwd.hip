@@ -9,8 +9,10 @@
 //                    (the tiles the mask does not skip), 64 query rows at a
 //                    time:
 //                        S = Q K^T, P = exp(S - LSE) (interval mask on partial
-//                        tiles only), dP = dO V^T, dS = P (dP - Delta) scale,
-//                        dV += P^T dO, dK += dS^T Q;
+//                        tiles only), dP = dO V^T, dS' = P (dP - Delta),
+//                        dV += P^T dO, dK += dS'^T Q, and dK = scale dK at
+//                        the end (dS = scale dS': the scale is applied once
+//                        per output instead of once per score);
 //   attn_bwd_dq_kernel (its own file) then computes dQ query-stationary.
 // dQ is not accumulated here: fp32 atomic adds into a shared accumulator run
 // at a fraction of the rate of plain stores on this GPU, and at this kernel's
@@ -78,7 +80,7 @@ constexpr int kBwdThreads = 512;
 // is -LSE / scale to about 16 bits (zeros elsewhere), and each dO row the pair
 // for -Delta.  With a constant B operand of ones in those two columns, one
 // more k-step of S = Q K^T and dP = dO V^T yields S - LSE / scale and
-// dP - Delta, so P = exp2(scale log2(e) S') and dS = scale P dP' need no
+// dP - Delta, so P = exp2(scale log2(e) S') and dS' = P dP' need no
 // per-row value in the lanes, whose rows differ from lane to lane.
 // The LDS of a workgroup is three separate arrays (row-major staging,
 // transposed staging, P / dS exchange) rather than one structure, so that the
@@ -94,7 +96,7 @@ struct BwdSmem {
   bf16* q;      // [QC * QST]
   bf16* dout;   // [QC * QST]
   bf16* tr;     // [2 buffers][Q^T, dO^T][D * QTS], one row per head-dim column
-  // P and scale*dS of (key group g, half m) in the A-operand layout of the
+  // P and dS' of (key group g, half m) in the A-operand layout of the
   // dV / dK products: pds[g][m][0 = P, 1 = dS][t2][lane]
   bf16x8 (*pds)[2][2][2][64];
   __device__ __forceinline__ bf16* qt(int buf) const { return tr + (2 * buf) * TR; }
@@ -169,7 +171,7 @@ __device__ __forceinline__ void load_chunk(ChunkStage<D>& r, BufRsrc qb, BufRsrc
 // Row-major Q and dO (A operands of S and dP) and the row terms.
 template <int D, typename Smem>
 __device__ __forceinline__ void store_rowmajor(const ChunkStage<D>& r, const Smem& sm, int q0, int Sq,
-                                               float scale, unsigned t) {
+                                               float inv_scale, unsigned t) {
   using C = ChunkStage<D>;
   constexpr int QST = Smem::QST;
   if (C::active(t)) {
@@ -186,7 +188,7 @@ __device__ __forceinline__ void store_rowmajor(const ChunkStage<D>& r, const Sme
     float x;
     if (is_q) {
       const bool live = q0 + row < Sq && r.row_term < INFINITY;
-      x = live ? -r.row_term / scale : -INFINITY;
+      x = live ? -r.row_term * inv_scale : -INFINITY;
     } else {
       x = -r.row_term;
     }
@@ -307,7 +309,7 @@ __device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, const uint32_t (&h
 // kernel at the 128K workload, where the cache is 21 GiB).
 constexpr int kStoreNonTemporal = 2;
 
-// This wave's scale * dS of one chunk into the item's tile of the cache.  A
+// This wave's dS' = dS / scale of one chunk into the item's tile of the cache.  A
 // tile is stored as the waves hold it: for chunk c2 (two per tile), wave
 // (g, m) and register pair rr, a block of 512 bytes in which lane l (key
 // 32 g + l % 32) has 8 bytes, rows 32 m + 8 rr + 4 (l / 32) + q (q = 0..3)
@@ -357,6 +359,7 @@ void attn_bwd_kernel(const BwdArgs a) {
   constexpr int EST = D + 8;
   static_assert(2 * BK * EST <= 4 * Smem::TR, "the dK / dV tile fits the transposed staging buffers");
   const int Sq = a.Sq, Sk = a.Sk;
+  const float inv_scale = 1.0f / a.scale;
 
   const ItemQueue iq{&a.counters[kCtrBwdNext], a.queue, a.cnt_k, n_items, max_items, a.nK, a.H, a.Hm, a.nQ};
   const bool cache = tile_cache_on(a.counters, a.ds_cap);
@@ -509,13 +512,13 @@ void attn_bwd_kernel(const BwdArgs a) {
           for (int v = 0; v < 16; ++v)
             s[v] = (hidden >> (8 * (v >> 2) + (v & 3))) & 1u ? -INFINITY : s[v];
         }
-        // P = exp2(S' scale log2(e)); scale dS = scale P dP'
+        // P = exp2(S' scale log2(e)); dS' = P dP' (dS / scale)
         bf16x8 pb[2], dsb[2];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float p = fast_exp2(s[v] * a.scale_log2);
           pb[v >> 3][v & 7] = (bf16)p;
-          dsb[v >> 3][v & 7] = (bf16)((p * a.scale) * dp[v]);
+          dsb[v >> 3][v & 7] = (bf16)(p * dp[v]);
         }
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
@@ -523,7 +526,7 @@ void attn_bwd_kernel(const BwdArgs a) {
           sm.pds[g][m][1][t2][lane] = dsb[t2];
         }
         {
-          // the chunk's scale * dS into the tile cache: tile j of the item is
+          // the chunk's dS' into the tile cache: tile j of the item is
           // its j-th list entry (the walk starts at entry rot)
           int j = c / CPB + cur.rot;
           j = j < cnt ? j : j - cnt;
@@ -587,7 +590,7 @@ void attn_bwd_kernel(const BwdArgs a) {
             if (i + 2 < NP) read_b(i + 2);
             ts.row(2 * i);
             ts.row(2 * i + 1);
-            if (i == 1) store_rowmajor<D>(X, sm, q0n, Sq, a.scale, t);
+            if (i == 1) store_rowmajor<D>(X, sm, q0n, Sq, inv_scale, t);
             if (i == NP - 1) {
               load_chunk<D>(X, qbase, obase, lbase, dbase, q0l, t);
               lw3 = lword(c + 4);
@@ -604,7 +607,7 @@ void attn_bwd_kernel(const BwdArgs a) {
               dk[dd] = mfma32(as_bf16x8(qtc + off), dh[t2], dk[dd]);
             }
           store_transposed<D>(X, sm, bn, q0n, t);
-          store_rowmajor<D>(X, sm, q0n, Sq, a.scale, t);
+          store_rowmajor<D>(X, sm, q0n, Sq, inv_scale, t);
           load_chunk<D>(X, qbase, obase, lbase, dbase, q0l, t);
           lw3 = lword(c + 4);
         }
@@ -617,7 +620,7 @@ void attn_bwd_kernel(const BwdArgs a) {
       // chunk 0 (in r0) staged; chunk 1 -> r1, chunk 2 -> r0
       const int bq0 = row0(list_value(lw0), 0);
       store_transposed<D>(r0, sm, 0, bq0, t);
-      store_rowmajor<D>(r0, sm, bq0, Sq, a.scale, t);
+      store_rowmajor<D>(r0, sm, bq0, Sq, inv_scale, t);
       // K, V are in registers by now (loaded before chunk 0, which the stores
       // waited for); an explicit wait says so to the compiler, which would
       // otherwise wait for them, and with them for the loads of later chunks,
@@ -654,7 +657,7 @@ void attn_bwd_kernel(const BwdArgs a) {
           bf16x4 xk, xv;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            xk[q] = (bf16)dk[dd][4 * r + q];
+            xk[q] = (bf16)(dk[dd][4 * r + q] * a.scale);
             xv[q] = (bf16)dv[dd][4 * r + q];
           }
           *reinterpret_cast<bf16x4*>(&tile[krow * EST + col]) = xk;

@@ -12,9 +12,10 @@
 // block:
 //     S^T = K Q^T,  dP^T = V dO^T           (A operands: K, V rows from LDS)
 //     P = exp(S - LSE) (interval mask on partial tiles),
-//     dS^T = P (dP - Delta) scale,
-//     dQ^T += K^T dS^T                       (A operand: K^T rows from LDS,
-//                                             B operand: the dS^T accumulator)
+//     dS'^T = P (dP - Delta)                 (dS / scale),
+//     dQ^T += K^T dS'^T                      (A operand: K^T rows from LDS,
+//                                             B operand: the dS'^T accumulator)
+// and dQ = scale dQ' when it is written.
 // S^T and dP^T are recomputed here rather than shared with the key-stationary
 // kernel: exchanging dS between the two would cost more memory traffic than
 // the two extra products.  At the end the two key halves' dQ^T are summed in
@@ -147,7 +148,7 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
   constexpr int KST = DqSmem<D>::KST, KTS = DqSmem<D>::KTS;
   __shared__ DqSmem<D> sm;
   // with the tile cache on, the cached kernel computes dQ from the stored
-  // scale * dS instead (the queue counters are left untouched)
+  // dS' instead (the queue counters are left untouched)
   if (tile_cache_on(a.counters, a.ds_cap)) return;
 
   const unsigned t = threadIdx.x;
@@ -258,7 +259,7 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
       __syncthreads();
       const bool live = qrow < Sq;
       const float lse2 = live ? lse_raw * kLog2e : INFINITY;
-      const float dls = live ? dl_raw * a.scale : 0.f;
+      const float dl = live ? dl_raw : 0.f;
 
       // Per key block t (K, V, hid of t and K^T of t in LDS; t+1 in registers):
       //   S^T, dP^T, dS^T of both 32-key sub-blocks | barrier | K, V, hid of
@@ -292,7 +293,7 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
             dp = mfma32(as_bf16x8(&sm.u.kv.v[off]), of[kk], dp);
           }
           __builtin_amdgcn_s_setprio(0);
-          // ---- dS^T = P (dP scale - Delta scale), P = exp2(S scale log2 e - LSE log2 e) ----
+          // ---- dS'^T = P (dP - Delta), P = exp2(S scale log2 e - LSE log2 e) ----
           if (need_mask) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -306,7 +307,7 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const float p = fast_exp2(fmaf(s[v], a.scale_log2, -lse2));
-            dsb[jj][v >> 3][v & 7] = (bf16)(p * fmaf(dp[v], a.scale, -dls));
+            dsb[jj][v >> 3][v & 7] = (bf16)(p * (dp[v] - dl));
           }
         }
         __syncthreads();   // every wave is done with this block's K, V and hid
@@ -365,10 +366,10 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
         for (int r = 0; r < 4; ++r) {
           const float4 o = red[((qw * ND + d) * 4 + r) * 64 + lane];
           bf16x4 x;
-          x[0] = (bf16)(acc[d][4 * r] + o.x);
-          x[1] = (bf16)(acc[d][4 * r + 1] + o.y);
-          x[2] = (bf16)(acc[d][4 * r + 2] + o.z);
-          x[3] = (bf16)(acc[d][4 * r + 3] + o.w);
+          x[0] = (bf16)((acc[d][4 * r] + o.x) * a.scale);
+          x[1] = (bf16)((acc[d][4 * r + 1] + o.y) * a.scale);
+          x[2] = (bf16)((acc[d][4 * r + 2] + o.z) * a.scale);
+          x[3] = (bf16)((acc[d][4 * r + 3] + o.w) * a.scale);
           *reinterpret_cast<bf16x4*>(&drow[32 * d + 8 * r + 4 * hh]) = x;
         }
     }

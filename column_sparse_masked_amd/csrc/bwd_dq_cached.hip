@@ -2,13 +2,13 @@
 // accumulate).  FlashMask-3 paper summary, abstract: the mask-aware kernel
 // visits only the tiles the column-wise sparse mask does not fully hide.
 //
-// The key-stationary backward kernel already forms scale * dS of every
+// The key-stationary backward kernel already forms dS' = dS / scale of every
 // non-skipped tile; with the tile cache on it also stores it, one tile per
 // slot (bf16, 128 rows x 128 keys, in the blocks of 4 rows x 1 key per 8
 // bytes in which its waves hold it), and this kernel only has to contract it
 // with K:
-//     dQ_i = sum over the query block's listed key blocks kb of
-//            sum_j (scale dS)_ij K_j,
+//     dQ_i = scale * sum over the query block's listed key blocks kb of
+//            sum_j dS'_ij K_j,
 // with no exponentials, no interval tests and no recomputed S or dP.  The
 // work is then bound by reading the cached tiles from memory (32 KiB per
 // tile against 4 MFLOP of products), not by the matrix cores.
@@ -255,7 +255,7 @@ void attn_bwd_dq_cached_kernel(const BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         bf16x4 x;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) x[q] = (bf16)acc[d][4 * r + q];
+        for (int q = 0; q < 4; ++q) x[q] = (bf16)(acc[d][4 * r + q] * a.scale);
         *reinterpret_cast<bf16x4*>(&drow[32 * d + 8 * r + 4 * hh]) = x;
       }
   }

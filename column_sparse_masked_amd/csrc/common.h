@@ -21,7 +21,7 @@ constexpr int kCtrFwdItems = 0, kCtrBwdItems = 1, kCtrFwdNext = 2, kCtrBwdNext =
               kCtrTiles = 9,      // non-skipped tiles over all (batch, head) pairs (saturating)
               kCtrRowDone = 10;   // tile pass: row-kernel workgroups finished
 
-// Bytes of one cached tile of scale * dS (bf16, BQ rows of BK keys).
+// Bytes of one cached tile of dS / scale (bf16, BQ rows of BK keys).
 constexpr int kTileBytes = BQ * BK * 2;
 
 typedef __bf16 bf16;

@@ -77,7 +77,7 @@ struct BwdArgs {
   __bf16* dk;
   __bf16* dv;
   float* delta;       // fp32 [B][H][Sq]
-  // Tile cache: scale * dS of every non-skipped tile, bf16 [slot][BQ rows][BK keys],
+  // Tile cache: dS' = dS / scale of every non-skipped tile, bf16 [slot][BQ rows][BK keys],
   // written by the key-stationary kernel and read by the dQ kernel.  Used
   // when ds_cap > 0 and the tile pass counted at most ds_cap tiles.
   __bf16* ds;

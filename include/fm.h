@@ -122,7 +122,7 @@ fm_status fm_tileinfo_layout_query(const fm_problem* p, fm_tileinfo_layout* out)
 fm_status fm_bwd_workspace_bytes(const fm_problem* p, size_t* bytes);
 
 /* Bytes of a fm_attn_bwd workspace that also holds the tile cache for
- * n_tiles non-skipped tiles (32 KiB each: scale * dS in bf16), after the Delta
+ * n_tiles non-skipped tiles (32 KiB each: dS / scale in bf16), after the Delta
  * row terms: the size at which the backward computes dQ from the cache.  The
  * tile count of a problem is counter 9 of its tileinfo after fm_tile_bounds
  * (host only; FM_ERR_SHAPE for n_tiles >= 2^32 - 1). */
@@ -226,16 +226,17 @@ fm_status fm_attn_fwd_fp8(const fm_problem* p, const void* q, const void* k, con
  * aligned, caller-owned, contents on entry irrelevant) holds
  * `workspace_bytes` bytes, at least fm_bwd_workspace_bytes: the Delta row
  * terms, then optionally the tile cache.  Kernels: Delta; dK and dV
- * key-stationary over the tiles of each key block, which forms scale * dS
- * of every tile; dQ query-stationary over the tiles of each query block.
+ * key-stationary over the tiles of each key block, which forms dS / scale
+ * of every tile (the scale is applied to dK and dQ as they are written); dQ
+ * query-stationary over the tiles of each query block.
  * When the workspace holds the tile cache for every non-skipped tile
  * (fm_bwd_cache_bytes of the tile count the tile pass leaves in tileinfo
- * counter 9), the dK/dV kernel also stores scale * dS there (bf16) and dQ is
+ * counter 9), the dK/dV kernel also stores dS / scale there (bf16) and dQ is
  * its product with K, read back from the cache; otherwise dQ recomputes S
  * and dP.  The choice is made on the device from the tile count, so a cache
  * sized for other bounds is never overrun: the call falls back to the
  * recompute.  No atomics; the results are deterministic (the two dQ paths
- * round dS identically but may differ in the last bits).
+ * both round dS / scale to bf16, but may differ in its last bits).
  * Errors: FM_ERR_NULL for a missing tensor that the problem needs,
  * FM_ERR_ALIGN as fm_attn_fwd (workspace: 16 bytes), the problem's own
  * checks, FM_ERR_HIP for a launch the runtime rejects.  With Sq = 0, dK and

@@ -28,7 +28,7 @@ def say(msg):
 def run_gpu(w, tensors=None, device="cuda", want_bwd=True, both_paths=False):
     """Upload a workload, run tile pass + forward (+ backward) on the GPU and
     return numpy results (float64) and the tileinfo dictionary.  The backward
-    runs with the tile cache (dQ from the cached scale * dS, as the benchmark
+    runs with the tile cache (dQ from the cached dS / scale, as the benchmark
     runs it); with both_paths it runs again without the cache (dQ recomputed)
     into dq_rc, dk_rc, dv_rc."""
     import torch
