@@ -286,19 +286,39 @@ void attn_fwd_kernel(const FwdArgs a) {
         };
         auto half_pv = [&](int hk, f32x16 (&s)[2]) __attribute__((always_inline)) {
           // ---- online softmax in the log2 domain ----
-          // The running maximum m_run is only moved when a row's maximum
-          // exceeds it by more than 8 (P <= 2^8 otherwise): O and l are sums
-          // taken against the same reference, so their ratio is unchanged,
-          // and most halves skip the rescale of the accumulators.
-          float mx = -INFINITY;
+          // P is taken against the running reference m_run as it stands; only
+          // when some row has no reference yet or a lane's P sum leaves
+          // [0, 2^20] is the half's row maximum formed, the accumulators
+          // rescaled and P recomputed.  O and l are sums against the same
+          // reference, so their ratio does not depend on it.
+          bf16x8 pb[2][2];
+          float hs = 0.f;
+          auto make_p = [&](float base) __attribute__((always_inline)) {
+            hs = 0.f;
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[j][v]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float m_tile = mx * a.scale_log2;
-          if (__any(m_tile > m_run + 8.f)) {
-            const float m_new = fmaxf(m_run, m_tile);
+              for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+                for (int e8 = 0; e8 < 8; ++e8) {
+                  const float pv = fast_exp2(fmaf(s[j][8 * t2 + e8], a.scale_log2, -base));
+                  hs += pv;
+                  pb[j][t2][e8] = (bf16)pv;
+                }
+          };
+          bool ok = __all(m_run > -INFINITY);
+          if (ok) {
+            make_p(m_run);
+            ok = __all(hs <= 0x1p20f);
+          }
+          if (!ok) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[j][v]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx * a.scale_log2);
             const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
 #pragma unroll
             for (int d = 0; d < ND; ++d)
@@ -307,25 +327,18 @@ void attn_fwd_kernel(const FwdArgs a) {
             l_run *= alpha;
             rs *= alpha;
             m_run = m_new;
+            make_p((m_run == -INFINITY) ? 0.f : m_run);
           }
-          const float base = (m_run == -INFINITY) ? 0.f : m_run;
-          // ---- P (8 keys at a time, rounded to bf16) and O^T += V^T P^T ----
+          rs += hs;
+          // ---- O^T += V^T P^T ----
 #pragma unroll
           for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-              bf16x8 pb;
-#pragma unroll
-              for (int e8 = 0; e8 < 8; ++e8) {
-                const float pv = fast_exp2(fmaf(s[j][8 * t2 + e8], a.scale_log2, -base));
-                rs += pv;
-                pb[e8] = (bf16)pv;
-              }
+            for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
               for (int d = 0; d < ND; ++d)
                 acc[d] = mfma32(as_bf16x8(&sm.vt[(32 * d + li) * VTS + 32 * (2 * hk + j) + 16 * t2 + 8 * hh]),
-                                pb, acc[d]);
-            }
+                                pb[j][t2], acc[d]);
         };
         {
           f32x16 s0[2];
