@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <mutex>
 
 #include "../../include/fm.h"
@@ -135,7 +136,11 @@ thread_local fm::KernelEvents g_events;
 extern "C" {
 
 const char* fm_status_str(fm_status s) {
-  switch (s) {
+  // A C caller may pass any int; reading such a value as the C++ enum would
+  // be undefined, so the argument's bits are taken as an integer.
+  int code;
+  std::memcpy(&code, &s, sizeof code);
+  switch (code) {
     case FM_OK: return "FM_OK";
     case FM_ERR_NULL: return "FM_ERR_NULL: a required pointer is NULL";
     case FM_ERR_SHAPE: return "FM_ERR_SHAPE: a size is negative or beyond the supported range";
@@ -390,6 +395,10 @@ static fm_status attn_bwd(const fm_problem* p, const void* q, const void* k, con
       !aligned(o, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
       !aligned(dv, 16) || !aligned(bounds, 16) || !aligned(lse, 4) || !aligned(workspace, 16))
     return FM_ERR_ALIGN;
+  // the workspace must hold Delta (fm_bwd_workspace_bytes), else the first
+  // kernel would write past it
+  if (!use_scratch && has_rows && workspace_bytes < (size_t)p->batch * p->heads * p->seqlen_q * sizeof(float))
+    return FM_ERR_SHAPE;
   if (!has_rows && !has_cols) return FM_OK;
   Layout L = make_layout(p);
   const hipStream_t s = (hipStream_t)stream;

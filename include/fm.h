@@ -238,7 +238,8 @@ fm_status fm_attn_fwd_fp8(const fm_problem* p, const void* q, const void* k, con
  * recompute.  No atomics; the results are deterministic (the two dQ paths
  * both round dS / scale to bf16, but may differ in its last bits).
  * Errors: FM_ERR_NULL for a missing tensor that the problem needs,
- * FM_ERR_ALIGN as fm_attn_fwd (workspace: 16 bytes), the problem's own
+ * FM_ERR_ALIGN as fm_attn_fwd (workspace: 16 bytes), FM_ERR_SHAPE when
+ * workspace_bytes is below the B*H*Sq*4 bytes of Delta, the problem's own
  * checks, FM_ERR_HIP for a launch the runtime rejects.  With Sq = 0, dK and
  * dV are zero-filled; with Sk = 0, dQ is written as zero.
  */

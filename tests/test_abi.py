@@ -115,6 +115,15 @@ def test_misaligned_tensors_rejected_before_launch():
         assert L.lib.fm_attn_bwd(ctypes.byref(p), *a, 1 << 20, None) == L.FM_ERR_ALIGN, i
 
 
+def test_backward_workspace_smaller_than_delta_rejected():
+    """fm_attn_bwd's workspace must hold Delta (B*H*Sq fp32 values); a
+    smaller one is refused before any HIP call instead of being overrun."""
+    p = _p()                              # 1 x 2 x 300 rows: 2400 bytes of Delta
+    ok = ctypes.c_void_p(1 << 20)
+    for nbytes in (0, 16, 2396):
+        assert L.lib.fm_attn_bwd(ctypes.byref(p), *([ok] * 12), nbytes, None) == L.FM_ERR_SHAPE, nbytes
+
+
 def test_status_strings():
     for c in range(7):
         s = L.status_str(c)
