@@ -512,32 +512,38 @@ void attn_bwd_kernel(const BwdArgs a) {
           for (int v = 0; v < 16; ++v)
             s[v] = (hidden >> (8 * (v >> 2) + (v & 3))) & 1u ? -INFINITY : s[v];
         }
-        // P = exp2(S' scale log2(e)); dS' = P dP' (dS / scale)
+        // P = exp2(S' scale log2(e)); dS' = P dP' (dS / scale), 8 values (one
+        // k-step of the dV / dK products) at a time
         bf16x8 pb[2], dsb[2];
+        auto make_half = [&](int t2) __attribute__((always_inline)) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = fast_exp2(s[v] * a.scale_log2);
-          pb[v >> 3][v & 7] = (bf16)p;
-          dsb[v >> 3][v & 7] = (bf16)(p * dp[v]);
-        }
+          for (int e = 0; e < 8; ++e) {
+            const float p = fast_exp2(s[8 * t2 + e] * a.scale_log2);
+            pb[t2][e] = (bf16)p;
+            dsb[t2][e] = (bf16)(p * dp[8 * t2 + e]);
+          }
+        };
+        auto cache_and_exchange = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          sm.pds[g][m][0][t2][lane] = pb[t2];
-          sm.pds[g][m][1][t2][lane] = dsb[t2];
-        }
-        {
+          for (int t2 = 0; t2 < 2; ++t2) {
+            sm.pds[g][m][0][t2][lane] = pb[t2];
+            sm.pds[g][m][1][t2][lane] = dsb[t2];
+          }
           // the chunk's dS' into the tile cache: tile j of the item is
           // its j-th list entry (the walk starts at entry rot)
           int j = c / CPB + cur.rot;
           j = j < cnt ? j : j - cnt;
           store_ds_tile(cur.dsrc, dsb, g, m, j * kTileBytes + (c % CPB) * (kTileBytes / CPB), c);
-        }
+        };
         // ---- dV += P^T dO, dK += dS^T Q, head-dim half m, own rows ----
         constexpr int NP = NDH * 2;   // product pairs per half: (dd, t2)
         if constexpr (D == 128) {
+          // the first k-step's products run beside the second k-step's
+          // exponentials: pair i is (dd, t2) = (i % 2, i / 2)
+          make_half(0);
           bf16x8 bo[NP][2];
           auto read_b = [&](int i) __attribute__((always_inline)) {
-            const int off = boff(m, i >> 1, i & 1);
+            const int off = boff(m, i & 1, i >> 1);
             bo[i][0] = as_bf16x8(dotc + off);
             bo[i][1] = as_bf16x8(qtc + off);
           };
@@ -545,13 +551,23 @@ void attn_bwd_kernel(const BwdArgs a) {
           read_b(1);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int i = 0; i < NP; ++i) {
-            dv[i >> 1] = mfma32(bo[i][0], pb[i & 1], dv[i >> 1]);
-            dk[i >> 1] = mfma32(bo[i][1], dsb[i & 1], dk[i >> 1]);
-            if (i + 2 < NP) read_b(i + 2);
-            __builtin_amdgcn_sched_barrier(0);
+          for (int i = 0; i < 2; ++i) {
+            dv[i & 1] = mfma32(bo[i][0], pb[0], dv[i & 1]);
+            dk[i & 1] = mfma32(bo[i][1], dsb[0], dk[i & 1]);
+            read_b(i + 2);
+          }
+          make_half(1);
+          __builtin_amdgcn_sched_barrier(0);
+          cache_and_exchange();
+#pragma unroll
+          for (int i = 2; i < NP; ++i) {
+            dv[i & 1] = mfma32(bo[i][0], pb[1], dv[i & 1]);
+            dk[i & 1] = mfma32(bo[i][1], dsb[1], dk[i & 1]);
           }
         } else {
+          make_half(0);
+          make_half(1);
+          cache_and_exchange();
 #pragma unroll
           for (int dd = 0; dd < NDH; ++dd)
 #pragma unroll
