@@ -77,7 +77,8 @@ __device__ int block_exclusive_scan(int x, int* scratch, int* total) {
 // sorted queue.  Counted from the histogram of tile counts, which is exact
 // below the top bucket; with any item in the top bucket nothing is split.
 struct SplitRule {
-  bool on;
+  bool on;    // this part sorts the forward queue and splitting is allowed
+  bool any;   // splitting is allowed at all (the same in both parts)
   int fwd_slots, split_cap;
 };
 
@@ -221,9 +222,9 @@ __device__ void sort_items(int tp, Counts cnt, uint32_t* __restrict__ queue, int
     for (int u = 0; u < kUnroll; ++u) wave_bucket_add(hist, c[u], e0 + (uint32_t)(u * NT + tp) < m);
   }
   __syncthreads();
-  {
+  if (split.any) {
     // Which forward items to split, counted in items (the barriers run in
-    // every part).
+    // every part; when no item may be split, in none).
     long tiles = 0;
     for (int i = tp; i < min(nb, kBuckets - 1); i += NT) tiles += (long)i * hist[i];
     const long total = part_sum<NT>(tiles, tp, lscratch) * (long)reps;
@@ -533,7 +534,7 @@ __global__ __launch_bounds__(kQueueThreads) void row_kernel(
     // the two halves of the workgroup sort the two queues side by side
     constexpr int kHalf = kQueueThreads / 2;
     const int part = t / kHalf, tp = t % kHalf;
-    const SplitRule sr{part == 0 && split_cap > 0, fwd_slots, split_cap};
+    const SplitRule sr{part == 0 && split_cap > 0, split_cap > 0, fwd_slots, split_cap};
     int* sc = scratch + part * (kHalf / 64);
     long* lsc = lscratch + part * (kHalf / 64);
     // (a forward item's count is at most nK, a backward item's at most nQ)
