@@ -58,8 +58,10 @@ struct Stage {
   static constexpr int NK = BK * CPR / 256;       // K rows per thread
   static constexpr int NV = (BK / 4) * CPR / 256; // V units per thread
   static_assert(CPR % 4 == 0 && ((BK / 4) * CPR) % 256 == 0, "whole V units per thread");
-  bf16x8 k[NK];
-  bf16x8 v[4 * NV];
+  static_assert(NK == 4 * NV, "a K block and a V block take the same registers");
+  // One set of registers holds K of the next block until it is stored, then
+  // V of that block: the two are never held at the same time in the loop.
+  bf16x8 x[NK];
 
   static __device__ __forceinline__ int k_row(unsigned t) { return NK * (int)(t / CPR); }
   static __device__ __forceinline__ int k_col(unsigned t) { return (int)(t % CPR); }
@@ -79,7 +81,7 @@ __device__ __forceinline__ void load_k(Stage<D>& r, BufRsrc kb, int k0, unsigned
   using S = Stage<D>;
   const uint32_t base = opaque(((uint32_t)S::k_row(t) * S::CPR + S::k_col(t)) * 16u) + (uint32_t)k0 * (D * 2);
 #pragma unroll
-  for (int i = 0; i < S::NK; ++i) r.k[i] = buf_load16(kb, base + (uint32_t)i * (D * 2));
+  for (int i = 0; i < S::NK; ++i) r.x[i] = buf_load16(kb, base + (uint32_t)i * (D * 2));
 }
 
 template <int D>
@@ -88,7 +90,7 @@ __device__ __forceinline__ void store_k(const Stage<D>& r, bf16* sk, unsigned t)
   constexpr int KST = FwdSmem<D>::KST;
   bf16* dst = sk + opaque(S::k_row(t) * KST + S::k_col(t) * 8);
 #pragma unroll
-  for (int i = 0; i < S::NK; ++i) *reinterpret_cast<bf16x8*>(dst + i * KST) = r.k[i];
+  for (int i = 0; i < S::NK; ++i) *reinterpret_cast<bf16x8*>(dst + i * KST) = r.x[i];
 }
 
 template <int D>
@@ -99,7 +101,7 @@ __device__ __forceinline__ void load_v(Stage<D>& r, BufRsrc vb, int k0, unsigned
     const uint32_t base =
         opaque(((uint32_t)S::v_key(t, j) * S::CPR + S::v_col(t, j)) * 16u) + (uint32_t)k0 * (D * 2);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) r.v[4 * j + rr] = buf_load16(vb, base + (uint32_t)rr * (D * 2));
+    for (int rr = 0; rr < 4; ++rr) r.x[4 * j + rr] = buf_load16(vb, base + (uint32_t)rr * (D * 2));
   }
 }
 
@@ -113,9 +115,9 @@ __device__ __forceinline__ void store_vt(const Stage<D>& r, bf16* vt, unsigned t
     bf16* dst = vt + opaque((8 * S::v_col(t, i)) * VTS + vt_pos(S::v_key(t, i)));
     // 4 keys x 8 columns -> 8 rows of 4 keys (constant shuffles only, so the
     // compiler keeps everything in registers)
-    const bf16x16 p01 = __builtin_shufflevector(r.v[4 * i], r.v[4 * i + 1], 0, 8, 1, 9, 2, 10, 3,
+    const bf16x16 p01 = __builtin_shufflevector(r.x[4 * i], r.x[4 * i + 1], 0, 8, 1, 9, 2, 10, 3,
                                                 11, 4, 12, 5, 13, 6, 14, 7, 15);
-    const bf16x16 p23 = __builtin_shufflevector(r.v[4 * i + 2], r.v[4 * i + 3], 0, 8, 1, 9, 2, 10,
+    const bf16x16 p23 = __builtin_shufflevector(r.x[4 * i + 2], r.x[4 * i + 3], 0, 8, 1, 9, 2, 10,
                                                 3, 11, 4, 12, 5, 13, 6, 14, 7, 15);
 #define FM_VT_ROW(e)                                                                      \
   *reinterpret_cast<bf16x4*>(dst + (e) * VTS) =                                           \
@@ -129,6 +131,9 @@ __device__ __forceinline__ void store_vt(const Stage<D>& r, bf16* vt, unsigned t
 // SPLIT: whether items may be split in two (the instance without is used
 // when the problem has enough items per workgroup for the longest-first
 // order to balance the grid; its code has none of the split handling).
+// LDS operands of the S and PV products are read this many products ahead.
+constexpr int kRA = 3;
+
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const FwdArgs a) {
@@ -202,14 +207,14 @@ void attn_fwd_kernel(const FwdArgs a) {
       auto list_at = [&](int i) -> uint32_t {
         return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(lbase, i * 2, 0, 0);
       };
-      Stage<D> st;
+      Stage<D> st, st_v;   // (st_v: V of the first block only)
       int e_cur = list_entry(lst, 0);
       int e_next = cnt > 1 ? list_entry(lst, 1) : 0;
       bf16x8 qf[NS];   // Q rows of this wave (B operand of S^T = K Q^T)
       {
         const int k0 = block_start(e_cur);
         load_k<D>(st, kbase, k0, t);
-        load_v<D>(st, vbase, k0, t);
+        load_v<D>(st_v, vbase, k0, t);
         int4 breg = make_int4(0, 0, 0, 0);
         if (block_masked(e_cur, k0) && t < BK) breg = load_bnd(bbase, k0, Sk, t);
         // issued after the block's loads: the staging below waits for those only
@@ -217,7 +222,7 @@ void attn_fwd_kernel(const FwdArgs a) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) qf[s] = buf_load16(qbase, qoff + 32u * s);
         store_k<D>(st, sm.k, t);
-        store_vt<D>(st, sm.vt, t);
+        store_vt<D>(st_v, sm.vt, t);
         if (block_masked(e_cur, k0) && t < BK) {
           uint32_t wd[BQ / 32];
           hidden_rows(breg, qb * BQ, wd);
@@ -226,6 +231,11 @@ void attn_fwd_kernel(const FwdArgs a) {
         }
       }
       pf.stash(sm.hdr[(n + 1) & 1], t);   // the stores above waited for loads issued after the ticket
+      // The Q rows are in registers by now (loaded right after the block's K
+      // and V, which the stores waited for).  Saying so with an explicit wait
+      // keeps the compiler from waiting for the loads of later key blocks,
+      // issued after Q, before the S products of every block.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       if (cnt > 1) load_k<D>(st, kbase, block_start(e_next), t);
       __syncthreads();
 
@@ -234,14 +244,16 @@ void attn_fwd_kernel(const FwdArgs a) {
       //   S_t(h0) | barrier | softmax, PV_t(h0); S_t(h1) | barrier | K_{t+1}
       //   -> LDS; bounds_{t+1}, V_{t+1} -> registers; softmax, PV_t(h1);
       //   bounds_{t+1} -> LDS | barrier | V_{t+1} -> LDS, K_{t+2} -> registers.
-      for (int tt = 0; tt < cnt; ++tt) {
+      for (int tt = 0;; ++tt) {
         const int k0 = block_start(e_cur);
         const bool need_mask = block_masked(e_cur, k0);
         const bool has_next = tt + 1 < cnt;
         const int k0n = block_start(e_next);
         const bool nm_next = has_next && block_masked(e_next, k0n);
-        // list entry of block t+2, consumed after the second barrier
-        const uint32_t e2_pending = (tt + 2 < cnt) ? list_at(tt + 2) : 0u;
+        // list entry of block t+2, consumed after the last barrier (past the
+        // end of the list the range check reads 0; the load is unconditional
+        // so that no path leaves it in flight into the next block)
+        const uint32_t e2_pending = list_at(tt + 2);
 
         // The block is taken as two halves of 64 keys: S of a half, then its
         // softmax and PV, so that S needs 32 accumulator registers rather
@@ -258,13 +270,26 @@ void attn_fwd_kernel(const FwdArgs a) {
           for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) s[j][v] = 0.f;
-          // k-step major: the two accumulators advance together
+          // k-step major: the two accumulators advance together.  Product i
+          // is (k-step i / 2, key group i % 2); its K operand is read from LDS
+          // kRA products ahead, and the scheduling fences keep that order
+          // (left to itself the compiler reads each operand just before its
+          // product, which then waits for the whole LDS round trip).
+          constexpr int NP = 2 * NS;
+          bf16x8 ka[NP];
+          auto read_k = [&](int i) __attribute__((always_inline)) {
+            ka[i] = as_bf16x8(&sm.k[(32 * (2 * hk + (i & 1)) + li) * KST + 16 * (i >> 1) + 8 * hh]);
+          };
+#pragma unroll
+          for (int i = 0; i < kRA; ++i) read_k(i);
           __builtin_amdgcn_s_setprio(1);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int kk = 0; kk < NS; ++kk)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              s[j] = mfma32(as_bf16x8(&sm.k[(32 * (2 * hk + j) + li) * KST + 16 * kk + 8 * hh]), qf[kk], s[j]);
+          for (int i = 0; i < NP; ++i) {
+            s[i & 1] = mfma32(ka[i], qf[i >> 1], s[i & 1]);
+            if (i + kRA < NP) read_k(i + kRA);
+            __builtin_amdgcn_sched_barrier(0);
+          }
           __builtin_amdgcn_s_setprio(0);
           if (need_mask) {
             // words of 4 consecutive keys for this wave's 32 rows; bit li is
@@ -306,6 +331,16 @@ void attn_fwd_kernel(const FwdArgs a) {
                   pb[j][t2][e8] = (bf16)pv;
                 }
           };
+          // the first V^T operands of the PV products are read before the
+          // exponentials, whose time covers their LDS round trip
+          constexpr int NP = 4 * ND;   // product i: (j, t2) = (i / (2 ND), i / ND % 2), d = i % ND
+          bf16x8 va[NP];
+          auto read_v = [&](int i) __attribute__((always_inline)) {
+            const int j = i / (2 * ND), t2 = (i / ND) & 1, d = i % ND;
+            va[i] = as_bf16x8(&sm.vt[(32 * d + li) * VTS + 32 * (2 * hk + j) + 16 * t2 + 8 * hh]);
+          };
+#pragma unroll
+          for (int i = 0; i < kRA; ++i) read_v(i);
           bool ok = __all(m_run > -INFINITY);
           if (ok) {
             make_p(m_run);
@@ -331,14 +366,13 @@ void attn_fwd_kernel(const FwdArgs a) {
           }
           rs += hs;
           // ---- O^T += V^T P^T ----
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-              for (int d = 0; d < ND; ++d)
-                acc[d] = mfma32(as_bf16x8(&sm.vt[(32 * d + li) * VTS + 32 * (2 * hk + j) + 16 * t2 + 8 * hh]),
-                                pb[j][t2], acc[d]);
+          for (int i = 0; i < NP; ++i) {
+            acc[i % ND] = mfma32(va[i], pb[i / (2 * ND)][(i / ND) & 1], acc[i % ND]);
+            if (i + kRA < NP) read_v(i + kRA);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         };
         {
           f32x16 s0[2];
@@ -372,16 +406,15 @@ void attn_fwd_kernel(const FwdArgs a) {
         if (tt == 0) pf.fetch_entry(iq, sm.hdr[(n + 1) & 1]);
         if (tt == 1) pf.fetch_count(iq);
         __syncthreads();   // every wave is done with this block's V^T; K_{t+1} is in LDS
-        if (has_next) {
-          store_vt<D>(st, sm.vt, t);
-          int e2 = 0;
-          if (tt + 2 < cnt) {
-            e2 = __builtin_amdgcn_readfirstlane(e2_pending);
-            load_k<D>(st, kbase, block_start(e2), t);
-          }
-          e_cur = e_next;
-          e_next = e2;
-        }
+        // read on every path, so that no trip back to the top of the loop
+        // leaves the list load in flight (the compiler would then wait for
+        // every load, the next K block's included, at the top)
+        const int e2 = __builtin_amdgcn_readfirstlane(e2_pending);
+        if (!has_next) break;
+        store_vt<D>(st, sm.vt, t);
+        if (tt + 2 < cnt) load_k<D>(st, kbase, block_start(e2), t);
+        e_cur = e_next;
+        e_next = e2;
       }
       if (cnt == 1) pf.fetch_count(iq);
       pf.publish(iq, sm.hdr[(n + 1) & 1], t);
