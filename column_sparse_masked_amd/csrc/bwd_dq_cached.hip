@@ -102,6 +102,7 @@ __device__ __forceinline__ void tile_store_t(const TileStage<COLS>& r, bf16* dst
 }
 
 constexpr int kKSteps = BK / 16;   // 16-key steps per tile
+constexpr int kCqRA = 3;           // products whose LDS operands are read ahead
 
 // A cached dS tile in registers (256 threads): unit u of thread t is
 // u = t + 256 i (i < 4), i.e. (c2, m, g, rr) = u / 64 and, within it, hh =
@@ -227,18 +228,34 @@ void attn_bwd_dq_cached_kernel(const BwdArgs a) {
       ds_store_t<ST>(x.ds, sm.ds, t, i);
       __syncthreads();
       load_tile(x, i + 2);
+      // product j is (k-step j / ND, head-dim block j % ND); its operands are
+      // read from LDS kCqRA products ahead, in the order the fences keep
       const bf16* drow = sm.ds + (32 * w + li) * ST + 8 * hh;
+      constexpr int NP = kKSteps * ND;
+      bf16x8 av[NP], bv[kKSteps];
+      auto read_ops = [&](int j) __attribute__((always_inline)) {
+        const int kk = j / ND, d = j % ND;
+        if (d == 0) bv[kk] = as_bf16x8(drow + 16 * kk);
+        av[j] = as_bf16x8(&sm.kt[(32 * d + li) * ST + 16 * kk + 8 * hh]);
+      };
 #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) {
-        const bf16x8 bop = as_bf16x8(drow + 16 * kk);
+      for (int j = 0; j < kCqRA; ++j) read_ops(j);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int d = 0; d < ND; ++d)
-          acc[d] = mfma32(as_bf16x8(&sm.kt[(32 * d + li) * ST + 16 * kk + 8 * hh]), bop, acc[d]);
+      for (int j = 0; j < NP; ++j) {
+        acc[j % ND] = mfma32(av[j], bv[j / ND], acc[j % ND]);
+        if (j + kCqRA < NP) read_ops(j + kCqRA);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
-    for (int i = 0; i < n; i += 2) {
+    // (exits by break, so that every trip back to the top has issued the
+    // same loads in the same order: the compiler then waits for each tile's
+    // own loads only, not for the next tile's as well)
+    for (int i = 0;; i += 2) {
       step(i, pa);
-      if (i + 1 < n) step(i + 1, pb);
+      if (i + 1 >= n) break;
+      step(i + 1, pb);
+      if (i + 2 >= n) break;
     }
     // the loads past the last tile were empty; wait for them before the
     // table is refilled
