@@ -46,7 +46,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("mask_heads", ctypes.c_int32), ("seqlen_q", ctypes.c_int32),
                 ("seqlen_k", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("fwd_rows", ctypes.c_int32)]
 
 
 class TileinfoLayout(ctypes.Structure):
@@ -59,6 +59,7 @@ class TileinfoLayout(ctypes.Structure):
                 ("list_k", ctypes.c_size_t), ("fwd_queue", ctypes.c_size_t),
                 ("bwd_queue", ctypes.c_size_t), ("fwd_partials", ctypes.c_size_t),
                 ("cpos", ctypes.c_size_t), ("colbase", ctypes.c_size_t),
+                ("cnt_p", ctypes.c_size_t), ("list_p", ctypes.c_size_t),
                 ("total", ctypes.c_size_t)]
 
 
@@ -100,8 +101,8 @@ def status_str(status: int) -> str:
     return lib.fm_status_str(status).decode()
 
 
-def problem(batch, heads, mask_heads, seqlen_q, seqlen_k, head_dim, softmax_scale) -> Problem:
-    return Problem(batch, heads, mask_heads, seqlen_q, seqlen_k, head_dim, softmax_scale)
+def problem(batch, heads, mask_heads, seqlen_q, seqlen_k, head_dim, softmax_scale, fwd_rows=0) -> Problem:
+    return Problem(batch, heads, mask_heads, seqlen_q, seqlen_k, head_dim, softmax_scale, fwd_rows)
 
 
 def tile_shape(p: Problem) -> tuple[int, int]:

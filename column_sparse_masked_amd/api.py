@@ -48,17 +48,17 @@ class MaskedAttention:
     read or write outside it, so a mismatch raises ValueError instead."""
 
     def __init__(self, batch, heads, mask_heads, seqlen_q, seqlen_k, head_dim,
-                 softmax_scale=None, device="cuda"):
+                 softmax_scale=None, device="cuda", fwd_rows=0):
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(head_dim)
-        self.p = _lib.problem(batch, heads, mask_heads, seqlen_q, seqlen_k, head_dim, softmax_scale)
+        self.p = _lib.problem(batch, heads, mask_heads, seqlen_q, seqlen_k, head_dim, softmax_scale, fwd_rows)
         self.device = torch.device(device)
         self.buf = _lib.alloc_buffers(self.p, self.device)
         self.block_q, self.block_k = _lib.tile_shape(self.p)
 
     @classmethod
-    def for_workload(cls, w, device="cuda"):
-        return cls(w.B, w.H, w.Hm, w.Sq, w.Sk, w.D, w.scale, device)
+    def for_workload(cls, w, device="cuda", fwd_rows=0):
+        return cls(w.B, w.H, w.Hm, w.Sq, w.Sk, w.D, w.scale, device, fwd_rows)
 
     # ---- argument checks ----
     def _shape(self, kind):
@@ -158,6 +158,8 @@ class MaskedAttention:
         raw = self.buf.tileinfo.cpu().numpy()
         bhm, bh = p.batch * p.mask_heads, p.batch * p.heads
         nQ, nK = L.n_qblocks, L.n_kblocks
+        # the pair lists exist where pair mode can be chosen (head_dim 128)
+        nP = (nQ + 1) // 2 if p.head_dim == 128 and p.fwd_rows != 128 else 0
 
         def view(off, dtype, shape):
             n = int(np.prod(shape))
@@ -175,5 +177,7 @@ class MaskedAttention:
             "bwd_queue": view(L.bwd_queue, np.uint32, (bh * nK,)),
             "cpos": view(L.cpos, np.uint16, (bhm, nK, nQ)).reshape(p.batch, p.mask_heads, nK, nQ),
             "colbase": view(L.colbase, np.uint32, (bh * nK,)),
+            "cnt_p": view(L.cnt_p, np.int32, (p.batch, p.mask_heads, nP)),
+            "list_p": view(L.list_p, np.uint32, (bhm, nP, nK)).reshape(p.batch, p.mask_heads, nP, nK),
             "nQ": nQ, "nK": nK,
         }

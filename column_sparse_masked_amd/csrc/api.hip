@@ -28,6 +28,8 @@ fm_status check_problem(const fm_problem* p) {
   if (p->head_dim != 64 && p->head_dim != 128) return FM_ERR_UNSUPPORTED;
   if (p->mask_heads != 1 && p->mask_heads != p->heads) return FM_ERR_UNSUPPORTED;
   if (!(p->softmax_scale > 0.f) || !std::isfinite(p->softmax_scale)) return FM_ERR_UNSUPPORTED;
+  if (p->fwd_rows != 0 && p->fwd_rows != fm::BQ && p->fwd_rows != 2 * fm::BQ) return FM_ERR_UNSUPPORTED;
+  if (p->fwd_rows == 2 * fm::BQ && p->head_dim != 128) return FM_ERR_UNSUPPORTED;
   const long nQ = (p->seqlen_q + fm::BQ - 1) / fm::BQ, nK = (p->seqlen_k + fm::BK - 1) / fm::BK;
   const long items = (long)p->batch * p->heads * (nQ > nK ? nQ : nK);
   if (items >= (1L << 31)) return FM_ERR_SHAPE;
@@ -38,8 +40,20 @@ struct Layout {
   int nQ, nK;
   int split_cap;   // forward items that may be split in two
   size_t counters, kbsum, cls, cnt_q, cnt_k, list_q, list_k, fwd_queue, bwd_queue, fwd_partials, cpos, colbase,
-      total;
+      cnt_p, list_p, total;
 };
+
+// Pair mode (forward items of two neighbouring query blocks, head_dim 128):
+// asked for with fwd_rows = 256, or chosen when there are at least four
+// pairs per workgroup of the pair kernel's grid (one per compute unit), so
+// that the longest-first order balances the grid without splitting items.
+// fm_tile_bounds and the attention calls take the same decision.
+bool pairs_for(const fm_problem* p, int nQ, int cus) {
+  if (p->head_dim != 128 || p->fwd_rows == fm::BQ) return false;
+  if (p->fwd_rows == 2 * fm::BQ) return true;
+  const long pairs = (long)p->batch * p->heads * ((nQ + 1) / 2);
+  return pairs >= 4L * cus * fm::fwd_pair_blocks_per_cu();
+}
 
 // At most this many forward items are split (two partial-result slots each).
 constexpr long kMaxSplitItems = 512;
@@ -49,6 +63,7 @@ constexpr long kMaxSplitItems = 512;
 // order already balances the grid, and the kernel without split handling
 // runs.  fm_tile_bounds and fm_attn_fwd take the same decision.
 int split_cap_for(const fm_problem* p, const Layout& L, int cus) {
+  if (pairs_for(p, L.nQ, cus)) return 0;
   const long items = (long)p->batch * p->heads * L.nQ;
   const long slots = (long)cus * fm::fwd_blocks_per_cu(p->head_dim);
   return items < 4 * slots ? L.split_cap : 0;
@@ -75,6 +90,10 @@ Layout make_layout(const fm_problem* p) {
   off = align256(off + (size_t)2 * L.split_cap * fm::BQ * ((size_t)p->head_dim * 2 + sizeof(float)));
   L.cpos = off;      off = align256(off + bhm * L.nK * L.nQ * sizeof(uint16_t));
   L.colbase = off;   off = align256(off + bh * L.nK * sizeof(uint32_t));
+  // the pair lists only where pair mode can be chosen
+  const size_t nP = (p->head_dim == 128 && p->fwd_rows != fm::BQ) ? (size_t)(L.nQ + 1) / 2 : 0;
+  L.cnt_p = off;     off = align256(off + bhm * nP * sizeof(int32_t));
+  L.list_p = off;    off = align256(off + bhm * nP * L.nK * sizeof(uint32_t));
   L.total = off;
   return L;
 }
@@ -184,6 +203,8 @@ fm_status fm_tileinfo_layout_query(const fm_problem* p, fm_tileinfo_layout* out)
   out->fwd_partials = L.fwd_partials;
   out->cpos = L.cpos;
   out->colbase = L.colbase;
+  out->cnt_p = L.cnt_p;
+  out->list_p = L.list_p;
   out->total = L.total;
   return FM_OK;
 }
@@ -276,12 +297,15 @@ fm_status fm_tile_bounds(const fm_problem* p, const int32_t* bounds, void* tilei
   a.bwd_queue = at<uint32_t>(tileinfo, L.bwd_queue);
   a.colbase = at<uint32_t>(tileinfo, L.colbase);
   a.counters = at<uint32_t>(tileinfo, L.counters);
+  a.cnt_p = at<int>(tileinfo, L.cnt_p);
+  a.list_p = at<uint32_t>(tileinfo, L.list_p);
   a.B = p->batch; a.H = p->heads; a.Hm = p->mask_heads;
   a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
   int cus = 0;
   if ((st = cu_count(&cus)) != FM_OK) return st;
   a.fwd_slots = cus * fm::fwd_blocks_per_cu(p->head_dim);
   a.split_cap = split_cap_for(p, L, cus);
+  a.pairs = pairs_for(p, L.nQ, cus) ? 1 : 0;
   return fm::launch_tile_bounds(a, (hipStream_t)stream) == hipSuccess ? FM_OK : FM_ERR_HIP;
 }
 
@@ -313,10 +337,18 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
   a.queue = at<uint32_t>(tileinfo, L.fwd_queue);
   a.counters = at<uint32_t>(tileinfo, L.counters);
   a.partials = at<float>(tileinfo, L.fwd_partials);
+  a.list_p = at<uint32_t>(tileinfo, L.list_p);
+  a.cnt_p = at<int>(tileinfo, L.cnt_p);
   a.split_cap = split_cap_for(p, L, cus);
   a.B = p->batch; a.H = p->heads; a.Hm = p->mask_heads;
   a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
   a.scale_log2 = p->softmax_scale * fm::kLog2e;
+  if (pairs_for(p, L.nQ, cus)) {
+    const long pairs = (long)p->batch * p->heads * ((L.nQ + 1) / 2);
+    const long slots = (long)cus * fm::fwd_pair_blocks_per_cu();
+    const int grid = (int)(pairs < slots ? pairs : slots);
+    return fm::launch_attn_fwd_pair(a, grid, (hipStream_t)stream, g_events) == hipSuccess ? FM_OK : FM_ERR_HIP;
+  }
   // tickets: every item, plus a second one for each item that may be split
   const long items = (long)p->batch * p->heads * L.nQ;
   const long tickets = items + (items < a.split_cap ? items : a.split_cap);
@@ -444,6 +476,7 @@ static fm_status attn_bwd(const fm_problem* p, const void* q, const void* k, con
   a.Sq = p->seqlen_q; a.Sk = p->seqlen_k; a.nQ = L.nQ; a.nK = L.nK;
   a.scale = p->softmax_scale;
   a.scale_log2 = p->softmax_scale * fm::kLog2e;
+  a.pairs = pairs_for(p, L.nQ, cus) ? 1 : 0;
   const long items = (long)p->batch * p->heads * L.nK;
   const long slots = (long)cus * fm::bwd_blocks_per_cu(p->head_dim);
   const int grid = (int)(items < slots ? items : slots);

@@ -175,7 +175,18 @@ void attn_bwd_dq_cached_kernel(const BwdArgs a) {
   const int lane = (int)(t & 63), w = (int)(t >> 6);
   const int li = lane & 31, hh = lane >> 5;
   const uint32_t max_items = (uint32_t)((long)a.B * a.H * a.nQ);
-  const uint32_t it = min(*(const_u32*)(a.queue_q + blockIdx.x), max_items - 1);
+  // one workgroup per queue entry, or in pair mode two per entry (a pair of
+  // query blocks; the second of a last block without a partner has nothing to do)
+  uint32_t it;
+  if (a.pairs) {
+    const uint32_t nP = (uint32_t)(a.nQ + 1) >> 1;
+    const uint32_t raw = min(*(const_u32*)(a.queue_q + (blockIdx.x >> 1)), (uint32_t)((long)a.B * a.H * nP) - 1u);
+    const uint32_t pbh = raw / nP, blk = 2 * (raw - pbh * nP) + (blockIdx.x & 1u);
+    if (blk >= (uint32_t)a.nQ) return;
+    it = pbh * (uint32_t)a.nQ + blk;
+  } else {
+    it = min(*(const_u32*)(a.queue_q + blockIdx.x), max_items - 1);
+  }
   const long bh = it / a.nQ;
   const int qb = (int)(it % a.nQ);
   const int b = (int)(bh / a.H), h = (int)(bh % a.H);
@@ -279,7 +290,7 @@ void attn_bwd_dq_cached_kernel(const BwdArgs a) {
 }
 
 hipError_t launch_attn_bwd_dq_cached(const BwdArgs& a, int head_dim, hipStream_t stream) {
-  const long items = (long)a.B * a.H * a.nQ;
+  const long items = (long)a.B * a.H * (a.pairs ? 2 * ((a.nQ + 1) / 2) : a.nQ);
   if (items <= 0 || a.ds_cap == 0) return hipSuccess;
   if (head_dim == 128)
     attn_bwd_dq_cached_kernel<128><<<(unsigned)items, kCqThreads, 0, stream>>>(a);

@@ -19,7 +19,14 @@ constexpr int kCtrFwdItems = 0, kCtrBwdItems = 1, kCtrFwdNext = 2, kCtrBwdNext =
               kCtrFwdExit = 4, kCtrBwdExit = 5, kCtrDqNext = 6, kCtrDqExit = 7,
               kCtrFwdSplit = 8,   // forward items split in two (the first of the queue)
               kCtrTiles = 9,      // non-skipped tiles over all (batch, head) pairs (saturating)
-              kCtrRowDone = 10;   // tile pass: row-kernel workgroups finished
+              kCtrRowDone = 10,   // tile pass: row-kernel workgroups finished
+              kCtrFwdPairs = 11;  // 1 when forward items are pairs of query blocks
+
+// Union-list entries of a query-block pair (pair mode): the key block, and
+// for each of the two query blocks whether it sees the block and whether
+// that tile is partial.
+constexpr uint32_t kPairBlock = 0xFFFFu, kPairSee0 = 1u << 16, kPairPart0 = 1u << 17,
+                   kPairSee1 = 1u << 18, kPairPart1 = 1u << 19;
 
 // Bytes of one cached tile of dS / scale (bf16, BQ rows of BK keys).
 constexpr int kTileBytes = BQ * BK * 2;
@@ -210,9 +217,27 @@ struct ItemQueue {
   // blocks): ticket v < 2 nsplit is entry v / 2, ticket v >= 2 nsplit entry
   // v - nsplit; n_items counts tickets.
   uint32_t nsplit = 0;
+  // nP > 0: the queue holds pairs (b*H + h)*nP + qp of blocks 2qp, 2qp+1 (pair
+  // mode), at most max_entries of them, and ticket v is block 2qp + v % 2 of
+  // entry v / 2; a second block past the last one (nBlk odd) is no item.
+  int nP = 0;
+  uint32_t max_entries = 0;
 
   __device__ __forceinline__ uint32_t position(uint32_t v) const {
+    if (nP > 0) return v >> 1;
     return v < 2 * nsplit ? v >> 1 : v - nsplit;
+  }
+  __device__ __forceinline__ uint32_t entries() const { return nP > 0 ? max_entries : max_items; }
+  // The item of ticket v with queue entry raw (clamped to the queue's range);
+  // none: the ticket has no item (its block would be nBlk).
+  __device__ __forceinline__ uint32_t item_of(uint32_t v, uint32_t raw, bool& none) const {
+    raw = min(raw, entries() - 1);
+    none = false;
+    if (nP <= 0) return raw;
+    const uint32_t bh = raw / (uint32_t)nP, qp = raw - bh * (uint32_t)nP;
+    const uint32_t blk = 2 * qp + (v & 1u);
+    none = blk >= (uint32_t)nBlk;
+    return min(bh * (uint32_t)nBlk + min(blk, (uint32_t)nBlk - 1), max_items - 1);
   }
 
   // index of item `it` (= (b * H + h) * nBlk + blk) in `cnt`
@@ -222,13 +247,15 @@ struct ItemQueue {
     return ((long)b * Hm + (Hm == 1 ? 0 : (long)h)) * nBlk + blk;
   }
   // The first item's header, read directly (thread 0, before the first item).
+  // A ticket without an item has count -1.
   __device__ __forceinline__ void first(uint32_t (&hdr)[4]) const {
     const uint32_t idx = atomicAdd(ticket, 1u);
     uint32_t it = 0;
     int c = 0;
     if (idx < n_items) {
-      it = min(queue[position(idx)], max_items - 1);
-      c = min(cnt[cnt_index(it)], cap);
+      bool none;
+      it = item_of(idx, queue[position(idx)], none);
+      c = none ? -1 : min(cnt[cnt_index(it)], cap);
     }
     hdr[0] = idx;
     hdr[1] = it;
@@ -266,11 +293,12 @@ struct ItemPrefetch {
   }
   __device__ __forceinline__ void fetch_entry(const ItemQueue& q, const uint32_t (&hdr)[4]) {
     idx = __builtin_amdgcn_readfirstlane(hdr[3]);
-    item = *(const_u32*)(q.queue + min(q.position(idx), q.max_items - 1));   // raw until fetch_count
+    item = *(const_u32*)(q.queue + min(q.position(idx), q.entries() - 1));   // raw until fetch_count
   }
   __device__ __forceinline__ void fetch_count(const ItemQueue& q) {
-    item = min(item, q.max_items - 1);
-    cnt = *(const_i32*)(q.cnt + q.cnt_index(item));              // raw until publish
+    bool none;
+    item = q.item_of(idx, item, none);
+    cnt = none ? -1 : *(const_i32*)(q.cnt + q.cnt_index(item));   // raw until publish
   }
   __device__ __forceinline__ void publish(const ItemQueue& q, uint32_t (&hdr)[4], unsigned t) const {
     if (t == 0) {

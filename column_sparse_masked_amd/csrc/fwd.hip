@@ -25,15 +25,15 @@
 
 namespace fm {
 
-template <int D>
+template <int D, int NQB = 1>
 struct alignas(16) FwdSmem {
   static constexpr int KST = D + 8;    // K row stride (elements): conflict-free 16-byte row reads
   static constexpr int VTS = BK + 8;   // V^T row stride (elements)
   bf16 k[BK * KST];                    // K tile, one key per row
   bf16 vt[D * VTS];                    // V^T tile, one head-dim column per row, keys in vt_pos order
   // partial tiles (key blocks t even / odd): bit i of hid[.][g][j] says
-  // whether key j hides row 32 g + i of the query block
-  uint32_t hid[2][BQ / 32][BK];
+  // whether key j hides row 32 g + i of the item's NQB query blocks
+  uint32_t hid[2][NQB * BQ / 32][BK];
   uint32_t hdr[2][4];   // headers of this and the next work item
 };
 
@@ -42,22 +42,23 @@ struct alignas(16) FwdSmem {
 // in the P operand of the PV product are 8 neighbouring elements.
 __device__ __forceinline__ int vt_pos(int x) { return (x & ~15) | perm16(x & 15); }
 
-// Global -> register staging of one key block (256 threads).
+// Global -> register staging of one key block (NT threads: 256, or 512 for
+// a pair of query blocks).
 //   K: thread t holds column chunk t % CPR (8 head-dim values) of the NK
 //      consecutive rows NK*(t / CPR) ...  (loads and LDS stores then differ
 //      only by constant offsets);
-//   V: units of 4 consecutive keys x 8 head-dim columns, unit p = t + 256 j
+//   V: units of 4 consecutive keys x 8 head-dim columns, unit p = t + NT j
 //      (j < NV) at key-unit 16 ((p / 64) / (CPR / 4)) + p % 16 and chunk
 //      stage_chunk(p % 64, (p / 64) % (CPR / 4)): the staging map that keeps
 //      the transposed 8-byte LDS stores free of bank conflicts (the 16 lanes
 //      served together write 16 distinct 8-byte places of rows that start on
 //      the same bank).
-template <int D>
+template <int D, int NT = 256>
 struct Stage {
   static constexpr int CPR = D / 8;               // 16-byte chunks per row
-  static constexpr int NK = BK * CPR / 256;       // K rows per thread
-  static constexpr int NV = (BK / 4) * CPR / 256; // V units per thread
-  static_assert(CPR % 4 == 0 && ((BK / 4) * CPR) % 256 == 0, "whole V units per thread");
+  static constexpr int NK = BK * CPR / NT;        // K rows per thread
+  static constexpr int NV = (BK / 4) * CPR / NT;  // V units per thread
+  static_assert(CPR % 4 == 0 && ((BK / 4) * CPR) % NT == 0, "whole V units per thread");
   static_assert(NK == 4 * NV, "a K block and a V block take the same registers");
   // One set of registers holds K of the next block until it is stored, then
   // V of that block: the two are never held at the same time in the loop.
@@ -67,35 +68,35 @@ struct Stage {
   static __device__ __forceinline__ int k_col(unsigned t) { return (int)(t % CPR); }
   // first key and column chunk of V unit j of thread t
   static __device__ __forceinline__ int v_key(unsigned t, int j) {
-    const int p = (int)t + 256 * j;
+    const int p = (int)t + NT * j;
     return 4 * (16 * ((p >> 6) / (CPR / 4)) + stage_row_unit(p & 63));
   }
   static __device__ __forceinline__ int v_col(unsigned t, int j) {
-    const int p = (int)t + 256 * j;
+    const int p = (int)t + NT * j;
     return stage_chunk(p & 63, (p >> 6) % (CPR / 4));
   }
 };
 
-template <int D>
-__device__ __forceinline__ void load_k(Stage<D>& r, BufRsrc kb, int k0, unsigned t) {
-  using S = Stage<D>;
+template <int D, int NT>
+__device__ __forceinline__ void load_k(Stage<D, NT>& r, BufRsrc kb, int k0, unsigned t) {
+  using S = Stage<D, NT>;
   const uint32_t base = opaque(((uint32_t)S::k_row(t) * S::CPR + S::k_col(t)) * 16u) + (uint32_t)k0 * (D * 2);
 #pragma unroll
   for (int i = 0; i < S::NK; ++i) r.x[i] = buf_load16(kb, base + (uint32_t)i * (D * 2));
 }
 
-template <int D>
-__device__ __forceinline__ void store_k(const Stage<D>& r, bf16* sk, unsigned t) {
-  using S = Stage<D>;
+template <int D, int NT>
+__device__ __forceinline__ void store_k(const Stage<D, NT>& r, bf16* sk, unsigned t) {
+  using S = Stage<D, NT>;
   constexpr int KST = FwdSmem<D>::KST;
   bf16* dst = sk + opaque(S::k_row(t) * KST + S::k_col(t) * 8);
 #pragma unroll
   for (int i = 0; i < S::NK; ++i) *reinterpret_cast<bf16x8*>(dst + i * KST) = r.x[i];
 }
 
-template <int D>
-__device__ __forceinline__ void load_v(Stage<D>& r, BufRsrc vb, int k0, unsigned t) {
-  using S = Stage<D>;
+template <int D, int NT>
+__device__ __forceinline__ void load_v(Stage<D, NT>& r, BufRsrc vb, int k0, unsigned t) {
+  using S = Stage<D, NT>;
 #pragma unroll
   for (int j = 0; j < S::NV; ++j) {
     const uint32_t base =
@@ -105,9 +106,9 @@ __device__ __forceinline__ void load_v(Stage<D>& r, BufRsrc vb, int k0, unsigned
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_vt(const Stage<D>& r, bf16* vt, unsigned t) {
-  using S = Stage<D>;
+template <int D, int NT>
+__device__ __forceinline__ void store_vt(const Stage<D, NT>& r, bf16* vt, unsigned t) {
+  using S = Stage<D, NT>;
   constexpr int VTS = FwdSmem<D>::VTS;
   static_assert((8 * VTS * 2) % 128 == 0, "8 transposed rows start on the same bank");
 #pragma unroll
@@ -134,20 +135,33 @@ __device__ __forceinline__ void store_vt(const Stage<D>& r, bf16* vt, unsigned t
 // LDS operands of the S and PV products are read this many products ahead.
 constexpr int kRA = 3;
 
-template <int D, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+//
+// PAIR: an item is a pair of neighbouring query blocks (2qp, 2qp+1) of one
+// head, taken by 8 waves (waves 4 hq .. 4 hq + 3 hold the rows of block
+// 2qp + hq), which walk the pair's union list of key blocks: each key block
+// is loaded and staged in LDS once for both query blocks, and a wave works on
+// it only when its own query block sees it.
+template <int D, bool SPLIT, bool PAIR>
+__global__ __launch_bounds__(PAIR ? 512 : 256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const FwdArgs a) {
+  static_assert(!(SPLIT && PAIR), "pair items are not split");
+  constexpr int NT = PAIR ? 512 : 256;   // threads
+  constexpr int NQB = PAIR ? 2 : 1;      // query blocks per item
   constexpr int NS = D / 16;   // k-steps over the head dimension
   constexpr int ND = D / 32;   // 32-wide blocks of the head dimension
-  constexpr int KST = FwdSmem<D>::KST, VTS = FwdSmem<D>::VTS;
-  __shared__ FwdSmem<D> sm;
+  constexpr int KST = FwdSmem<D, NQB>::KST, VTS = FwdSmem<D, NQB>::VTS;
+  __shared__ FwdSmem<D, NQB> sm;
 
   const unsigned t = threadIdx.x;
   const int lane = (int)(t & 63), w = (int)(t >> 6);
   const int li = lane & 31, hh = lane >> 5;
+  const int hq = PAIR ? (w >> 2) : 0;   // which query block of the item holds this wave's rows
+  const int wr = PAIR ? (w & 3) : w;    // this wave's 32-row group within that block
+  // items per head: query blocks, or pairs of them
+  const int nF = PAIR ? (a.nQ + 1) >> 1 : a.nQ;
   // item count and queue entries are range-checked so that a stale or foreign
   // tileinfo cannot make the kernel read outside its tensors
-  const uint32_t max_items = (uint32_t)((long)a.B * a.H * a.nQ);
+  const uint32_t max_items = (uint32_t)((long)a.B * a.H * nF);
   const uint32_t n_real = min(a.counters[kCtrFwdItems], max_items);
   // the first nsplit items of the queue are taken as two halves each
   const uint32_t nsplit =
@@ -155,8 +169,8 @@ void attn_fwd_kernel(const FwdArgs a) {
   const uint32_t n_items = n_real + nsplit;
   const int Sq = a.Sq, Sk = a.Sk;
 
-  const ItemQueue iq{&a.counters[kCtrFwdNext], a.queue, a.cnt_q, n_items, max_items, a.nQ, a.H, a.Hm, a.nK,
-                     nsplit};
+  const ItemQueue iq{&a.counters[kCtrFwdNext], a.queue, PAIR ? a.cnt_p : a.cnt_q, n_items, max_items, nF, a.H,
+                     a.Hm, a.nK, nsplit};
   if (t == 0) iq.first(sm.hdr[0]);
   __syncthreads();
   for (int n = 0;; ++n) {
@@ -173,23 +187,46 @@ void attn_fwd_kernel(const FwdArgs a) {
     const int cnt = split ? ((idx & 1u) ? cnt_all - half : half) : cnt_all;
     ItemPrefetch pf;
     pf.take(iq, t);
-    const long bh = it / a.nQ;
-    const int qb = (int)(it % a.nQ);
+    const long bh = it / nF;
+    const int ib = (int)(it % nF);            // the item's query block, or pair
+    const int qb0 = PAIR ? 2 * ib : ib;       // its first query block
+    const int qb = qb0 + hq;                  // this wave's query block
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
     const long bhm = (long)b * a.Hm + (a.Hm == 1 ? 0 : h);
+    // the key block list: of the query block (16-bit entries, bit 15 partial),
+    // or of the pair (32-bit entries with the kPair* flags)
     const uint16_t* lst = a.list_q + (bhm * a.nQ + qb) * (long)a.nK + first;
+    const uint32_t* lstp = a.list_p + (bhm * nF + ib) * (long)a.nK;
     // buffer resources over this head's Q, K, V and bounds: loads past the
     // end of the rows return zeros
     const BufRsrc qbase = make_rsrc(a.q + bh * Sq * (long)D, (uint32_t)Sq * D * 2u);
     const BufRsrc kbase = make_rsrc(a.k + bh * Sk * (long)D, (uint32_t)Sk * D * 2u);
     const BufRsrc vbase = make_rsrc(a.v + bh * Sk * (long)D, (uint32_t)Sk * D * 2u);
     const BufRsrc bbase = make_rsrc(a.bounds + bhm * Sk, (uint32_t)Sk * 16u);
-    // key block list entry -> first key, and whether the tile needs the
-    // elementwise interval test (partial, or ragged at the end of the keys)
-    auto block_start = [&](int e) { return min(e & kListIndex, a.nK - 1) * BK; };
-    auto block_masked = [&](int e, int k0) { return (e & kListPartial) || (k0 + BK > Sk); };
+    // key block list entry -> first key, whether the item needs the bounds
+    // of the block (a tile partial, or ragged at the end of the keys), and
+    // whether this wave's block sees it and needs the elementwise interval test
+    auto block_start = [&](int e) { return min(e & (int)(PAIR ? kPairBlock : kListIndex), a.nK - 1) * BK; };
+    auto block_masked = [&](int e, int k0) {
+      return (e & (int)(PAIR ? (kPairPart0 | kPairPart1) : kListPartial)) || (k0 + BK > Sk);
+    };
+    auto wave_sees = [&](int e) { return !PAIR || (e & (int)(hq ? kPairSee1 : kPairSee0)) != 0; };
+    auto wave_masked = [&](int e, int k0) {
+      return PAIR ? ((e & (int)(hq ? kPairPart1 : kPairPart0)) != 0 || (k0 + BK > Sk)) : block_masked(e, k0);
+    };
+    // the hidden-row words of the item's query blocks for a block's bounds
+    // (threads < BK, key t of the block)
+    auto stage_hidden = [&](const int4 breg, int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qq = 0; qq < NQB; ++qq) {
+        uint32_t wd[BQ / 32];
+        hidden_rows(breg, (qb0 + qq) * BQ, wd);
+#pragma unroll
+        for (int g = 0; g < BQ / 32; ++g) sm.hid[buf][qq * (BQ / 32) + g][t] = wd[g];
+      }
+    };
 
-    const int qrow = qb * BQ + 32 * w + li;
+    const int qrow = qb * BQ + 32 * wr + li;
     f32x16 acc[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d)
@@ -203,13 +240,18 @@ void attn_fwd_kernel(const FwdArgs a) {
       // resource (a vector load whose value is the same in every lane).  The
       // first two are scalar loads: waiting for a vector load would also wait
       // for every vector load issued before it.
-      const BufRsrc lbase = make_rsrc(lst, (uint32_t)cnt * 2u);
+      const BufRsrc lbase = PAIR ? make_rsrc(lstp, (uint32_t)cnt * 4u) : make_rsrc(lst, (uint32_t)cnt * 2u);
       auto list_at = [&](int i) -> uint32_t {
+        if constexpr (PAIR) return __builtin_amdgcn_raw_buffer_load_b32(lbase, i * 4, 0, 0);
         return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(lbase, i * 2, 0, 0);
       };
-      Stage<D> st, st_v;   // (st_v: V of the first block only)
-      int e_cur = list_entry(lst, 0);
-      int e_next = cnt > 1 ? list_entry(lst, 1) : 0;
+      auto list_first = [&](int i) -> int {
+        if constexpr (PAIR) return (int)*(const_u32*)(lstp + i);
+        return list_entry(lst, i);
+      };
+      Stage<D, NT> st, st_v;   // (st_v: V of the first block only)
+      int e_cur = list_first(0);
+      int e_next = cnt > 1 ? list_first(1) : 0;
       bf16x8 qf[NS];   // Q rows of this wave (B operand of S^T = K Q^T)
       {
         const int k0 = block_start(e_cur);
@@ -223,12 +265,7 @@ void attn_fwd_kernel(const FwdArgs a) {
         for (int s = 0; s < NS; ++s) qf[s] = buf_load16(qbase, qoff + 32u * s);
         store_k<D>(st, sm.k, t);
         store_vt<D>(st_v, sm.vt, t);
-        if (block_masked(e_cur, k0) && t < BK) {
-          uint32_t wd[BQ / 32];
-          hidden_rows(breg, qb * BQ, wd);
-#pragma unroll
-          for (int g = 0; g < BQ / 32; ++g) sm.hid[0][g][t] = wd[g];
-        }
+        if (block_masked(e_cur, k0) && t < BK) stage_hidden(breg, 0);
       }
       pf.stash(sm.hdr[(n + 1) & 1], t);   // the stores above waited for loads issued after the ticket
       // The Q rows are in registers by now (loaded right after the block's K
@@ -246,7 +283,8 @@ void attn_fwd_kernel(const FwdArgs a) {
       //   bounds_{t+1} -> LDS | barrier | V_{t+1} -> LDS, K_{t+2} -> registers.
       for (int tt = 0;; ++tt) {
         const int k0 = block_start(e_cur);
-        const bool need_mask = block_masked(e_cur, k0);
+        const bool need_mask = wave_masked(e_cur, k0);
+        const bool sees = wave_sees(e_cur);   // (the same in every lane of the wave)
         const bool has_next = tt + 1 < cnt;
         const int k0n = block_start(e_next);
         const bool nm_next = has_next && block_masked(e_next, k0n);
@@ -374,14 +412,16 @@ void attn_fwd_kernel(const FwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
           }
         };
+        // (a wave whose query block does not see the block only stages and
+        // meets the barriers)
         {
           f32x16 s0[2];
-          half_s(0, s0);
+          if (sees) half_s(0, s0);
           __syncthreads();   // V^T of this block is in LDS
-          half_pv(0, s0);
+          if (sees) half_pv(0, s0);
         }
         f32x16 s1[2];
-        half_s(1, s1);
+        if (sees) half_s(1, s1);
         __syncthreads();   // every wave is done with this block's K
         int4 breg = make_int4(0, 0, 0, 0);
         if (has_next) {
@@ -389,18 +429,13 @@ void attn_fwd_kernel(const FwdArgs a) {
           if (nm_next && t < BK) breg = load_bnd(bbase, k0n, Sk, t);
           load_v<D>(st, vbase, k0n, t);
         }
-        half_pv(1, s1);
+        if (sees) half_pv(1, s1);
         // keep the row sum here: left to itself the compiler sinks it past
         // the barrier and keeps the P values alive into the next loads
         asm volatile("" : "+v"(rs));
         l_run += rs;
         // the other mask buffer was last read before the first barrier of block t-1
-        if (nm_next && t < BK) {
-          uint32_t wd[BQ / 32];
-          hidden_rows(breg, qb * BQ, wd);
-#pragma unroll
-          for (int g = 0; g < BQ / 32; ++g) sm.hid[(tt + 1) & 1][g][t] = wd[g];
-        }
+        if (nm_next && t < BK) stage_hidden(breg, (tt + 1) & 1);
 
         // the next item's header, one scalar load in each of the first two blocks
         if (tt == 0) pf.fetch_entry(iq, sm.hdr[(n + 1) & 1]);
@@ -520,14 +555,14 @@ hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t
   const bool split = a.split_cap > 0;
   if (head_dim == 128) {
     if (split)
-      attn_fwd_kernel<128, true><<<grid, 256, 0, stream>>>(a);
+      attn_fwd_kernel<128, true, false><<<grid, 256, 0, stream>>>(a);
     else
-      attn_fwd_kernel<128, false><<<grid, 256, 0, stream>>>(a);
+      attn_fwd_kernel<128, false, false><<<grid, 256, 0, stream>>>(a);
   } else {
     if (split)
-      attn_fwd_kernel<64, true><<<grid, 256, 0, stream>>>(a);
+      attn_fwd_kernel<64, true, false><<<grid, 256, 0, stream>>>(a);
     else
-      attn_fwd_kernel<64, false><<<grid, 256, 0, stream>>>(a);
+      attn_fwd_kernel<64, false, false><<<grid, 256, 0, stream>>>(a);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (a.split_cap > 0 && grid > 0) {
@@ -541,6 +576,17 @@ hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // the end event covers the merge of split items too: it is part of the forward
+  if (ev.end && (err = hipEventRecord(ev.end, stream)) != hipSuccess) return err;
+  return hipSuccess;
+}
+
+int fwd_pair_blocks_per_cu() { return 1; }
+
+hipError_t launch_attn_fwd_pair(const FwdArgs& a, int grid, hipStream_t stream, const KernelEvents& ev) {
+  hipError_t err;
+  if (ev.begin && (err = hipEventRecord(ev.begin, stream)) != hipSuccess) return err;
+  if (grid > 0) attn_fwd_kernel<128, false, true><<<grid, 512, 0, stream>>>(a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ev.end && (err = hipEventRecord(ev.end, stream)) != hipSuccess) return err;
   return hipSuccess;
 }

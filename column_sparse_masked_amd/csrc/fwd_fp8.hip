@@ -132,10 +132,16 @@ void attn_fwd_fp8_kernel(const Fp8FwdArgs a) {
   const int lane = (int)(t & 63), w = (int)(t >> 6);
   const int li = lane & 31, hh = lane >> 5;
   const uint32_t max_items = (uint32_t)((long)a.B * a.H * a.nQ);
-  const uint32_t n_items = min(a.counters[kCtrFwdItems], max_items);
+  // in pair mode the queue holds pairs of query blocks, two tickets each
+  const bool pairs = a.counters[kCtrFwdPairs] == 1u;
+  const int nP = pairs ? (a.nQ + 1) >> 1 : 0;
+  const uint32_t max_entries = (uint32_t)((long)a.B * a.H * (pairs ? nP : a.nQ));
+  const uint32_t n_entries = min(a.counters[kCtrFwdItems], max_entries);
+  const uint32_t n_items = pairs ? 2u * n_entries : n_entries;
   const int Sq = a.Sq, Sk = a.Sk;
 
-  const ItemQueue iq{&a.counters[kCtrFwdNext], a.queue, a.cnt_q, n_items, max_items, a.nQ, a.H, a.Hm, a.nK};
+  const ItemQueue iq{&a.counters[kCtrFwdNext], a.queue, a.cnt_q, n_items, max_items, a.nQ, a.H, a.Hm, a.nK,
+                     0u, nP, max_entries};
   if (t == 0) iq.first(sm.hdr[0]);
   __syncthreads();
   for (int n = 0;; ++n) {
@@ -146,7 +152,9 @@ void attn_fwd_fp8_kernel(const Fp8FwdArgs a) {
     ItemPrefetch pf;
     pf.take(iq, t);
     const long bh = it / a.nQ;
-    const int qb = (int)(it % a.nQ);
+    // (a ticket without an item, count -1, takes block nQ: every row past
+    // the end, so that nothing is written)
+    const int qb = cnt < 0 ? a.nQ : (int)(it % a.nQ);
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
     const long bhm = (long)b * a.Hm + (a.Hm == 1 ? 0 : h);
     const uint16_t* lst = a.list_q + (bhm * a.nQ + qb) * (long)a.nK;

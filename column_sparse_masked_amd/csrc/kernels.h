@@ -19,9 +19,12 @@ struct TileArgs {
   uint32_t* bwd_queue;
   uint32_t* colbase;    // [B*H*nK]: first tile slot of each backward item
   uint32_t* counters;
+  int* cnt_p;           // pair mode: [B*Hm][nP] key blocks either block of pair qp does not skip
+  uint32_t* list_p;     // pair mode: [B*Hm][nP][nK] those blocks with per-block flags
   int B, H, Hm, Sq, Sk, nQ, nK;
   int fwd_slots;   // workgroups of the forward's persistent grid
   int split_cap;   // forward items that may be split (partial-result slots / 2)
+  int pairs;       // forward items are pairs of neighbouring query blocks
 };
 
 struct FwdArgs {
@@ -36,6 +39,8 @@ struct FwdArgs {
   const uint32_t* queue;
   uint32_t* counters;
   float* partials;    // bf16 O [2 split_cap][BQ][D], then fp32 LSE [2 split_cap][BQ]: halves of split items
+  const uint32_t* list_p;   // pair mode: union lists of query-block pairs
+  const int* cnt_p;
   int split_cap;
   int B, H, Hm, Sq, Sk, nQ, nK;
   float scale_log2;   // softmax_scale * log2(e)
@@ -85,6 +90,7 @@ struct BwdArgs {
   const uint32_t* colbase;   // first slot of each backward item
   const uint16_t* cpos;      // [B*Hm][nK][nQ]: position of a tile in its key block's list
   int B, H, Hm, Sq, Sk, nQ, nK;
+  int pairs;          // the forward queue holds pairs of query blocks
   float scale;        // softmax_scale
   float scale_log2;   // softmax_scale * log2(e)
 };
@@ -112,6 +118,8 @@ struct KernelEvents {
 
 hipError_t launch_attn_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream,
                            const KernelEvents& ev);
+// Pair mode (head_dim 128): one workgroup of 8 waves per pair of query blocks.
+hipError_t launch_attn_fwd_pair(const FwdArgs& a, int grid, hipStream_t stream, const KernelEvents& ev);
 hipError_t launch_attn_fwd_fp8(const Fp8FwdArgs& a, int grid, hipStream_t stream, const KernelEvents& ev);
 hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, int grid, int dq_grid,
                            hipStream_t stream, const KernelEvents& ev);
@@ -122,6 +130,7 @@ hipError_t launch_zero16(void* p, size_t bytes, hipStream_t stream);
 
 // Workgroups per compute unit the persistent kernels are sized for.
 int fwd_blocks_per_cu(int head_dim);
+int fwd_pair_blocks_per_cu();
 int bwd_blocks_per_cu(int head_dim);   // the dQ kernel: one workgroup per CU
 
 }  // namespace fm

@@ -473,16 +473,20 @@ __global__ __launch_bounds__(256) void column_kernel(const int4* __restrict__ bo
 // grid (max(nQ, 1), max(B*Hm, 1)), kQueueThreads threads.  Workgroup
 // (qb, bhm): the class of every tile of query block qb (cls) from the key
 // block summaries, and its list of non-skipped key blocks (list_q, cnt_q).
-// The last workgroup to finish (counted on counters[kCtrRowDone], zeroed by
-// the column kernel) then builds, with every count in place, the forward
-// queue (and how many of its items to split), the backward queue, the
-// backward items' first tile slots, and the counters the attention kernels
-// start from.
+// In pair mode the workgroup of the second block of a pair (2qp, 2qp+1), or
+// of a last block without a partner, also lists the key blocks that either
+// block of the pair sees (list_p, cnt_p), classing the first block's tiles
+// again for it.  The last workgroup to finish (counted on
+// counters[kCtrRowDone], zeroed by the column kernel) then builds, with
+// every count in place, the forward queue (of blocks, and how many of them to
+// split; or of pairs), the backward queue, the backward items' first tile
+// slots, and the counters the attention kernels start from.
 __global__ __launch_bounds__(kQueueThreads) void row_kernel(
     const int* __restrict__ kbsum, uint8_t* __restrict__ cls, int* __restrict__ cnt_q,
     const int* __restrict__ cnt_k, uint16_t* __restrict__ list_q, uint32_t* __restrict__ fwd_q,
-    uint32_t* __restrict__ bwd_q, uint32_t* __restrict__ colbase, uint32_t* __restrict__ counters, int B, int H,
-    int Hm, int Sq, int nQ, int nK, int fwd_slots, int split_cap) {
+    uint32_t* __restrict__ bwd_q, uint32_t* __restrict__ colbase, uint32_t* __restrict__ counters,
+    int* __restrict__ cnt_p, uint32_t* __restrict__ list_p, int B, int H, int Hm, int Sq, int nQ, int nK,
+    int fwd_slots, int split_cap, int pairs) {
   __shared__ int hist[2][kBuckets];
   __shared__ uint16_t ccache[2][kCountCache];
   __shared__ uint16_t sorted[2][kCountCache];
@@ -492,30 +496,48 @@ __global__ __launch_bounds__(kQueueThreads) void row_kernel(
   const int t = threadIdx.x;
   const int qb = blockIdx.x;
   const long bhm = blockIdx.y;
+  const int nP = (nQ + 1) >> 1;
   if (qb < nQ && bhm < (long)B * Hm) {
     uint16_t* list = list_q + (bhm * nQ + qb) * (long)nK;
     const int q0 = qb * BQ, q1 = min(Sq, q0 + BQ);
-    int base = 0;
+    // (the same in every thread)
+    const bool unite = pairs && ((qb & 1) || qb == nQ - 1);
+    const bool second = (qb & 1) != 0;
+    const int f0 = (qb - 1) * BQ, f1 = min(Sq, f0 + BQ);   // rows of the pair's first block, when second
+    uint32_t* plist = list_p + (bhm * nP + (qb >> 1)) * (long)nK;
+    int base = 0, ubase = 0;
     for (int o0 = 0; o0 < nK; o0 += kQueueThreads) {
       const int o = o0 + t;
-      int c = 0;
+      int c = 0, cf = 0;   // classes of this block's and (second) the first block's tile
       if (o < nK) {
         int ks[8];
         load_ks(kbsum, bhm * nK + o, ks);
         c = tile_class(ks, q0, q1);
         cls[(bhm * nQ + qb) * (long)nK + o] = (uint8_t)c;
+        if (unite && second) cf = tile_class(ks, f0, f1);
       }
       const bool keep = o < nK && c != 0;
       int at;
       const int n = compact<kQueueThreads>(keep, scratch, base, &at);
       if (keep) list[at] = (uint16_t)(o | (c == 2 ? kListPartial : 0));
       base += n;
+      if (unite) {
+        const int c0 = second ? cf : c, c1 = second ? c : 0;   // blocks 2qp and 2qp+1
+        const bool ukeep = o < nK && (c0 != 0 || c1 != 0);
+        int uat;
+        const int un = compact<kQueueThreads>(ukeep, scratch, ubase, &uat);
+        if (ukeep)
+          plist[uat] = (uint32_t)o | (c0 != 0 ? kPairSee0 : 0u) | (c0 == 2 ? kPairPart0 : 0u) |
+                       (c1 != 0 ? kPairSee1 : 0u) | (c1 == 2 ? kPairPart1 : 0u);
+        ubase += un;
+      }
     }
-    // the row's count as an atomic, performed (the value returned) before
-    // this workgroup is counted as finished
+    // the row's (and pair's) count as an atomic, performed (the value
+    // returned) before this workgroup is counted as finished
     if (t == 0) {
       const int old = atomicExch(&cnt_q[bhm * nQ + qb], base);
-      asm volatile("s_waitcnt vmcnt(0)" ::"v"(old) : "memory");
+      const int oldp = unite ? atomicExch(&cnt_p[bhm * nP + (qb >> 1)], ubase) : 0;
+      asm volatile("s_waitcnt vmcnt(0)" ::"v"(old), "v"(oldp) : "memory");
     }
   }
   // ---- the last workgroup to finish builds the queues ----
@@ -537,15 +559,18 @@ __global__ __launch_bounds__(kQueueThreads) void row_kernel(
     const SplitRule sr{part == 0 && split_cap > 0, split_cap > 0, fwd_slots, split_cap};
     int* sc = scratch + part * (kHalf / 64);
     long* lsc = lscratch + part * (kHalf / 64);
-    // (a forward item's count is at most nK, a backward item's at most nQ)
-    const int nBlk = part == 0 ? nQ : nK, max_cnt = part == 0 ? nK : nQ;
+    // (a forward item's count is at most nK, a backward item's at most nQ;
+    // forward items are query blocks, or in pair mode pairs of them)
+    const int nF = pairs ? nP : nQ;
+    const int* fcnt = pairs ? cnt_p : cnt_q;
+    const int nBlk = part == 0 ? nF : nK, max_cnt = part == 0 ? nK : nQ;
     uint32_t* queue = part == 0 ? fwd_q : bwd_q;
-    const long mq = (long)B * Hm * nQ, mk = (long)B * Hm * nK;
+    const long mq = (long)B * Hm * nF, mk = (long)B * Hm * nK;
     if (mq <= kCountCache && mk <= kCountCache) {   // the same in every thread
       int cq[kCountCache / kQueueThreads], ck[kCountCache / kQueueThreads];
       // range-checked buffer loads (zero past the end): no branch around
       // the loads, which are then in flight together
-      const BufRsrc rq = make_rsrc(cnt_q, (uint32_t)mq * 4u), rk = make_rsrc(cnt_k, (uint32_t)mk * 4u);
+      const BufRsrc rq = make_rsrc(fcnt, (uint32_t)mq * 4u), rk = make_rsrc(cnt_k, (uint32_t)mk * 4u);
 #pragma unroll
       for (int u = 0; u < kCountCache / kQueueThreads; ++u) {
         const uint32_t off = (uint32_t)(u * kQueueThreads + t) * 4u;
@@ -563,14 +588,15 @@ __global__ __launch_bounds__(kQueueThreads) void row_kernel(
       // (the histograms are free again: they hold the running sums)
       tile_slots_lds(ccache[1], colbase, B, H, Hm, nK, &ntiles, scratch, hist[0]);
     } else {
-      sort_items<kHalf>(tp, GlobalCounts{part == 0 ? cnt_q : cnt_k}, queue, B, H, Hm, nBlk, max_cnt, hist[part],
+      sort_items<kHalf>(tp, GlobalCounts{part == 0 ? fcnt : cnt_k}, queue, B, H, Hm, nBlk, max_cnt, hist[part],
                         sc, lsc, sr, &nsplit, nullptr);
       tile_slots(GlobalCounts{cnt_k}, colbase, B, H, Hm, nK, &ntiles, scratch);
     }
   }
   __syncthreads();
   if (t == 0) {
-    counters[kCtrFwdItems] = (uint32_t)((long)B * H * nQ);
+    counters[kCtrFwdItems] = (uint32_t)((long)B * H * (pairs ? nP : nQ));
+    counters[kCtrFwdPairs] = pairs ? 1u : 0u;
     counters[kCtrFwdSplit] = nsplit;
     counters[kCtrFwdNext] = 0;
     counters[kCtrFwdExit] = 0;
@@ -610,8 +636,8 @@ hipError_t launch_tile_bounds(const TileArgs& a, hipStream_t stream) {
   column_kernel<<<dim3((unsigned)(a.nK > 0 ? a.nK : 1), gy), 256, 0, stream>>>(
       a.bounds, a.kbsum, a.cnt_k, a.list_k, a.cpos, a.counters, a.Sq, a.Sk, a.nQ, a.nK, bhm);
   row_kernel<<<dim3((unsigned)(a.nQ > 0 ? a.nQ : 1), gy), kQueueThreads, 0, stream>>>(
-      a.kbsum, a.cls, a.cnt_q, a.cnt_k, a.list_q, a.fwd_queue, a.bwd_queue, a.colbase, a.counters, a.B, a.H,
-      a.Hm, a.Sq, a.nQ, a.nK, a.fwd_slots, a.split_cap);
+      a.kbsum, a.cls, a.cnt_q, a.cnt_k, a.list_q, a.fwd_queue, a.bwd_queue, a.colbase, a.counters, a.cnt_p,
+      a.list_p, a.B, a.H, a.Hm, a.Sq, a.nQ, a.nK, a.fwd_slots, a.split_cap, a.pairs);
   return hipGetLastError();
 }
 

@@ -66,16 +66,24 @@ typedef struct {
   int32_t seqlen_k;       /* Sk >= 0                                            */
   int32_t head_dim;       /* D, 64 or 128                                       */
   float softmax_scale;    /* multiplies q.k before the softmax                  */
+  int32_t fwd_rows;       /* query rows per forward work item: 0 lets the
+                           * library choose; 128 (one query block); 256 (two
+                           * neighbouring query blocks of one head, whose
+                           * workgroup stages each key block once for both;
+                           * head_dim 128 only).  fm_tile_bounds and the
+                           * attention calls on one tileinfo must agree on it. */
 } fm_problem;
 
 /* Byte offsets of the parts of a tileinfo buffer (each 256-byte aligned), as
  * written by fm_tile_bounds.  nQ = ceil(Sq/block_q), nK = ceil(Sk/block_k).
- *   counters  uint32[16]: [0] forward items, [1] backward items,
+ *   counters  uint32[16]: [0] forward items (query-block pairs in pair mode),
+ *             [1] backward items,
  *             [2],[3] forward / backward next-item counters, [4],[5] exit counters,
  *             [6],[7] the dQ kernel's next-item and exit counters,
  *             [8] forward items split in two (the first entries of fwd_queue),
  *             [9] non-skipped tiles over every (batch, head) pair (saturating),
- *             [10] the tile pass's own count of finished workgroups (left at 0)
+ *             [10] the tile pass's own count of finished workgroups (left at 0),
+ *             [11] 1 in pair mode (forward items of two query blocks), else 0
  *   kbsum     int32 [B][Hm][nK][8]  per key block, over its columns j < Sk, the
  *             min and max of each bound clamped to [0, Sq]:
  *             LTS min, LTS max, LTE min, LTE max, UTS min, UTS max, UTE min, UTE max
@@ -85,7 +93,10 @@ typedef struct {
  *   list_q    uint16[B][Hm][nQ][nK] per query block, its non-skipped key blocks in
  *             increasing order (first cnt_q entries), bit 15 set if partial
  *   list_k    uint16[B][Hm][nK][nQ] per key block, its non-skipped query blocks
- *   fwd_queue uint32[B*H*nQ]         forward items (b*H+h)*nQ+qb, most tiles first
+ *   fwd_queue uint32[B*H*nQ]         forward items (b*H+h)*nQ+qb, most tiles first;
+ *             in pair mode the first B*H*nP entries, nP = ceil(nQ/2), are
+ *             pair items (b*H+h)*nP+qp (query blocks 2qp and 2qp+1 < nQ),
+ *             most union tiles (cnt_p) first
  *   bwd_queue uint32[B*H*nK]         backward items (b*H+h)*nK+kb, most tiles first
  *   fwd_partials bf16[2*C][block_q][D] then float[2*C][block_q], C = min(B*H*nQ, 512):
  *             for each split forward item, the output and LSE of each half of
@@ -100,11 +111,17 @@ typedef struct {
  *             sum of cnt_k over the entries before e.  The tiles of item i,
  *             in its list order, take slots colbase[i] .. colbase[i] + cnt - 1
  *             of the backward's tile cache; counters[9] holds the total
- *             (values saturate at 2^32 - 1) */
+ *             (values saturate at 2^32 - 1)
+ *   cnt_p     int32 [B][Hm][nP]     pair mode: key blocks that either query
+ *             block of pair qp does not skip (other modes: not written)
+ *   list_p    uint32[B][Hm][nP][nK] pair mode: those key blocks in increasing
+ *             order (first cnt_p entries): bits 0-15 the block, bit 16 set if
+ *             block 2qp sees it, bit 17 if that tile is partial, bits 18 and
+ *             19 the same for block 2qp+1 */
 typedef struct {
   int32_t block_q, block_k, n_qblocks, n_kblocks;
   size_t counters, kbsum, cls, cnt_q, cnt_k, list_q, list_k, fwd_queue, bwd_queue, fwd_partials;
-  size_t cpos, colbase;
+  size_t cpos, colbase, cnt_p, list_p;
   size_t total;           /* bytes the caller must allocate                     */
 } fm_tileinfo_layout;
 

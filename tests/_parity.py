@@ -25,18 +25,19 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(w, tensors=None, device="cuda", want_bwd=True, both_paths=False):
+def run_gpu(w, tensors=None, device="cuda", want_bwd=True, both_paths=False, fwd_rows=0):
     """Upload a workload, run tile pass + forward (+ backward) on the GPU and
     return numpy results (float64) and the tileinfo dictionary.  The backward
     runs with the tile cache (dQ from the cached dS / scale, as the benchmark
     runs it); with both_paths it runs again without the cache (dQ recomputed)
-    into dq_rc, dk_rc, dv_rc."""
+    into dq_rc, dk_rc, dv_rc.  fwd_rows: query rows per forward item (0: the
+    library's choice; 256: pairs of query blocks)."""
     import torch
     from column_sparse_masked_amd.api import MaskedAttention, to_device_bf16, to_device_bounds
     q, k, v, do = tensors if tensors is not None else w.draw()
     tq, tk, tv, tdo = (to_device_bf16(x, device) for x in (q, k, v, do))
     tb = to_device_bounds(w.bounds, device)
-    att = MaskedAttention.for_workload(w, device)
+    att = MaskedAttention.for_workload(w, device, fwd_rows)
     att.tile_bounds(tb)
     o, lse = att.forward(tq, tk, tv, tb)
     res = {"o": o, "lse": lse}
@@ -91,7 +92,40 @@ def check_full(w, got, tensors, label=""):
     return err_o, errs
 
 
-def check_tileinfo(w, ti):
+def expected_pairs(w, fwd_rows=0):
+    """Whether the library runs the forward on pairs of query blocks: asked
+    for (fwd_rows 256), or with head_dim 128 and at least four pairs per
+    compute unit (the pair kernel's grid), unless fwd_rows is 128."""
+    from column_sparse_masked_amd import _lib
+    if w.D != 128 or fwd_rows == 128:
+        return False
+    if fwd_rows == 256:
+        return True
+    nQ = -(-w.Sq // 128)
+    return w.B * w.H * ((nQ + 1) // 2) >= 4 * _lib.device_cu_count()
+
+
+def pair_lists(cls):
+    """Per pair of query blocks (2qp, 2qp+1 < nQ): the key blocks either one
+    sees, in increasing order, each with the flags: bit 16 block 2qp sees it,
+    bit 17 that tile is partial, bits 18, 19 the same for block 2qp+1."""
+    B, Hm, nQ, nK = cls.shape
+    nP = (nQ + 1) // 2
+    lists = {}
+    cnt = np.zeros((B, Hm, nP), np.int64)
+    for b in range(B):
+        for hm in range(Hm):
+            for qp in range(nP):
+                c0 = cls[b, hm, 2 * qp].astype(np.int64)
+                c1 = cls[b, hm, 2 * qp + 1].astype(np.int64) if 2 * qp + 1 < nQ else np.zeros(nK, np.int64)
+                kbs = np.nonzero((c0 != 0) | (c1 != 0))[0]
+                lists[b, hm, qp] = (kbs | ((c0[kbs] != 0) << 16) | ((c0[kbs] == 2) << 17)
+                                    | ((c1[kbs] != 0) << 18) | ((c1[kbs] == 2) << 19))
+                cnt[b, hm, qp] = kbs.size
+    return lists, cnt
+
+
+def check_tileinfo(w, ti, fwd_rows=0):
     """Bit-exact tile pass against the oracle's classification."""
     kbsum, cls, cq, ck = oracle.classify(w.bounds, w.Sq, 128, 128)
     assert np.array_equal(ti["kbsum"], kbsum), "kbsum differs"
@@ -111,18 +145,28 @@ def check_tileinfo(w, ti):
                 qbs = np.nonzero(col)[0]
                 want = qbs | np.where(col[qbs] == 2, 0x8000, 0)
                 assert np.array_equal(ti["list_k"][b, hm, kb, :qbs.size], want), (b, hm, kb)
+    # pair mode: the union lists of the query-block pairs and their counts
+    pairs = expected_pairs(w, fwd_rows)
+    c = ti["counters"]
+    assert c[11] == (1 if pairs else 0), "pair mode differs"
+    nP = (nQ + 1) // 2
+    if pairs:
+        plists, cp = pair_lists(cls)
+        assert np.array_equal(ti["cnt_p"], cp), "cnt_p differs"
+        for key, want in plists.items():
+            assert np.array_equal(ti["list_p"][key][:want.size].astype(np.int64), want), ("list_p", key)
     # queues: a permutation of every item, tile counts non-increasing
     H = w.H
-    for name, cnt, nb in (("fwd_queue", cq, nQ), ("bwd_queue", ck, nK)):
-        qu = ti[name].astype(np.int64)
+    fwd = ("fwd_queue", cp, nP) if pairs else ("fwd_queue", cq, nQ)
+    for name, cnt, nb in (fwd, ("bwd_queue", ck, nK)):
+        qu = ti[name][:B * H * nb].astype(np.int64)
         assert np.array_equal(np.sort(qu), np.arange(B * H * nb)), name
         bh, blk = qu // nb, qu % nb
         b_, h_ = bh // H, bh % H
         cost = cnt[b_, 0 if Hm == 1 else h_, blk]
         assert np.all(np.diff(np.minimum(cost, 4095)) <= 0), f"{name} not sorted by tile count"
-    c = ti["counters"]
-    assert c[0] == B * H * nQ and c[1] == B * H * nK and c[2] == 0 and c[3] == 0
-    assert c[8] == expected_split_count(cq, H, Hm), "number of split forward items differs"
+    assert c[0] == B * H * (nP if pairs else nQ) and c[1] == B * H * nK and c[2] == 0 and c[3] == 0
+    assert c[8] == (0 if pairs else expected_split_count(cq, H, Hm)), "number of split forward items differs"
     # the backward's tile slots: each listed tile's position in its key
     # block's list, and each backward item's first slot.  Slots go to the
     # (b, mask head, key block) entries in order, and within an entry to the
@@ -231,12 +275,12 @@ def fp8_head_check(qd, kd, vd, bounds_h, scale, rows, go, gl):
     return num, den, lse_err, worst
 
 
-def run_gpu_fp8(w, codes, descale, device="cuda"):
+def run_gpu_fp8(w, codes, descale, device="cuda", fwd_rows=0):
     import torch
     from column_sparse_masked_amd.api import MaskedAttention, to_device_bounds, to_device_u8
     tq, tk, tv = (to_device_u8(c, device) for c in codes)
     tb = to_device_bounds(w.bounds, device)
-    att = MaskedAttention.for_workload(w, device)
+    att = MaskedAttention.for_workload(w, device, fwd_rows)
     att.tile_bounds(tb)
     o, lse = att.forward_fp8(tq, tk, tv, descale, tb)
     torch.cuda.synchronize()

@@ -29,6 +29,7 @@ static fm_problem prob(int32_t b, int32_t h, int32_t hm, int32_t sq, int32_t sk,
   fm_problem p;
   p.batch = b; p.heads = h; p.mask_heads = hm; p.seqlen_q = sq; p.seqlen_k = sk; p.head_dim = d;
   p.softmax_scale = scale;
+  p.fwd_rows = 0;
   return p;
 }
 

@@ -29,8 +29,8 @@ def test_every_declared_function_is_exported():
 
 
 def test_struct_sizes_match_header():
-    assert ctypes.sizeof(L.Problem) == 28
-    assert ctypes.sizeof(L.TileinfoLayout) == 16 + 13 * 8
+    assert ctypes.sizeof(L.Problem) == 32
+    assert ctypes.sizeof(L.TileinfoLayout) == 16 + 15 * 8
 
 
 def _p(**kw):
@@ -53,6 +53,9 @@ def _p(**kw):
     (dict(softmax_scale=float("nan")), L.FM_ERR_UNSUPPORTED),
     (dict(softmax_scale=float("inf")), L.FM_ERR_UNSUPPORTED),
     (dict(batch=65536, heads=1024, seqlen_q=4096), L.FM_ERR_SHAPE),
+    (dict(fwd_rows=64), L.FM_ERR_UNSUPPORTED),
+    (dict(fwd_rows=-1), L.FM_ERR_UNSUPPORTED),
+    (dict(fwd_rows=256, head_dim=64), L.FM_ERR_UNSUPPORTED),
 ])
 def test_bad_problems_rejected_everywhere(kw, code):
     p = _p(**kw)

@@ -61,6 +61,19 @@ def test_fp8_small_problem_parity(name):
     check_fp8(w, go, gl, (q8, k8, v8), ds, label=name)
 
 
+@pytest.mark.parametrize("name", ["sliding_ragged_S1000", "causal_docs_S1300", "tiny_S17", "share_question_S1500"])
+def test_fp8_pair_mode_parity(name):
+    """A tileinfo built for pairs of query blocks (fwd_rows 256): the fp8
+    forward takes two tickets per queue entry, one per query block, and none
+    for the missing second block of an odd last pair."""
+    w = CASES[name]()
+    say(f"[fp8 pairs] {name}: B={w.B} H={w.H} Hm={w.Hm} Sq={w.Sq} Sk={w.Sk}")
+    q8, k8, v8, ds = M.fp8_inputs(w.draw())
+    go, gl, att = run_gpu_fp8(w, (q8, k8, v8), ds, fwd_rows=256)
+    check_tileinfo(w, att.read_tileinfo(), 256)
+    check_fp8(w, go, gl, (q8, k8, v8), ds, label=name + " (pairs)")
+
+
 def test_fp8_empty_key_set():
     w = M.custom(np.zeros((0, 4), np.int32), B=1, H=2, Sq=200, D=128, seed=62)
     say("[fp8] empty key set")

@@ -98,6 +98,30 @@ def test_small_problem_parity(name):
     check_full(w, got, tensors, name)
 
 
+# head_dim 128 cases run again with the forward on pairs of query blocks
+# (odd block counts: prefix_document, document_bidir, everything_masked,
+# extreme_int32, single_row)
+PAIR_CASES = ["sliding_ragged_S1000_D128", "share_question_S1500", "prefix_document_S1300",
+              "cp_share_S2048_w4_r1", "document_bidir_S1100_D128", "global_sliding_S1200_g70_w150",
+              "random_shared_Sq200_Sk900_D128", "unmasked_S700_D128", "everything_masked_S260",
+              "single_row_S1_D128", "extreme_int32_bounds", "split_unmasked_S4000_D128",
+              "split_masked_rows_S3000"]
+
+
+@pytest.mark.parametrize("name", PAIR_CASES)
+def test_pair_mode_parity(name):
+    """fwd_rows 256: the forward's items are pairs of neighbouring query
+    blocks walking their union list (a wave works on a key block only when
+    its own block sees it), and the backward's dQ kernels take the pair
+    queue's two query blocks per entry."""
+    w = CASES[name]()
+    assert w.D == 128
+    say(f"[pairs] {name}: B={w.B} H={w.H} Hm={w.Hm} Sq={w.Sq} Sk={w.Sk}")
+    got, tensors = run_gpu(w, both_paths=True, fwd_rows=256)
+    check_tileinfo(w, got["tileinfo"], 256)
+    check_full(w, got, tensors, name + " (pairs)")
+
+
 def _scaled_bf16(bits, mult):
     """bf16 bits times a power of two (exact: only the exponent changes)."""
     return M.bf16_bits(M.bf16_to_f32(bits) * np.float32(mult))
@@ -148,8 +172,10 @@ def _o_bound_large_logits(w, q, k, v, lse_ref):
     return out
 
 
-@pytest.mark.parametrize("name", list(LARGE_LOGIT_CASES))
-def test_large_logit_parity(name):
+@pytest.mark.parametrize("name,fwd_rows", [(n, 0) for n in LARGE_LOGIT_CASES]
+                         + [("large_logits_split_unmasked_S3000_D128", 256),
+                            ("large_logits_sliding_S1300_D128", 256)])
+def test_large_logit_parity(name, fwd_rows):
     """Scores far from N(0, 1): Q multiplied by 8 or 16, and the K rows of
     spike columns (every 97th key of the second half of the keys) by a
     further 2 or 4, so that LSE / scale runs into the hundreds or thousands
@@ -169,12 +195,12 @@ def test_large_logit_parity(name):
     spikes = spikes[spikes % 97 == 0]
     k = k.copy()
     k[:, :, spikes] = _scaled_bf16(k[:, :, spikes], km)
-    say(f"[parity] {name}: Q x{qm}, K x{km} on {spikes.size} spike columns")
+    say(f"[parity] {name}: Q x{qm}, K x{km} on {spikes.size} spike columns, fwd_rows {fwd_rows}")
     up = oracle.upcast_bf16
     ro, rl, rdq, rdk, rdv = oracle.attention(up(q), up(k), up(v), up(do), w.bounds, w.scale)
     fin = np.isfinite(rl)
     assert np.abs(rl[fin]).max() / w.scale > 200, "the case does not reach large logits"
-    got, _ = run_gpu(w, (q, k, v, do), both_paths=True)
+    got, _ = run_gpu(w, (q, k, v, do), both_paths=True, fwd_rows=fwd_rows)
     bound = _o_bound_large_logits(w, q, k, v, rl) + 2.0 ** -8 * np.abs(ro) + 1e-4 * np.abs(up(v)).max()
     err = np.abs(got["o"] - ro)
     ratio = float((err / bound).max())

@@ -44,41 +44,49 @@ def _random_problem(rng):
 
 
 def test_tile_pass_fuzz():
+    """Also in pair mode (head_dim 128 with fwd_rows 256: union lists of the
+    query-block pairs and a queue of pairs), on a third of the problems."""
     import torch
     from column_sparse_masked_amd.api import MaskedAttention, to_device_bounds
     rng = np.random.default_rng(2024)
+    rng_mode = np.random.default_rng(77)
     n = 300
     for i in range(n):
         w = _random_problem(rng)
-        att = MaskedAttention.for_workload(w)
+        fwd_rows = 256 if rng_mode.random() < 1 / 3 else 0
+        if fwd_rows:
+            w.D = 128
+        att = MaskedAttention.for_workload(w, fwd_rows=fwd_rows)
         att.buf.tileinfo.fill_(0xA5)          # garbage from a previous user
         att.tile_bounds(to_device_bounds(w.bounds))
         torch.cuda.synchronize()
         try:
-            check_tileinfo(w, att.read_tileinfo())
+            check_tileinfo(w, att.read_tileinfo(), fwd_rows)
         except AssertionError as e:
-            raise AssertionError(f"problem {i}: B={w.B} H={w.H} Hm={w.Hm} Sq={w.Sq} Sk={w.Sk}: {e}") from e
+            raise AssertionError(f"problem {i}: B={w.B} H={w.H} Hm={w.Hm} Sq={w.Sq} Sk={w.Sk} "
+                                 f"fwd_rows={fwd_rows}: {e}") from e
         if i % 50 == 0:
             say(f"[fuzz] {i} problems bit-exact (last: B={w.B} H={w.H} Hm={w.Hm} Sq={w.Sq} Sk={w.Sk})")
     say(f"[fuzz] {n} problems bit-exact")
 
 
-@pytest.mark.parametrize("B,H,Hm,Sq,Sk", [(2, 24, 24, 13000, 9000),    # 4896 forward entries
-                                          (48, 2, 1, 9000, 13000),     # 4896 backward entries
-                                          (1, 40, 40, 16384, 16384)])  # 5120 of each
-def test_tile_pass_many_entries(B, H, Hm, Sq, Sk):
+@pytest.mark.parametrize("B,H,Hm,Sq,Sk,fwd_rows", [(2, 24, 24, 13000, 9000, 0),    # 4896 forward entries
+                                                   (48, 2, 1, 9000, 13000, 0),     # 4896 backward entries
+                                                   (1, 40, 40, 16384, 16384, 0),   # 5120 of each
+                                                   (2, 40, 40, 26000, 9000, 256)])  # 8160 pair entries
+def test_tile_pass_many_entries(B, H, Hm, Sq, Sk, fwd_rows):
     """More (batch, mask head, block) entries than the sort keeps in LDS: the
     last workgroup reads the counts from global memory instead."""
     import torch
     from column_sparse_masked_amd.api import MaskedAttention, to_device_bounds
     rng = np.random.default_rng(B * 1000 + H)
     b = rng.integers(-50, Sq + 50, size=(B, Hm, Sk, 4))
-    w = M.custom(None, B=B, H=H, Sq=Sq, D=64, seed=0,
+    w = M.custom(None, B=B, H=H, Sq=Sq, D=128 if fwd_rows else 64, seed=0,
                  per_head_bounds=np.ascontiguousarray(b, dtype=np.int64).astype(np.int32))
     assert w.Sk == Sk
-    say(f"[many entries] B={B} H={H} Hm={Hm} Sq={Sq} Sk={Sk}")
-    att = MaskedAttention.for_workload(w)
+    say(f"[many entries] B={B} H={H} Hm={Hm} Sq={Sq} Sk={Sk} fwd_rows={fwd_rows}")
+    att = MaskedAttention.for_workload(w, fwd_rows=fwd_rows)
     att.buf.tileinfo.fill_(0xA5)
     att.tile_bounds(to_device_bounds(w.bounds))
     torch.cuda.synchronize()
-    check_tileinfo(w, att.read_tileinfo())
+    check_tileinfo(w, att.read_tileinfo(), fwd_rows)
