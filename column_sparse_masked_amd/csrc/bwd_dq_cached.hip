@@ -176,12 +176,20 @@ void attn_bwd_dq_cached_kernel(const BwdArgs a) {
   const int li = lane & 31, hh = lane >> 5;
   const uint32_t max_items = (uint32_t)((long)a.B * a.H * a.nQ);
   // one workgroup per queue entry, or in pair mode two per entry (a pair of
-  // query blocks; the second of a last block without a partner has nothing to do)
+  // query blocks; the second of a last block without a partner has nothing
+  // to do).  With a shared mask the queue holds the H heads of a pair next
+  // to each other; workgroups x .. x + 2H - 1 take their second blocks, then
+  // their first blocks, so that workgroup x + H (and x) works on head x % H
+  // as in the order of single query blocks: neighbouring workgroups go to
+  // different dies, and each die then sees the blocks of a few heads in turn.
   uint32_t it;
   if (a.pairs) {
     const uint32_t nP = (uint32_t)(a.nQ + 1) >> 1;
-    const uint32_t raw = min(*(const_u32*)(a.queue_q + (blockIdx.x >> 1)), (uint32_t)((long)a.B * a.H * nP) - 1u);
-    const uint32_t pbh = raw / nP, blk = 2 * (raw - pbh * nP) + (blockIdx.x & 1u);
+    const uint32_t G = a.Hm == 1 ? (uint32_t)a.H : 1u;
+    const uint32_t grp = blockIdx.x / (2 * G), r = blockIdx.x - grp * 2 * G;
+    const uint32_t entry = grp * G + (r % G), second = r < G ? 1u : 0u;
+    const uint32_t raw = min(*(const_u32*)(a.queue_q + entry), (uint32_t)((long)a.B * a.H * nP) - 1u);
+    const uint32_t pbh = raw / nP, blk = 2 * (raw - pbh * nP) + second;
     if (blk >= (uint32_t)a.nQ) return;
     it = pbh * (uint32_t)a.nQ + blk;
   } else {

@@ -25,12 +25,12 @@
 
 namespace fm {
 
-template <int D, int NQB = 1>
+template <int D, int NQB = 1, int NBUF = 1>
 struct alignas(16) FwdSmem {
   static constexpr int KST = D + 8;    // K row stride (elements): conflict-free 16-byte row reads
   static constexpr int VTS = BK + 8;   // V^T row stride (elements)
-  bf16 k[BK * KST];                    // K tile, one key per row
-  bf16 vt[D * VTS];                    // V^T tile, one head-dim column per row, keys in vt_pos order
+  bf16 k[NBUF][BK * KST];              // K tiles, one key per row
+  bf16 vt[NBUF][D * VTS];              // V^T tiles, one head-dim column per row, keys in vt_pos order
   // partial tiles (key blocks t even / odd): bit i of hid[.][g][j] says
   // whether key j hides row 32 g + i of the item's NQB query blocks
   uint32_t hid[2][NQB * BQ / 32][BK];
@@ -149,8 +149,9 @@ void attn_fwd_kernel(const FwdArgs a) {
   constexpr int NQB = PAIR ? 2 : 1;      // query blocks per item
   constexpr int NS = D / 16;   // k-steps over the head dimension
   constexpr int ND = D / 32;   // 32-wide blocks of the head dimension
-  constexpr int KST = FwdSmem<D, NQB>::KST, VTS = FwdSmem<D, NQB>::VTS;
-  __shared__ FwdSmem<D, NQB> sm;
+  constexpr int NBUF = PAIR ? 2 : 1;     // K and V^T tiles in LDS (pairs: double-buffered)
+  constexpr int KST = FwdSmem<D, NQB, NBUF>::KST, VTS = FwdSmem<D, NQB, NBUF>::VTS;
+  __shared__ FwdSmem<D, NQB, NBUF> sm;
 
   const unsigned t = threadIdx.x;
   const int lane = (int)(t & 63), w = (int)(t >> 6);
@@ -263,8 +264,8 @@ void attn_fwd_kernel(const FwdArgs a) {
         const uint32_t qoff = ((uint32_t)qrow * D + 8u * hh) * 2u;
 #pragma unroll
         for (int s = 0; s < NS; ++s) qf[s] = buf_load16(qbase, qoff + 32u * s);
-        store_k<D>(st, sm.k, t);
-        store_vt<D>(st_v, sm.vt, t);
+        store_k<D>(st, sm.k[0], t);
+        store_vt<D>(st_v, sm.vt[0], t);
         if (block_masked(e_cur, k0) && t < BK) stage_hidden(breg, 0);
       }
       pf.stash(sm.hdr[(n + 1) & 1], t);   // the stores above waited for loads issued after the ticket
@@ -273,7 +274,12 @@ void attn_fwd_kernel(const FwdArgs a) {
       // keeps the compiler from waiting for the loads of later key blocks,
       // issued after Q, before the S products of every block.
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      if (cnt > 1) load_k<D>(st, kbase, block_start(e_next), t);
+      int4 bnext = make_int4(0, 0, 0, 0);   // (pairs) bounds of the next block, loaded a block ahead
+      if (cnt > 1) {
+        load_k<D>(st, kbase, block_start(e_next), t);
+        if (PAIR && block_masked(e_next, block_start(e_next)) && t < BK)
+          bnext = load_bnd(bbase, block_start(e_next), Sk, t);
+      }
       __syncthreads();
 
       // Per key block t (K_t, bounds_t in LDS; V^T_t being stored, K_{t+1}
@@ -302,6 +308,9 @@ void attn_fwd_kernel(const FwdArgs a) {
         // before the first half's PV (barrier 0); K is free once the second
         // half's S is done (barrier 1); V^T once its PV is done (barrier 2).
         float rs = 0.f;   // row sum of this block's P
+        const int buf = PAIR ? (tt & 1) : 0;   // the block's K and V^T tiles
+        const bf16* kcur = sm.k[buf];
+        const bf16* vcur = sm.vt[buf];
         auto half_s = [&](int hk, f32x16 (&s)[2]) __attribute__((always_inline)) {
           // ---- S^T = K Q^T : lane holds query column li, keys 32*jb + 8r + 4hh + q ----
 #pragma unroll
@@ -316,7 +325,7 @@ void attn_fwd_kernel(const FwdArgs a) {
           constexpr int NP = 2 * NS;
           bf16x8 ka[NP];
           auto read_k = [&](int i) __attribute__((always_inline)) {
-            ka[i] = as_bf16x8(&sm.k[(32 * (2 * hk + (i & 1)) + li) * KST + 16 * (i >> 1) + 8 * hh]);
+            ka[i] = as_bf16x8(&kcur[(32 * (2 * hk + (i & 1)) + li) * KST + 16 * (i >> 1) + 8 * hh]);
           };
 #pragma unroll
           for (int i = 0; i < kRA; ++i) read_k(i);
@@ -375,7 +384,7 @@ void attn_fwd_kernel(const FwdArgs a) {
           bf16x8 va[NP];
           auto read_v = [&](int i) __attribute__((always_inline)) {
             const int j = i / (2 * ND), t2 = (i / ND) & 1, d = i % ND;
-            va[i] = as_bf16x8(&sm.vt[(32 * d + li) * VTS + 32 * (2 * hk + j) + 16 * t2 + 8 * hh]);
+            va[i] = as_bf16x8(&vcur[(32 * d + li) * VTS + 32 * (2 * hk + j) + 16 * t2 + 8 * hh]);
           };
 #pragma unroll
           for (int i = 0; i < kRA; ++i) read_v(i);
@@ -412,6 +421,47 @@ void attn_fwd_kernel(const FwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
           }
         };
+        if constexpr (PAIR) {
+          // Double-buffered: block t+1 goes into the other buffers while
+          // block t computes, one barrier per block.  The buffers of block
+          // t+1 held block t-1, which every wave finished before the last
+          // barrier.  One set of registers carries K_{t+1} (loaded in the
+          // middle of block t-1), then V_{t+1}, then K_{t+2}.
+          if (has_next) {
+            store_k<D>(st, sm.k[buf ^ 1], t);
+            load_v<D>(st, vbase, k0n, t);
+          }
+          // (a wave whose query block does not see the block only stages
+          // and meets the barrier)
+          {
+            f32x16 s0[2];
+            if (sees) half_s(0, s0);
+            if (sees) half_pv(0, s0);
+          }
+          f32x16 s1[2];
+          if (sees) half_s(1, s1);
+          if (has_next) {
+            store_vt<D>(st, sm.vt[buf ^ 1], t);
+            if (nm_next && t < BK) stage_hidden(bnext, buf ^ 1);
+          }
+          // read on every path (see below); block t+2's K and bounds
+          const int e2 = __builtin_amdgcn_readfirstlane(e2_pending);
+          if (tt + 2 < cnt) {
+            const int k02 = block_start(e2);
+            load_k<D>(st, kbase, k02, t);
+            if (block_masked(e2, k02) && t < BK) bnext = load_bnd(bbase, k02, Sk, t);
+          }
+          if (sees) half_pv(1, s1);
+          asm volatile("" : "+v"(rs));
+          l_run += rs;
+          // the next item's header, one scalar load in each of the first two blocks
+          if (tt == 0) pf.fetch_entry(iq, sm.hdr[(n + 1) & 1]);
+          if (tt == 1) pf.fetch_count(iq);
+          __syncthreads();   // block t+1 is staged; every wave is done with block t's buffers
+          if (!has_next) break;
+          e_cur = e_next;
+          e_next = e2;
+        } else {
         // (a wave whose query block does not see the block only stages and
         // meets the barriers)
         {
@@ -425,7 +475,7 @@ void attn_fwd_kernel(const FwdArgs a) {
         __syncthreads();   // every wave is done with this block's K
         int4 breg = make_int4(0, 0, 0, 0);
         if (has_next) {
-          store_k<D>(st, sm.k, t);
+          store_k<D>(st, sm.k[0], t);
           if (nm_next && t < BK) breg = load_bnd(bbase, k0n, Sk, t);
           load_v<D>(st, vbase, k0n, t);
         }
@@ -446,10 +496,11 @@ void attn_fwd_kernel(const FwdArgs a) {
         // every load, the next K block's included, at the top)
         const int e2 = __builtin_amdgcn_readfirstlane(e2_pending);
         if (!has_next) break;
-        store_vt<D>(st, sm.vt, t);
+        store_vt<D>(st, sm.vt[0], t);
         if (tt + 2 < cnt) load_k<D>(st, kbase, block_start(e2), t);
         e_cur = e_next;
         e_next = e2;
+        }
       }
       if (cnt == 1) pf.fetch_count(iq);
       pf.publish(iq, sm.hdr[(n + 1) & 1], t);
