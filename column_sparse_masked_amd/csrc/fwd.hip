@@ -133,7 +133,7 @@ __device__ __forceinline__ void store_vt(const Stage<D, NT>& r, bf16* vt, unsign
 // when the problem has enough items per workgroup for the longest-first
 // order to balance the grid; its code has none of the split handling).
 // LDS operands of the S and PV products are read this many products ahead.
-constexpr int kRA = 3;
+constexpr int kRASingle = 3, kRAPair = 4;
 
 //
 // PAIR: an item is a pair of neighbouring query blocks (2qp, 2qp+1) of one
@@ -149,6 +149,7 @@ void attn_fwd_kernel(const FwdArgs a) {
   constexpr int NQB = PAIR ? 2 : 1;      // query blocks per item
   constexpr int NS = D / 16;   // k-steps over the head dimension
   constexpr int ND = D / 32;   // 32-wide blocks of the head dimension
+  constexpr int kRA = PAIR ? kRAPair : kRASingle;
   constexpr int NBUF = PAIR ? 2 : 1;     // K and V^T tiles in LDS (pairs: double-buffered)
   constexpr int KST = FwdSmem<D, NQB, NBUF>::KST, VTS = FwdSmem<D, NQB, NBUF>::VTS;
   __shared__ FwdSmem<D, NQB, NBUF> sm;
