@@ -234,7 +234,8 @@ def test_empty_problem_zeroes_counters():
     att.buf.tileinfo.fill_(0xFF)
     att.tile_bounds(to_device_bounds(w.bounds))
     torch.cuda.synchronize()
-    assert att.read_tileinfo()["counters"].tolist() == [0] * 11 + [0xFFFFFFFF] * 5
+    # counters 0 .. 11 are the tile pass's (11: pair mode); 12 .. 15 are not written
+    assert att.read_tileinfo()["counters"].tolist() == [0] * 12 + [0xFFFFFFFF] * 4
 
 
 def test_empty_query_set():
