@@ -21,8 +21,10 @@
 // and the cache holds 4 rows per key: each tile's K (units of 4 keys x 8
 // columns) and dS (units of 4 keys x 4 rows) are loaded into registers and
 // stored transposed into LDS by maps free of bank conflicts, so every
-// operand is one 16-byte LDS read.  The loads run two tiles ahead of the
-// products.
+// operand is one 16-byte LDS read.  Every K load instruction of a wave
+// covers whole cache lines (8 lanes per 128 bytes): 16-byte loads that each
+// touch half a line keep the address unit busy longer.  The loads run two
+// tiles ahead of the products.
 // The cache is addressed by slot: the tiles of a key block's backward item
 // take consecutive slots from colbase[item] in its list order, so the slot
 // of tile (qb, kb) is colbase[(b H + h) nK + kb] + cpos[kb][qb]; a table of
@@ -41,30 +43,36 @@ template <int D>
 struct CqSmem {
   static constexpr int ST = BK + 8;    // row stride (elements) of both transposed tiles
   static_assert((8 * ST * 2) % 128 == 0, "8 transposed rows start on the same bank");
-  bf16 kt[D * ST];     // K^T: one head-dim column per row, keys in natural order
+  static_assert(ST * 2 % 128 == 16, "neighbouring transposed rows 16 bytes apart in the bank period");
+  bf16 kt[D * ST];     // K^T: one head-dim column per row, keys in groups of 8 swizzled (kt_key)
   bf16 ds[BQ * ST];    // dS: one query row per row, keys in natural order
   uint32_t slot[kTab];   // cache slot of table entry i
   uint32_t key0[kTab];   // first key of its key block
 };
 
-// Global -> register staging of a tile of BK keys x COLS values (K: COLS = D
-// head-dim columns; the cached dS^T: COLS = BQ query rows), 256 threads:
-// units of 4 keys x 8 columns by the staging map (stage_row_unit,
-// stage_chunk), which keeps the transposed 8-byte LDS stores free of bank
-// conflicts.
+// Place of key x of head-dim column c in the K^T tile: groups of 8 keys are
+// swizzled by the column's 16-byte chunk (c / 8), so that the 8 chunks one
+// load instruction brings for a key land in 8 different bank slots.
+__device__ __forceinline__ int kt_key(int c, int x) { return x ^ (8 * ((c >> 3) & 7)); }
+
+// Global -> register staging of a tile of BK keys x COLS head-dim columns of
+// K, 256 threads, in units of 4 keys x 8 columns (one 16-byte chunk of 4
+// neighbouring keys).  Unit p = t + 256 j of the tile: within its group of
+// 64, lane bits 0-2 pick the chunk and bits 3-5 the key unit, so the 4 load
+// instructions (one per key of the unit) each cover 8 whole 128-byte lines.
 template <int COLS>
 struct TileStage {
   static constexpr int CPR = COLS / 8;                       // 16-byte chunks per key
   static constexpr int NU = (BK / 4) * CPR / kCqThreads;     // units per thread
-  static_assert(NU >= 1 && ((BK / 4) * CPR) % kCqThreads == 0 && CPR % 4 == 0, "whole units per thread");
+  static_assert(NU >= 1 && ((BK / 4) * CPR) % kCqThreads == 0 && CPR % 8 == 0, "whole units per thread");
   bf16x8 v[NU][4];
   static __device__ __forceinline__ int key(unsigned t, int j) {
     const int p = (int)t + kCqThreads * j;
-    return 4 * (16 * ((p >> 6) / (CPR / 4)) + stage_row_unit(p & 63));
+    return 4 * (8 * ((p >> 6) / (CPR / 8)) + ((p >> 3) & 7));
   }
   static __device__ __forceinline__ int col(unsigned t, int j) {
     const int p = (int)t + kCqThreads * j;
-    return stage_chunk(p & 63, (p >> 6) % (CPR / 4));
+    return 8 * ((p >> 6) % (CPR / 8)) + (p & 7);
   }
 };
 
@@ -81,13 +89,16 @@ __device__ __forceinline__ void tile_load(TileStage<COLS>& r, BufRsrc src, int k
   }
 }
 
-// transposed into LDS: column c of key k goes to dst[c * ST + k]
+// transposed into LDS: column c of key k goes to dst[c * ST + kt_key(c, k)]
+// (the 8 columns of a chunk share the swizzle; 16 lanes served together hit
+// 8 chunks x 2 key units, 16 different 8-byte slots of a 128-byte period)
 template <int COLS, int ST>
 __device__ __forceinline__ void tile_store_t(const TileStage<COLS>& r, bf16* dst, unsigned t, int salt) {
   using S = TileStage<COLS>;
 #pragma unroll
   for (int j = 0; j < S::NU; ++j) {
-    bf16* tp = dst + opaque((8 * S::col(t, j)) * ST + S::key(t, j), salt);
+    const int c0 = 8 * S::col(t, j);
+    bf16* tp = dst + opaque(c0 * ST + kt_key(c0, S::key(t, j)), salt);
     const bf16x16 p01 = __builtin_shufflevector(r.v[j][0], r.v[j][1], 0, 8, 1, 9, 2, 10, 3, 11,
                                                 4, 12, 5, 13, 6, 14, 7, 15);
     const bf16x16 p23 = __builtin_shufflevector(r.v[j][2], r.v[j][3], 0, 8, 1, 9, 2, 10, 3, 11,
@@ -108,7 +119,9 @@ constexpr int kCqRA = 3;           // products whose LDS operands are read ahead
 // u = t + 256 i (i < 4), i.e. (c2, m, g, rr) = u / 64 and, within it, hh =
 // (u / 8) % 2 and key group j = u % 8: keys 32 g + 4 j .. +4, rows
 // 64 c2 + 32 m + 8 rr + 4 hh + q (q = 0..3), 32 contiguous bytes of the
-// cache (the 8-byte runs of 4 neighbouring lanes of one block).
+// cache (the 8-byte runs of 4 neighbouring lanes of one block).  (These
+// loads touch half lines: the runs of a 4-key unit are contiguous in the
+// order the dK/dV kernel stores them, and a lane loads at most 16 bytes.)
 struct DsStage {
   static constexpr int NU = BQ * BK / 16 / kCqThreads;   // 4-row x 4-key units per thread
   bf16x8 v[NU][2];   // keys 4 j, 4 j + 1 | keys 4 j + 2, 4 j + 3 (4 rows each)
@@ -120,7 +133,7 @@ struct DsStage {
   }
   // first row and first key of the unit
   static __device__ __forceinline__ int row(unsigned t, int i) {
-    const int u = unit(t, i), blk = u >> 4;   // blk = ((c2 * 2 + m) * 4 + g) * 4 + rr
+    const int u = unit(t, i), blk = u >> 4;
     return 64 * (blk >> 5) + 32 * ((blk >> 4) & 1) + 8 * (blk & 3) + 4 * ((u >> 3) & 1);
   }
   static __device__ __forceinline__ int key(unsigned t, int i) {
@@ -252,10 +265,17 @@ void attn_bwd_dq_cached_kernel(const BwdArgs a) {
       const bf16* drow = sm.ds + (32 * w + li) * ST + 8 * hh;
       constexpr int NP = kKSteps * ND;
       bf16x8 av[NP], bv[kKSteps];
+      // K^T operand of (kk, d): keys (16 kk + 8 hh) ^ 8 s = 16 kk ^ y[d] of
+      // column 32 d + li, s its chunk's swizzle (kt_key); y[d] is rebuilt per
+      // tile so that the 32 addresses are not all kept across the loop
+      uint32_t y[ND];
+#pragma unroll
+      for (int d = 0; d < ND; ++d) y[d] = opaque((uint32_t)(8 * hh) ^ (uint32_t)(8 * ((4 * d + (li >> 3)) & 7)), i);
+      const bf16* ktl = sm.kt + li * ST;
       auto read_ops = [&](int j) __attribute__((always_inline)) {
         const int kk = j / ND, d = j % ND;
         if (d == 0) bv[kk] = as_bf16x8(drow + 16 * kk);
-        av[j] = as_bf16x8(&sm.kt[(32 * d + li) * ST + 16 * kk + 8 * hh]);
+        av[j] = as_bf16x8(ktl + 32 * d * ST + ((uint32_t)(16 * kk) ^ y[d]));
       };
 #pragma unroll
       for (int j = 0; j < kCqRA; ++j) read_ops(j);
