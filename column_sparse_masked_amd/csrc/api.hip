@@ -52,7 +52,7 @@ bool pairs_for(const fm_problem* p, int nQ, int cus) {
   if (p->head_dim != 128 || p->fwd_rows == fm::BQ) return false;
   if (p->fwd_rows == 2 * fm::BQ) return true;
   const long pairs = (long)p->batch * p->heads * ((nQ + 1) / 2);
-  return pairs >= 4L * cus * fm::fwd_pair_blocks_per_cu();
+  return pairs >= 2L * cus * fm::fwd_pair_blocks_per_cu();
 }
 
 // At most this many forward items are split (two partial-result slots each).

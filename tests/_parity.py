@@ -94,7 +94,7 @@ def check_full(w, got, tensors, label=""):
 
 def expected_pairs(w, fwd_rows=0):
     """Whether the library runs the forward on pairs of query blocks: asked
-    for (fwd_rows 256), or with head_dim 128 and at least four pairs per
+    for (fwd_rows 256), or with head_dim 128 and at least two pairs per
     compute unit (the pair kernel's grid), unless fwd_rows is 128."""
     from column_sparse_masked_amd import _lib
     if w.D != 128 or fwd_rows == 128:
@@ -102,7 +102,7 @@ def expected_pairs(w, fwd_rows=0):
     if fwd_rows == 256:
         return True
     nQ = -(-w.Sq // 128)
-    return w.B * w.H * ((nQ + 1) // 2) >= 4 * _lib.device_cu_count()
+    return w.B * w.H * ((nQ + 1) // 2) >= 2 * _lib.device_cu_count()
 
 
 def pair_lists(cls):
