@@ -75,12 +75,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
 // while the other computes its exponentials.
 constexpr int kBwdThreads = 512;
 
-// Row terms ride in the matrix products.  Each staged Q row carries, in the
-// 16 columns after its D values, the pair (hi, lo) of bf16 numbers whose sum
-// is -LSE / scale to about 16 bits (zeros elsewhere), and each dO row the pair
-// for -Delta.  With a constant B operand of ones in those two columns, one
-// more k-step of S = Q K^T and dP = dO V^T yields S - LSE / scale and
-// dP - Delta, so P = exp2(scale log2(e) S') and dS' = P dP' need no
+// Row terms start the accumulators.  With each chunk, -LSE / scale and
+// -Delta of its rows are staged in LDS as fp32 (rterm); the S and dP
+// accumulators of a wave start from them instead of from zero (a lane's 16
+// rows are 4 runs of 4 consecutive rows: four 16-byte reads, the same for
+// every lane of a row half), so the products yield S - LSE / scale and
+// dP - Delta, and P = exp2(scale log2(e) S') and dS' = P dP' need no
 // per-row value in the lanes, whose rows differ from lane to lane.
 // The LDS of a workgroup is three separate arrays (row-major staging,
 // transposed staging, P / dS exchange) rather than one structure, so that the
@@ -88,7 +88,7 @@ constexpr int kBwdThreads = 512;
 // of one past the reads of another.  BwdSmem points into them.
 template <int D>
 struct BwdSmem {
-  static constexpr int QST = D + 24;   // Q / dO row stride: D values, 16 row-term columns, pad
+  static constexpr int QST = D + 24;   // Q / dO row stride: D values, pad
   static constexpr int QTS = QC + 8;   // Q^T / dO^T row stride; rows in qt_pos order
   static constexpr int RM = QC * QST;  // elements of one row-major tile
   static constexpr int TR = D * QTS;   // elements of one transposed tile
@@ -99,6 +99,7 @@ struct BwdSmem {
   // P and dS' of (key group g, half m) in the A-operand layout of the
   // dV / dK products: pds[g][m][0 = P, 1 = dS][t2][lane]
   bf16x8 (*pds)[2][2][2][64];
+  float (*rterm)[QC];   // [0]: -LSE / scale (-inf: no P), [1]: -Delta of the chunk's rows
   __device__ __forceinline__ bf16* qt(int buf) const { return tr + (2 * buf) * TR; }
   __device__ __forceinline__ bf16* dot(int buf) const { return tr + (2 * buf + 1) * TR; }
 };
@@ -179,9 +180,8 @@ __device__ __forceinline__ void store_rowmajor(const ChunkStage<D>& r, const Sme
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) *reinterpret_cast<bf16x8*>(rm + rr * QST) = r.v[rr];
   }
-  // row terms: -LSE / scale into the Q row (-inf for rows past the end and
-  // rows no key sees, so P = 0 there), -Delta into the dO row, each as a
-  // (hi, lo) pair of bf16
+  // row terms: -LSE / scale (-inf for rows past the end and rows no key
+  // sees, so P = 0 there) and -Delta
   if (t < 2 * QC) {
     const bool is_q = t < QC;
     const int row = (int)t % QC;
@@ -192,11 +192,7 @@ __device__ __forceinline__ void store_rowmajor(const ChunkStage<D>& r, const Sme
     } else {
       x = -r.row_term;
     }
-    const bf16 hi = (bf16)x;
-    const bf16 lo = (bf16)(x == -INFINITY ? 0.f : x - (float)hi);
-    bf16* dst = (is_q ? sm.q : sm.dout) + row * QST + D;
-    dst[0] = hi;
-    dst[1] = lo;
+    sm.rterm[is_q ? 0 : 1][row] = x;
   }
 }
 
@@ -236,18 +232,6 @@ __device__ __forceinline__ void store_transposed(const ChunkStage<D>& r, const S
   const TransposedStore<D, Smem> ts(r, sm, buf, salt, t);
 #pragma unroll
   for (int e = 0; e < 8; ++e) ts.row(e);
-}
-
-// Columns D .. D+15 of every staged Q and dO row start as zero (the row-term
-// pair is written into the first two for each chunk).
-template <int D, typename Smem>
-__device__ __forceinline__ void zero_row_terms(const Smem& sm, unsigned t) {
-  constexpr int QST = Smem::QST;
-  if (t < 2 * QC) {
-    bf16* dst = (t < QC ? sm.q : sm.dout) + (int)(t % QC) * QST + D;
-    *reinterpret_cast<bf16x8*>(dst) = zero_bf16x8();
-    *reinterpret_cast<bf16x8*>(dst + 8) = zero_bf16x8();
-  }
 }
 
 // One key-stationary work item (batch*head, key block): what the kernel needs
@@ -342,12 +326,14 @@ void attn_bwd_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 lds_rm[2 * Smem::RM];
   __shared__ __attribute__((aligned(16))) bf16 lds_t[4 * Smem::TR];
   __shared__ bf16x8 lds_pds[4][2][2][2][64];
+  __shared__ __attribute__((aligned(16))) float lds_rterm[2][QC];
   __shared__ uint32_t lds_hdr[2][4];   // headers of this and the next item
   Smem sm;
   sm.q = lds_rm;
   sm.dout = lds_rm + Smem::RM;
   sm.tr = lds_t;
   sm.pds = lds_pds;
+  sm.rterm = lds_rterm;
 
   const unsigned t = threadIdx.x;
   const int lane = (int)(t & 63), w = (int)(t >> 6);
@@ -363,16 +349,8 @@ void attn_bwd_kernel(const BwdArgs a) {
 
   const ItemQueue iq{&a.counters[kCtrBwdNext], a.queue, a.cnt_k, n_items, max_items, a.nK, a.H, a.Hm, a.nQ};
   const bool cache = tile_cache_on(a.counters, a.ds_cap);
-  zero_row_terms<D>(sm, t);
   if (t == 0) iq.first(lds_hdr[0]);
   __syncthreads();
-
-  // B operand of the row-term k-step: ones in columns D, D+1
-  bf16x8 ones = zero_bf16x8();
-  if (hh == 0) {
-    ones[0] = (bf16)1.0f;
-    ones[1] = (bf16)1.0f;
-  }
   // first row of chunk c of a query block with list entry e
   auto row0 = [&](int e, int c) __attribute__((always_inline)) {
     return min(e & kListIndex, a.nQ - 1) * BQ + (c % CPB) * QC;
@@ -462,36 +440,41 @@ void attn_bwd_kernel(const BwdArgs a) {
         const bf16* dotc = sm.dot(bc);
 
         // ---- phase 1: S, dP of rows 32 m + 8 r + 4 hh + q (element 4r+q),
-        // key li, the row-term k-step first ----
+        // key li, starting from the rows' terms ----
         f32x16 s, dp;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          s[v] = 0.f;
-          dp[v] = 0.f;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 ls = *reinterpret_cast<const float4*>(&sm.rterm[0][32 * m + 8 * r4 + 4 * hh]);
+          const float4 ld = *reinterpret_cast<const float4*>(&sm.rterm[1][32 * m + 8 * r4 + 4 * hh]);
+          s[4 * r4] = ls.x;
+          s[4 * r4 + 1] = ls.y;
+          s[4 * r4 + 2] = ls.z;
+          s[4 * r4 + 3] = ls.w;
+          dp[4 * r4] = ld.x;
+          dp[4 * r4 + 1] = ld.y;
+          dp[4 * r4 + 2] = ld.z;
+          dp[4 * r4 + 3] = ld.w;
         }
         const bf16* qrow = sm.q + (32 * m + li) * QST + 8 * hh;
         const bf16* drow = sm.dout + (32 * m + li) * QST + 8 * hh;
         if constexpr (D == 128) {
           // operands read two k-steps ahead; the fences keep that order
-          bf16x8 qa[NS + 1], da[NS + 1];   // operand of k-step i: row term (i = 0), then i - 1
+          bf16x8 qa[NS], da[NS];
           auto read_ops = [&](int i) __attribute__((always_inline)) {
-            const int kk = i == 0 ? NS : i - 1;
-            qa[i] = as_bf16x8(qrow + 16 * kk);
-            da[i] = as_bf16x8(drow + 16 * kk);
+            qa[i] = as_bf16x8(qrow + 16 * i);
+            da[i] = as_bf16x8(drow + 16 * i);
           };
           read_ops(0);
           read_ops(1);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int i = 0; i <= NS; ++i) {
-            s = mfma32(qa[i], i == 0 ? ones : kf[i - 1], s);
-            dp = mfma32(da[i], i == 0 ? ones : vf[i - 1], dp);
-            if (i + 2 <= NS) read_ops(i + 2);
+          for (int i = 0; i < NS; ++i) {
+            s = mfma32(qa[i], kf[i], s);
+            dp = mfma32(da[i], vf[i], dp);
+            if (i + 2 < NS) read_ops(i + 2);
             __builtin_amdgcn_sched_barrier(0);
           }
         } else {
-          s = mfma32(as_bf16x8(qrow + 16 * NS), ones, s);
-          dp = mfma32(as_bf16x8(drow + 16 * NS), ones, dp);
 #pragma unroll
           for (int kk = 0; kk < NS; ++kk) {
             s = mfma32(as_bf16x8(qrow + 16 * kk), kf[kk], s);
