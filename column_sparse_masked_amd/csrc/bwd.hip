@@ -88,7 +88,7 @@ constexpr int kBwdThreads = 512;
 // of one past the reads of another.  BwdSmem points into them.
 template <int D>
 struct BwdSmem {
-  static constexpr int QST = D + 24;   // Q / dO row stride: D values, pad
+  static constexpr int QST = D + 24;   // Q / dO row stride (elements): D values, then padding
   static constexpr int QTS = QC + 8;   // Q^T / dO^T row stride; rows in qt_pos order
   static constexpr int RM = QC * QST;  // elements of one row-major tile
   static constexpr int TR = D * QTS;   // elements of one transposed tile
