@@ -182,7 +182,7 @@ def test_large_logit_parity(name, fwd_rows):
     and a row's running maximum jumps by far more than the forward's lazy
     rescale threshold partway along the row.  This exercises the forward's
     rescale of O and l, the split items' merge, and the backward's row term
-    -LSE / scale carried as a (hi, lo) bf16 pair.  LSE and the gradients are
+    -LSE / scale of large magnitude starting the S accumulators.  LSE and the gradients are
     held to the usual contract; O to the per-element bound derived from its
     bf16 roundings (_o_bound_large_logits), since one key dominates many
     rows here and |O| approaches max|v|."""
